@@ -1,0 +1,338 @@
+/*
+ * qw_oracle.c -- plain, slow CPU oracle for int8 weight-only (W8A16)
+ * quantization of Linear weights and the W8A16 matmul.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library calls, links
+ * or includes this file; only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark load it (through oracle/__init__.py).  It
+ * shares no code, header, table or constant with the HIP path.
+ *
+ * What it computes (the method, restated):
+ *   - Symmetric linear quantization to n = 8 bits: a per-row bound is mapped
+ *     onto the largest code 2^(n-1)-1 = 127, q = round(w / S), and a product
+ *     of two such values carries no zero-point cross terms.  Source: LightSeq
+ *     slide deck "LightSeq：高性能NLP序列推理实践", slide "量化：裁剪+对称"
+ *     (symmetric quantization formula).
+ *   - The bound is the row's largest |w|, or a clipped bound (a percentage
+ *     clip) when a percentile below 100 is requested.  Source: same deck,
+ *     slide "量化流程" (fixed range clip vs percentage clip).
+ *   - Weight-only W8A16: Linear weights are stored int8 with one scale per
+ *     output channel and dequantized back to F16 for the matmul.  Source:
+ *     "探索ChatGLM2在算能BM1684X上INT8量化部署" (elecfans), section 2
+ *     (量化方案) and section 3 (TPU-MLIR实现: weight is the right operand,
+ *     F16 scale).
+ *   - The matmul: load, cast int8 -> F16, multiply by the scale
+ *     (dequantize), multiply with the activation, store.  Source: same page,
+ *     section 4 (后端性能提升原理), its five-step list.
+ *   - Simulation style: low-precision values are carried in a wider float
+ *     type and every quantization step is applied explicitly after a
+ *     high-precision operation.  Source: QPyTorch review (nubint.ai),
+ *     section 提出的方法.
+ *
+ * Readings taken where the pages leave a step open (each also listed in
+ * the design notes):
+ *   R1 one scale per output row n of W[N,K] (the weight's output channel);
+ *   R2 the clip bound is the linear-interpolated (Hyndman-Fan type 7)
+ *      percentile of |w| over the row, interpolated in binary64;
+ *   R3 scale S = fp16_RNE( fp32( t / 127 ) ), and quantization divides by
+ *      the *stored* fp16 scale;
+ *   R4 q = clamp( round_half_even( fp32( w / S ) ), -127, 127 ), true IEEE
+ *      binary32 division; S == 0 gives q = 0;
+ *   R5 the matmul reference is exact-as-possible binary64:
+ *      ref[m][n] = sum_k x[m][k] * (q[n][k] * S[n]).
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -shared
+ * -fPIC.  No FMA contraction anywhere; every operation is one IEEE op.
+ */
+#include <math.h>
+#include <stdint.h>
+#if defined(_OPENMP)
+#include <omp.h>
+#endif
+#include <stdlib.h>
+#include <string.h>
+
+#if defined(__FAST_MATH__)
+#error "the oracle must not be built with fast-math"
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* IEEE 754 binary16 conversions, written from the format definition:       */
+/* 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits; subnormals have */
+/* quantum 2^-24; the largest finite value is 65504; rounding is to nearest */
+/* with ties to even.                                                       */
+/* ------------------------------------------------------------------------ */
+
+/* Round the non-negative finite value  sig * 2^e  (sig > 0 an integer of at
+ * most 63 bits) to binary16 and return the magnitude bits. */
+static uint16_t half_from_scaled(uint64_t sig, int e)
+{
+    /* exponent of the leading bit: |v| in [2^lead, 2^(lead+1)) */
+    int nbits = 64 - __builtin_clzll(sig);
+    int lead = nbits - 1 + e;
+    /* the binary16 quantum (unit in the last place) at this magnitude */
+    int quantum_exp = (lead < -14 ? -14 : lead) - 10;
+    int shift = quantum_exp - e; /* v / quantum = sig * 2^(-shift) */
+    uint64_t n;
+    if (shift <= 0) {
+        n = sig << (-shift); /* exact; only when v is a small multiple of the quantum */
+    } else if (shift > 63) {
+        n = 0; /* v < quantum / 2 for sure */
+    } else {
+        uint64_t whole = sig >> shift;
+        uint64_t rem = sig & ((((uint64_t)1) << shift) - 1);
+        uint64_t half = ((uint64_t)1) << (shift - 1);
+        if (rem > half || (rem == half && (whole & 1)))
+            whole += 1;
+        n = whole;
+    }
+    if (lead < -14) {
+        /* subnormal range: the bits are the quantum count; a count of 1024
+         * is exactly the smallest normal number 0x0400 */
+        return (uint16_t)n;
+    }
+    /* normal range: n in [1024, 2048] */
+    int biased = lead + 15;
+    if (n == 2048) {
+        n = 1024;
+        biased += 1;
+    }
+    if (biased >= 31)
+        return 0x7c00; /* overflow to infinity */
+    return (uint16_t)((biased << 10) | (int)(n - 1024));
+}
+
+uint16_t oracle_f32_to_f16(float x)
+{
+    uint32_t b;
+    memcpy(&b, &x, sizeof b);
+    uint16_t sign = (uint16_t)((b >> 16) & 0x8000u);
+    uint32_t mag = b & 0x7fffffffu;
+    if (mag >= 0x7f800000u) /* inf or nan */
+        return (uint16_t)(sign | (mag == 0x7f800000u ? 0x7c00u : 0x7e00u));
+    if (mag == 0)
+        return sign;
+    uint32_t expfield = mag >> 23;
+    uint64_t sig = mag & 0x7fffffu;
+    int e;
+    if (expfield == 0) {
+        e = -149; /* binary32 subnormal: sig * 2^-149 */
+    } else {
+        sig |= 0x800000u;
+        e = (int)expfield - 150;
+    }
+    return (uint16_t)(sign | half_from_scaled(sig, e));
+}
+
+uint16_t oracle_f64_to_f16(double x)
+{
+    uint64_t b;
+    memcpy(&b, &x, sizeof b);
+    uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
+    uint64_t mag = b & 0x7fffffffffffffffull;
+    if (mag >= 0x7ff0000000000000ull)
+        return (uint16_t)(sign | (mag == 0x7ff0000000000000ull ? 0x7c00u : 0x7e00u));
+    if (mag == 0)
+        return sign;
+    uint64_t expfield = mag >> 52;
+    uint64_t sig = mag & 0xfffffffffffffull;
+    int e;
+    if (expfield == 0) {
+        e = -1074;
+    } else {
+        sig |= 0x10000000000000ull;
+        e = (int)expfield - 1075;
+    }
+    return (uint16_t)(sign | half_from_scaled(sig, e));
+}
+
+float oracle_f16_to_f32(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expfield = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    float v;
+    if (expfield == 0x1f) {
+        v = frac ? NAN : INFINITY;
+    } else if (expfield == 0) {
+        v = ldexpf((float)frac, -24); /* exact */
+    } else {
+        v = ldexpf((float)(1024 + frac), expfield - 25); /* exact */
+    }
+    return sign ? -v : v;
+}
+
+void oracle_f32_to_f16_array(const float *x, uint16_t *out, int64_t count)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = oracle_f32_to_f16(x[i]);
+}
+
+void oracle_f64_to_f16_array(const double *x, uint16_t *out, int64_t count)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = oracle_f64_to_f16(x[i]);
+}
+
+void oracle_f16_to_f32_array(const uint16_t *h, float *out, int64_t count)
+{
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = oracle_f16_to_f32(h[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Row threshold (clip bound)                                               */
+/* ------------------------------------------------------------------------ */
+
+static int cmp_float_asc(const void *a, const void *b)
+{
+    float x = *(const float *)a, y = *(const float *)b;
+    return (x > y) - (x < y);
+}
+
+/* The pct-th percentile of the k values |row[j]|, type-7 linear
+ * interpolation between closest ranks, in binary64.  Returns the binary64
+ * interpolated value; the threshold is its binary32 rounding.  For
+ * pct == 100 this is the maximum (no clipping).  `scratch` holds k floats. */
+double oracle_row_percentile(const float *row, int64_t k, double pct, float *scratch)
+{
+    for (int64_t j = 0; j < k; ++j)
+        scratch[j] = fabsf(row[j]);
+    if (pct == 100.0) {
+        float mx = 0.0f;
+        for (int64_t j = 0; j < k; ++j)
+            if (scratch[j] > mx)
+                mx = scratch[j];
+        return (double)mx;
+    }
+    qsort(scratch, (size_t)k, sizeof(float), cmp_float_asc);
+    double frac_of_range = pct / 100.0;
+    double pos = frac_of_range * (double)(k - 1);
+    double i_floor = floor(pos);
+    int64_t i = (int64_t)i_floor;
+    if (i >= k - 1)
+        return (double)scratch[k - 1];
+    double f = pos - i_floor;
+    double lo = (double)scratch[i];
+    double hi = (double)scratch[i + 1];
+    double gap = hi - lo;
+    double step = f * gap;
+    return lo + step;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Quantizer                                                                */
+/* ------------------------------------------------------------------------ */
+
+/* Quantize W[n][k] (row-major binary32) per output row.
+ *   q       [n][k] int8 codes (out)
+ *   scales  [n] binary16 bit patterns (out)
+ *   thresh  [n] binary32 clip bound t (out, may be NULL)
+ * Returns 0, or -1 for invalid arguments (non-finite input included). */
+int oracle_quantize(const float *w, int64_t n, int64_t k, double pct,
+                    int8_t *q, uint16_t *scales, float *thresh)
+{
+    if (n < 0 || k <= 0 || !(pct > 0.0 && pct <= 100.0))
+        return -1;
+    for (int64_t i = 0; i < n * k; ++i)
+        if (!isfinite(w[i]))
+            return -1;
+    int bad = 0;
+#pragma omp parallel
+    {
+        float *scratch = (float *)malloc((size_t)k * sizeof(float));
+        if (!scratch) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < n; ++r) {
+            if (!scratch)
+                continue;
+            const float *row = w + r * k;
+            double t64 = oracle_row_percentile(row, k, pct, scratch);
+            float t = (float)t64;
+            float s32 = t / 127.0f;
+            uint16_t s16 = oracle_f32_to_f16(s32);
+            float s = oracle_f16_to_f32(s16);
+            scales[r] = s16;
+            if (thresh)
+                thresh[r] = t;
+            int8_t *qrow = q + r * k;
+            for (int64_t j = 0; j < k; ++j) {
+                if (s == 0.0f) {
+                    qrow[j] = 0;
+                    continue;
+                }
+                float ratio = row[j] / s;       /* binary32 IEEE division */
+                float rounded = rintf(ratio);  /* default mode: nearest, ties to even */
+                if (rounded > 127.0f)
+                    rounded = 127.0f;
+                if (rounded < -127.0f)
+                    rounded = -127.0f;
+                qrow[j] = (int8_t)rounded;
+            }
+        }
+        free(scratch);
+    }
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* W8A16 matmul reference                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* One output: sum_k x[m][k] * (q[n][k] * S[n]) in binary64.  x holds
+ * binary16 bit patterns.  Every product is exact in binary64 (11 x 8 x 11
+ * significant bits); only the K-term sum rounds. */
+static double dot_one(const uint16_t *xrow, const int8_t *qrow, double s, int64_t k)
+{
+    double acc = 0.0;
+    for (int64_t j = 0; j < k; ++j) {
+        double wdeq = (double)qrow[j] * s;
+        double xv = (double)oracle_f16_to_f32(xrow[j]);
+        acc += xv * wdeq;
+    }
+    return acc;
+}
+
+/* Full reference: ref[m][n] for X[m][k] (binary16 bits), Q[n][k], S[n]
+ * (binary16 bits). */
+void oracle_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                 int64_t m, int64_t n, int64_t k, double *ref)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j)
+            ref[i * n + j] = dot_one(x + i * k, q + j * k,
+                                     (double)oracle_f16_to_f32(scales[j]), k);
+}
+
+/* Sampled reference: out[c] = ref[mi[c]][ni[c]]. */
+void oracle_gemm_sampled(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                         int64_t k, const int64_t *mi, const int64_t *ni,
+                         int64_t count, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < count; ++c)
+        out[c] = dot_one(x + mi[c] * k, q + ni[c] * k,
+                         (double)oracle_f16_to_f32(scales[ni[c]]), k);
+}
+
+/* Threads the OpenMP runtime will use for the parallel loops above. */
+int oracle_num_threads(void)
+{
+    int nt = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#if defined(_OPENMP)
+            nt = omp_get_num_threads();
+#endif
+        }
+    }
+    return nt;
+}

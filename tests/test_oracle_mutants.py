@@ -1,0 +1,72 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch every one of them.
+
+Each mutant is a textual edit of ``oracle/qw_oracle.c`` compiled into a
+temporary library; the fast pins of ``oracle_pins.py`` then run against it
+and at least one must fail.  This is what makes the pins worth trusting: a
+pin set that a dropped term, a wrong sign or index, a transposed operand or
+a wrong rounding rule would slip through is not a pin set.
+"""
+
+import os
+
+import pytest
+
+import oracle
+import oracle_pins as P
+
+MUTANTS = {
+    # rounding: half away from zero instead of half to even
+    "round_half_away": ("float rounded = rintf(ratio);", "float rounded = roundf(ratio);"),
+    # reciprocal-multiply instead of true IEEE division
+    "reciprocal_multiply": ("float ratio = row[j] / s; ", "float ratio = row[j] * (1.0f / s); "),
+    # quantize with the unrounded binary32 scale
+    "fp32_scale_for_codes": ("float ratio = row[j] / s; ", "float ratio = row[j] / s32; "),
+    # clamp range +-128 on the negative side
+    "clamp_minus_128": ("if (rounded < -127.0f)\n                    rounded = -127.0f;",
+                        "if (rounded < -128.0f)\n                    rounded = -128.0f;"),
+    # wrong bound divisor
+    "divide_by_128": ("float s32 = t / 127.0f;", "float s32 = t / 128.0f;"),
+    # percentile: wrong rank (ceil) and dropped interpolation term
+    "percentile_ceil": ("double i_floor = floor(pos);", "double i_floor = ceil(pos);"),
+    "percentile_no_interp": ("return lo + step;", "return lo;"),
+    "percentile_wrong_neighbour": ("double hi = (double)scratch[i + 1];", "double hi = (double)scratch[k - 1];"),
+    # binary16 rounding: ties away, and a wrong subnormal boundary
+    "f16_ties_away": ("if (rem > half || (rem == half && (whole & 1)))", "if (rem >= half)"),
+    "f16_subnormal_edge": ("int quantum_exp = (lead < -14 ? -14 : lead) - 10;",
+                           "int quantum_exp = (lead < -15 ? -15 : lead) - 10;"),
+    "f16_decode_bias": ("v = ldexpf((float)(1024 + frac), expfield - 25);",
+                        "v = ldexpf((float)(1024 + frac), expfield - 24);"),
+    # matmul: dropped scale, wrong sign, transposed/wrong operand index
+    "gemm_drops_scale": ("double wdeq = (double)qrow[j] * s;", "double wdeq = (double)qrow[j];"),
+    "gemm_wrong_sign": ("acc += xv * wdeq;", "acc -= xv * wdeq;"),
+    "gemm_reversed_k": ("double xv = (double)oracle_f16_to_f32(xrow[j]);",
+                        "double xv = (double)oracle_f16_to_f32(xrow[k - 1 - j]);"),
+    "gemm_scale_of_wrong_row": ("(double)oracle_f16_to_f32(scales[j]), k);",
+                                "(double)oracle_f16_to_f32(scales[i % n]), k);"),
+}
+
+
+@pytest.fixture(scope="module")
+def source_text():
+    with open(oracle.SOURCE) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, source_text, name):
+    old, new = MUTANTS[name]
+    assert source_text.count(old) == 1, "mutation site for %s not found exactly once" % name
+    src = tmp_path / ("mutant_%s.c" % name)
+    src.write_text(source_text.replace(old, new))
+    lib_path = str(tmp_path / ("libmutant_%s.so" % name))
+    oracle.build(source=str(src), output=lib_path)
+    mut = oracle.Oracle(oracle.load_library(lib_path))
+    caught = []
+    for pin in P.FAST_PINS:
+        try:
+            pin(mut)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, "mutant %s passed every pin" % name
+    os.remove(lib_path)
