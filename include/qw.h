@@ -1,0 +1,169 @@
+/*
+ * qw.h -- int8 weight-only (W8A16) Linear layers for AMD Instinct MI355X
+ * (gfx950): a C ABI over hand-written HIP kernels.
+ *
+ * The method (restated from the pages, not quoted):
+ *   - Symmetric 8-bit quantization maps a per-channel bound onto the
+ *     largest code 2^(8-1)-1 = 127 with q = round(w / S); optional clipping
+ *     of the bound by a percentage of the weight magnitudes.  Source: LightSeq
+ *     slide deck "LightSeq：高性能NLP序列推理实践", slides "量化流程" and
+ *     "量化：裁剪+对称".
+ *   - Only Linear weights are quantized (per channel, stored int8 with an
+ *     F16 scale); at compute time they are cast back to F16, scaled and
+ *     multiplied with F16 activations; the weight is the right, 2-D operand.
+ *     Source: "探索ChatGLM2在算能BM1684X上INT8量化部署" (elecfans),
+ *     sections 2 (量化方案), 3 (TPU-MLIR实现) and 4 (后端性能提升原理).
+ *
+ * Conventions for every entry point:
+ *   - Matrices are row-major and contiguous.  W / Q are [n][k] (torch
+ *     Linear layout: n output channels, k input features, k contiguous),
+ *     X is [m][k], Y is [m][n].  fp16 values travel as their IEEE binary16
+ *     bit patterns (uint16_t).
+ *   - Every pointer is a HIP device pointer (or managed memory visible to
+ *     the device) owned by the caller; the library allocates no device
+ *     memory and keeps no per-call state.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls
+ *     enqueue work on it and return without waiting; results are visible
+ *     after the caller synchronizes the stream.
+ *   - Arguments are checked on the host before anything is enqueued; on
+ *     any error nothing is launched and no output byte is written.
+ *   - Results are deterministic: no atomics, fixed reduction order.
+ *   - Not safe to call with overlapping input and output buffers
+ *     (rejected with QW_ERROR_INVALID_VALUE when detected).
+ */
+#ifndef QW_H
+#define QW_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define QW_API __attribute__((visibility("default")))
+#else
+#define QW_API
+#endif
+
+typedef enum qw_status {
+    QW_SUCCESS = 0,
+    QW_ERROR_INVALID_VALUE = 1, /* null pointer, negative size, k == 0, bad percentile, overlap */
+    QW_ERROR_MISALIGNED = 2,    /* a pointer is not 16-byte aligned */
+    QW_ERROR_UNSUPPORTED = 3,   /* k % 16 != 0, or a size beyond the documented maximum */
+    QW_ERROR_LAUNCH = 4         /* the HIP runtime rejected a launch (no device, bad stream, ...) */
+} qw_status;
+
+/* Largest row length the quantizer accepts (a row is held in registers). */
+#define QW_QUANTIZE_MAX_K 65536
+
+/*
+ * qw_quantize_weights -- per-output-channel symmetric int8 quantization.
+ *
+ * Source: LightSeq slide deck, slides "量化流程" (fixed range clip vs
+ * percentage clip) and "量化：裁剪+对称" (bound -> 2^(n-1)-1, q = round(w/S));
+ * ChatGLM2/BM1684X page, section 2 (per-channel weight-only int8) and
+ * section 3 (F16 scale).
+ *
+ * For every row r of W[n][k] (fp32):
+ *   t[r]  = largest |W[r][j]| if clip_percentile == 100, otherwise the
+ *           clip_percentile-th percentile of |W[r][:]| with linear
+ *           interpolation between closest ranks (a = |row| sorted
+ *           ascending, pos = (clip_percentile / 100) * (k - 1) in binary64,
+ *           i = floor(pos), t = a[i] + (pos - i) * (a[i+1] - a[i]) in
+ *           binary64 without fused multiply-add, then rounded to binary32;
+ *           i >= k - 1 gives a[k-1]);
+ *   S[r]  = binary16( binary32( t[r] / 127 ) ), both roundings to nearest
+ *           even, true IEEE division;
+ *   q[r][j] = 0 if S[r] == 0, else clamp( round_half_even( binary32(
+ *           W[r][j] / S[r] ) ), -127, 127 ) -- the quotient divides by the
+ *           stored binary16 scale.  -128 is never produced.
+ *
+ *   w                fp32 [n][k], read only, finite values (non-finite input
+ *                    gives unspecified codes)
+ *   n                rows (output channels), 0 <= n <= INT32_MAX; n == 0 is a no-op
+ *   k                row length, 16 <= k <= QW_QUANTIZE_MAX_K, k % 16 == 0
+ *   clip_percentile  in (0, 100]; 100 means no clipping (absmax).  binary64,
+ *                    so that e.g. 99.99 is not first rounded to binary32
+ *   q                int8 [n][k] codes (written)
+ *   scales           binary16 bits [n] (written)
+ *   stream           hipStream_t
+ *
+ * Errors: QW_ERROR_INVALID_VALUE (null pointer with n > 0, n < 0, k <= 0,
+ * clip_percentile NaN or outside (0, 100], q/scales overlapping w or each
+ * other), QW_ERROR_UNSUPPORTED (k % 16 != 0, k > QW_QUANTIZE_MAX_K,
+ * n > INT32_MAX), QW_ERROR_MISALIGNED (w, q or scales not 16-byte aligned),
+ * QW_ERROR_LAUNCH.  Bit-exact by contract: the same inputs give the same
+ * bytes on every call.
+ */
+QW_API qw_status qw_quantize_weights(const float *w, int64_t n, int64_t k,
+                                     double clip_percentile, int8_t *q,
+                                     uint16_t *scales, void *stream);
+
+/*
+ * qw_w8a16_gemm -- Y = X * dequant(Q)^T with per-channel fp16 scales.
+ *
+ * Source: ChatGLM2/BM1684X page, section 4 (后端性能提升原理): load, cast
+ * int8 -> F16, multiply by the scale (dequantize), matrix multiply with the
+ * input activation, store; section 3: the quantized weight is the right
+ * operand of the MatMul.
+ *
+ *   Y[i][c] = binary16_RNE( S[c] * sum_j X[i][j] * q[c][j] )
+ *
+ * The int8 -> fp16 cast is exact; products are formed exactly and summed in
+ * binary32 (fp32 accumulation); the per-channel scale is applied to the
+ * fp32 sum (algebraically the same as scaling each weight first, with less
+ * rounding).  Accuracy contract: max |Y - exact| <= 2e-3 * max|exact| + 1e-3.
+ *
+ *   x       fp16 bits [m][k]
+ *   q       int8 [n][k] codes (as written by qw_quantize_weights)
+ *   scales  fp16 bits [n]
+ *   y       fp16 bits [m][n] (written)
+ *   m       rows of X, 0 <= m <= INT32_MAX; m == 0 is a no-op
+ *   n       output channels, 0 <= n <= INT32_MAX; n == 0 is a no-op
+ *   k       reduction length, k >= 16, k % 16 == 0, k <= INT32_MAX
+ *   stream  hipStream_t
+ *
+ * The kernel is chosen from m (and k): a bandwidth-bound GEMV for decode
+ * shapes, MFMA tiled GEMM for prefill shapes.
+ *
+ * Errors: QW_ERROR_INVALID_VALUE (null pointer with m, n > 0, negative
+ * size, k <= 0, y overlapping x, q or scales), QW_ERROR_UNSUPPORTED
+ * (k % 16 != 0, a size beyond INT32_MAX), QW_ERROR_MISALIGNED,
+ * QW_ERROR_LAUNCH.
+ */
+QW_API qw_status qw_w8a16_gemm(const uint16_t *x, const int8_t *q,
+                               const uint16_t *scales, uint16_t *y, int64_t m,
+                               int64_t n, int64_t k, void *stream);
+
+/* Kernel selection for qw_w8a16_gemm_path. */
+typedef enum qw_gemm_path {
+    QW_PATH_AUTO = 0,  /* what qw_w8a16_gemm does */
+    QW_PATH_GEMV = 1,  /* VALU dot products, weights streamed once (m <= 8) */
+    QW_PATH_MFMA = 2   /* MFMA tiled GEMM, int8 tiles dequantized into LDS */
+} qw_gemm_path;
+
+/*
+ * qw_w8a16_gemm_path -- qw_w8a16_gemm with the kernel forced, for parity
+ * tests of each path and for measuring the decode/prefill crossover.  Same
+ * arguments, result contract and errors as qw_w8a16_gemm, plus
+ * QW_ERROR_INVALID_VALUE for an unknown path and QW_ERROR_UNSUPPORTED when
+ * QW_PATH_GEMV is forced outside its limits (m > 8, or m * ceil(k / 1024)
+ * > 32).
+ */
+QW_API qw_status qw_w8a16_gemm_path(const uint16_t *x, const int8_t *q,
+                                    const uint16_t *scales, uint16_t *y,
+                                    int64_t m, int64_t n, int64_t k, int path,
+                                    void *stream);
+
+/* A static, human-readable name for a status code (never NULL). */
+QW_API const char *qw_status_string(qw_status status);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+QW_API int qw_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QW_H */

@@ -1,0 +1,183 @@
+"""int8 weight-only (W8A16) Linear layers for AMD Instinct MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libqw.so`` (declared in
+``include/qw.h``).  This module only marshals arguments: it checks tensor
+dtypes, shapes and devices, allocates outputs with torch, and passes raw
+device pointers plus the current HIP stream to the library.  Every step of
+the computation runs in the library's HIP kernels; there is no CPU or
+PyTorch fallback, and importing this package fails loudly when the library
+has not been built (``python -m int8_weight_quantized_amd.build``): the
+first call, or ``library()``, raises ImportError.
+
+    q, s = quantize_weights(w)              # w: cuda fp32 [N, K]
+    y = w8a16_gemm(x, q, s)                 # x: cuda fp16 [M, K] -> fp16 [M, N]
+
+Names follow the pages: symmetric per-channel int8 weight quantization with
+an optional percentage clip (LightSeq slide deck, "量化流程" and
+"量化：裁剪+对称") and the W8A16 MatMul whose right operand is the int8
+weight ("探索ChatGLM2在算能BM1684X上INT8量化部署", sections 2-4).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(HERE, "libqw.so")
+
+QW_SUCCESS = 0
+QW_ERROR_INVALID_VALUE = 1
+QW_ERROR_MISALIGNED = 2
+QW_ERROR_UNSUPPORTED = 3
+QW_ERROR_LAUNCH = 4
+
+PATHS = {"auto": 0, "gemv": 1, "mfma": 2}
+QUANTIZE_MAX_K = 65536
+
+
+class QwError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (where, status_string(status), status))
+
+
+_lib_handle = None
+
+
+def _load():
+    """Load libqw.so once; raises ImportError when it has not been built."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(LIBRARY_PATH):
+        raise ImportError(
+            "libqw.so is not built (expected at %s); run `python -m int8_weight_quantized_amd.build`"
+            % LIBRARY_PATH)
+    lib = ctypes.CDLL(LIBRARY_PATH)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.qw_quantize_weights.argtypes = [vp, i64, i64, ctypes.c_double, vp, vp, vp]
+    lib.qw_quantize_weights.restype = ctypes.c_int
+    lib.qw_w8a16_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.qw_w8a16_gemm.restype = ctypes.c_int
+    lib.qw_w8a16_gemm_path.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.qw_w8a16_gemm_path.restype = ctypes.c_int
+    lib.qw_status_string.argtypes = [ctypes.c_int]
+    lib.qw_status_string.restype = ctypes.c_char_p
+    lib.qw_version.argtypes = []
+    lib.qw_version.restype = ctypes.c_int
+    _lib_handle = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes handle of libqw.so (loads it on first use)."""
+    return _load()
+
+
+def status_string(status: int) -> str:
+    return library().qw_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(library().qw_version())
+
+
+# ---------------------------------------------------------------------------
+# raw C-ABI calls (device pointers as ints); used by tests and the benchmark
+# ---------------------------------------------------------------------------
+
+def quantize_weights_raw(w_ptr: int, n: int, k: int, clip_percentile: float,
+                         q_ptr: int, s_ptr: int, stream: int = 0) -> int:
+    return int(library().qw_quantize_weights(w_ptr, n, k, float(clip_percentile), q_ptr, s_ptr, stream))
+
+
+def w8a16_gemm_raw(x_ptr: int, q_ptr: int, s_ptr: int, y_ptr: int, m: int, n: int, k: int,
+                   stream: int = 0, path: int = 0) -> int:
+    return int(library().qw_w8a16_gemm_path(x_ptr, q_ptr, s_ptr, y_ptr, m, n, k, int(path), stream))
+
+
+# ---------------------------------------------------------------------------
+# torch-facing calls
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_of(t) -> int:
+    torch = _torch()
+    return int(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(t, name, dtype, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device, got %s" % (name, t.device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.dim() != ndim:
+        raise ValueError("%s must be %d-D, got shape %s" % (name, ndim, tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def quantize_weights(w, clip_percentile: float = 100.0, out=None):
+    """Per-output-row symmetric int8 quantization of an fp32 Linear weight.
+
+    w: cuda float32 [N, K] (K % 16 == 0, K <= 65536).  clip_percentile in
+    (0, 100]; 100 uses the row absmax.  Returns (q int8 [N, K], scales
+    float16 [N]); ``out=(q, scales)`` writes into preallocated tensors.
+    """
+    torch = _torch()
+    _check(w, "w", torch.float32, 2)
+    n, k = w.shape
+    if out is None:
+        q = torch.empty((n, k), dtype=torch.int8, device=w.device)
+        s = torch.empty((n,), dtype=torch.float16, device=w.device)
+    else:
+        q, s = out
+        _check(q, "q", torch.int8, 2)
+        _check(s, "scales", torch.float16, 1)
+        if tuple(q.shape) != (n, k) or tuple(s.shape) != (n,):
+            raise ValueError("output shapes must be [N, K] and [N]")
+    st = quantize_weights_raw(w.data_ptr(), n, k, clip_percentile, q.data_ptr(), s.data_ptr(),
+                              _stream_of(w))
+    if st != QW_SUCCESS:
+        raise QwError(st, "qw_quantize_weights")
+    return q, s
+
+
+def w8a16_gemm(x, q, scales, out=None, path: str = "auto"):
+    """Y = X * dequant(q)^T: x cuda fp16 [M, K], q int8 [N, K], scales fp16 [N]
+    -> fp16 [M, N].  ``path`` forces a kernel ("gemv" or "mfma")."""
+    torch = _torch()
+    _check(x, "x", torch.float16, 2)
+    _check(q, "q", torch.int8, 2)
+    _check(scales, "scales", torch.float16, 1)
+    m, k = x.shape
+    n = q.shape[0]
+    if q.shape[1] != k or scales.shape[0] != n:
+        raise ValueError("shape mismatch: x %s, q %s, scales %s" % (tuple(x.shape), tuple(q.shape),
+                                                                     tuple(scales.shape)))
+    if out is None:
+        y = torch.empty((m, n), dtype=torch.float16, device=x.device)
+    else:
+        y = out
+        _check(y, "out", torch.float16, 2)
+        if tuple(y.shape) != (m, n):
+            raise ValueError("out must be [M, N]")
+    if path not in PATHS:
+        raise ValueError("path must be one of %s" % sorted(PATHS))
+    st = w8a16_gemm_raw(x.data_ptr(), q.data_ptr(), scales.data_ptr(), y.data_ptr(), m, n, k,
+                        _stream_of(x), PATHS[path])
+    if st != QW_SUCCESS:
+        raise QwError(st, "qw_w8a16_gemm")
+    return y
+
+
+__all__ = ["quantize_weights", "w8a16_gemm", "QwError", "status_string", "version", "library",
+           "quantize_weights_raw", "w8a16_gemm_raw", "PATHS", "LIBRARY_PATH"]

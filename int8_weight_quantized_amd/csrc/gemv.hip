@@ -1,0 +1,166 @@
+// gemv.hip -- W8A16 decode GEMV / skinny GEMM on the VALU (gfx950).
+//
+// Decode multiplies one (or a few) activation rows with the whole weight
+// matrix, so the time goes into loading the weights, and casting and scaling
+// them can hide under that load ("探索ChatGLM2在算能BM1684X上INT8量化部署",
+// section 4, the small-left-matrix argument and the prefill/decode
+// discussion).  Here the int8 weights are streamed from HBM exactly once
+// with 16-byte nontemporal loads, dequantized in registers with an exact
+// byte-permute trick, and dotted with fp16 activations on v_dot2_f32_f16
+// (fp32 accumulation).  The per-channel scale multiplies the fp32 sum.
+//
+// Work split: a workgroup of 4 waves stages X (m rows, fp16) in LDS once;
+// each wave then owns groups of RU consecutive weight rows and walks the
+// whole k range of those rows: lane l reads bytes [c*1024 + 16 l, +16) of
+// each row for chunk c, i.e. every load instruction of the wave covers 1 KiB
+// of one row, fully coalesced.  The RU*M per-lane partial sums are combined
+// with a transposing butterfly (about RU*M shuffles instead of 6*RU*M).
+//
+// LDS layout of X: [m][chunk][half h][lane] x 16 bytes, where entry
+// (m, c, h, l) holds x[m][c*1024 + 16 l + 8 h .. +7].  Lane l reads
+// consecutive 16-byte slots for h = 0 and h = 1: no bank conflicts.
+#include "qw_device.h"
+#include "qw_internal.h"
+
+namespace qw {
+namespace {
+
+constexpr int kGemvThreads = 256;
+constexpr int kGemvWaves = kGemvThreads / kWave;
+constexpr int kChunkK = kWave * 16; // k values covered by one wave-wide 16-byte load
+constexpr int kGemvMaxMChunks = 32; // LDS budget: 32 * 2 KiB = 64 KiB
+
+template <int MT, int RU>
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
+    const uint16_t *__restrict__ x, const int8_t *__restrict__ q,
+    const uint16_t *__restrict__ scales, uint16_t *__restrict__ y,
+    int m, int n, int k, int chunks, int groups)
+{
+    extern __shared__ u32x4_t xs[];
+    const int tid = threadIdx.x;
+    const int lane = __lane_id();
+    const int wave = tid / kWave;
+
+    // ---- stage X into LDS (rows m..MT-1 are zero) ----
+    const int entries = MT * chunks * 2 * kWave;
+    for (int e = tid; e < entries; e += kGemvThreads) {
+        const int l = e % kWave;
+        const int h = (e / kWave) & 1;
+        const int mc = e / (2 * kWave);
+        const int c = mc % chunks;
+        const int mm = mc / chunks;
+        const int kk = c * kChunkK + l * 16 + h * 8;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (mm < m && kk < k)
+            v = *reinterpret_cast<const u32x4_t *>(x + (int64_t)mm * k + kk);
+        xs[e] = v;
+    }
+    __syncthreads();
+
+    constexpr int R = RU * MT;
+    for (int g = blockIdx.x * kGemvWaves + wave; g < groups; g += gridDim.x * kGemvWaves) {
+        const int row0 = g * RU;
+        float acc[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            acc[i] = 0.0f;
+
+#pragma unroll 2
+        for (int c = 0; c < chunks; ++c) {
+            const int kk = c * kChunkK + lane * 16;
+            if (kk < k) {
+                u32x4_t wv[RU];
+#pragma unroll
+                for (int r = 0; r < RU; ++r) {
+                    const int row = row0 + r;
+                    wv[r] = (u32x4_t){0u, 0u, 0u, 0u};
+                    if (row < n)
+                        wv[r] = __builtin_nontemporal_load(
+                            reinterpret_cast<const u32x4_t *>(q + (int64_t)row * k + kk));
+                }
+                half2_t xv[MT][8];
+#pragma unroll
+                for (int mm = 0; mm < MT; ++mm) {
+                    const u32x4_t a = xs[((mm * chunks + c) * 2 + 0) * kWave + lane];
+                    const u32x4_t b = xs[((mm * chunks + c) * 2 + 1) * kWave + lane];
+                    xv[mm][0] = as_half2(a.x);
+                    xv[mm][1] = as_half2(a.y);
+                    xv[mm][2] = as_half2(a.z);
+                    xv[mm][3] = as_half2(a.w);
+                    xv[mm][4] = as_half2(b.x);
+                    xv[mm][5] = as_half2(b.y);
+                    xv[mm][6] = as_half2(b.z);
+                    xv[mm][7] = as_half2(b.w);
+                }
+#pragma unroll
+                for (int r = 0; r < RU; ++r) {
+                    half2_t hw[8];
+                    i8x16_to_half2x8(wv[r], hw);
+#pragma unroll
+                    for (int mm = 0; mm < MT; ++mm) {
+                        float a = acc[r * MT + mm];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            a = dot2(hw[j], xv[mm][j], a);
+                        acc[r * MT + mm] = a;
+                    }
+                }
+            }
+        }
+
+        butterfly_reduce<R>(acc);
+        if ((lane & (kWave / R - 1)) == 0) {
+            const int idx = butterfly_index<R>(lane);
+            const int r = idx / MT;
+            const int mm = idx % MT;
+            const int row = row0 + r;
+            if (row < n && mm < m) {
+                const float s = f16_bits_to_f32(scales[row]);
+                y[(int64_t)mm * n + row] = f32_to_f16_bits(acc[0] * s);
+            }
+        }
+    }
+}
+
+template <int MT, int RU>
+hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
+                      int64_t m, int64_t n, int64_t k, hipStream_t stream)
+{
+    const int chunks = (int)((k + kChunkK - 1) / kChunkK);
+    const int groups = (int)((n + RU - 1) / RU);
+    const size_t lds = (size_t)MT * chunks * 2 * kWave * sizeof(u32x4_t);
+    int blocks = (groups + kGemvWaves - 1) / kGemvWaves;
+    const int cap = device_cu_count() * 8;
+    if (blocks > cap)
+        blocks = cap;
+    hipLaunchKernelGGL((gemv_kernel<MT, RU>), dim3(blocks), dim3(kGemvThreads), lds, stream,
+                       x, q, scales, y, (int)m, (int)n, (int)k, chunks, groups);
+    return hipGetLastError();
+}
+
+} // namespace
+
+bool gemv_supported(int64_t m, int64_t k)
+{
+    if (m < 1 || m > 8)
+        return false;
+    const int64_t chunks = (k + kChunkK - 1) / kChunkK;
+    int64_t mt = 1;
+    while (mt < m)
+        mt <<= 1;
+    return mt * chunks <= kGemvMaxMChunks;
+}
+
+hipError_t launch_gemv(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
+                       int64_t m, int64_t n, int64_t k, hipStream_t stream)
+{
+    if (m <= 1)
+        return launch_cfg<1, 4>(x, q, scales, y, m, n, k, stream);
+    if (m <= 2)
+        return launch_cfg<2, 4>(x, q, scales, y, m, n, k, stream);
+    if (m <= 4)
+        return launch_cfg<4, 4>(x, q, scales, y, m, n, k, stream);
+    return launch_cfg<8, 4>(x, q, scales, y, m, n, k, stream);
+}
+
+} // namespace qw

@@ -1,0 +1,274 @@
+// quantize.hip -- per-output-channel symmetric int8 weight quantizer (gfx950).
+//
+// Method: symmetric 8-bit quantization of each weight row onto codes
+// [-127, 127] with an absmax bound or a percentage-clipped bound (LightSeq
+// slide deck "LightSeq：高性能NLP序列推理实践", slides "量化流程" and
+// "量化：裁剪+对称"), one F16 scale per output channel of a Linear weight
+// ("探索ChatGLM2在算能BM1684X上INT8量化部署", sections 2 and 3).
+//
+// One workgroup owns one row.  The row is read from HBM exactly once with
+// 16-byte loads and stays in registers (VPT float4 per thread) while the
+// bound is found, so the kernel moves 4 bytes in and 1 byte out per weight
+// plus 2 bytes of scale per row -- the HBM roofline of the operation.
+//
+//   absmax bound:      wave max-reductions of the |w| bit patterns (for
+//                      non-negative binary32 values the integer order is
+//                      the numeric order), then across waves through LDS.
+//   percentile bound:  exact radix select of rank i over the |w| bit
+//                      patterns, 4 passes of 8 bits with a 256-bin LDS
+//                      histogram; the neighbour a[i+1] follows from a count
+//                      of values <= a[i] and a min-reduction of the values
+//                      above it.  Interpolation in binary64 without FMA.
+//
+// Rounding contract: the scale is binary16(binary32(t / 127)) with true
+// IEEE division; codes are clamp(rint(binary32(w / S)), -127, 127) where
+// rint rounds half to even (v_rndne_f32).  This file is compiled with
+// -ffp-contract=off and the pragma below so no multiply-add is fused.
+#pragma clang fp contract(off)
+
+#include "qw_device.h"
+#include "qw_internal.h"
+
+namespace qw {
+namespace {
+
+template <int THREADS>
+struct QuantShared {
+    uint32_t red[THREADS / kWave];
+    uint32_t red2[THREADS / kWave];
+    uint32_t hist[256];
+    uint32_t scan[256];
+    uint32_t digit;
+    uint32_t remaining;
+};
+
+template <int THREADS>
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, QuantShared<THREADS> &sh)
+{
+    constexpr int W = THREADS / kWave;
+    v = wave_max_u32(v);
+    const int wave = threadIdx.x / kWave;
+    if (__lane_id() == 0)
+        sh.red[wave] = v;
+    __syncthreads();
+    uint32_t r = sh.red[0];
+#pragma unroll
+    for (int i = 1; i < W; ++i)
+        r = sh.red[i] > r ? sh.red[i] : r;
+    __syncthreads();
+    return r;
+}
+
+// Sum of `a` and min of `b` over the block in one LDS round trip.
+template <int THREADS>
+__device__ __forceinline__ void block_sum_min_u32(uint32_t a, uint32_t b, QuantShared<THREADS> &sh,
+                                                  uint32_t &sum, uint32_t &mn)
+{
+    constexpr int W = THREADS / kWave;
+    a = wave_sum_u32(a);
+    b = wave_min_u32(b);
+    const int wave = threadIdx.x / kWave;
+    if (__lane_id() == 0) {
+        sh.red[wave] = a;
+        sh.red2[wave] = b;
+    }
+    __syncthreads();
+    sum = 0;
+    mn = 0xffffffffu;
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+        sum += sh.red[i];
+        mn = sh.red2[i] < mn ? sh.red2[i] : mn;
+    }
+    __syncthreads();
+}
+
+// Bit pattern of the element of 0-based ascending rank `rank` among the
+// valid |w| patterns held by the block (radix select, 8 bits per pass).
+__device__ __forceinline__ uint32_t abs_bits(float v)
+{
+    return __builtin_bit_cast(uint32_t, v) & 0x7fffffffu; // |w| as ordered bits
+}
+
+template <int THREADS, int VPT>
+__device__ uint32_t block_select_rank(const float (&v)[VPT * 4], const bool (&valid)[VPT],
+                                      uint32_t rank, QuantShared<THREADS> &sh)
+{
+    static_assert(THREADS >= 256, "the digit scan uses one thread per bin");
+    uint32_t prefix = 0, mask = 0, remaining = rank;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        if (tid < 256)
+            sh.hist[tid] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            if (!valid[j])
+                continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t x = abs_bits(v[j * 4 + e]);
+                if ((x & mask) == prefix)
+                    atomicAdd(&sh.hist[(x >> shift) & 255u], 1u);
+            }
+        }
+        __syncthreads();
+        // inclusive scan of the 256 bins (Hillis-Steele in LDS)
+        uint32_t c = 0;
+        if (tid < 256) {
+            c = sh.hist[tid];
+            sh.scan[tid] = c;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int off = 1; off < 256; off <<= 1) {
+            uint32_t add = 0;
+            if (tid < 256 && tid >= off)
+                add = sh.scan[tid - off];
+            __syncthreads();
+            if (tid < 256)
+                sh.scan[tid] += add;
+            __syncthreads();
+        }
+        if (tid < 256) {
+            const uint32_t incl = sh.scan[tid];
+            const uint32_t excl = incl - c;
+            if (excl <= remaining && remaining < incl) {
+                sh.digit = (uint32_t)tid;
+                sh.remaining = remaining - excl;
+            }
+        }
+        __syncthreads();
+        prefix |= sh.digit << shift;
+        mask |= 255u << shift;
+        remaining = sh.remaining;
+        __syncthreads();
+    }
+    return prefix;
+}
+
+template <int THREADS, int VPT, bool PERCENTILE>
+__global__ __launch_bounds__(THREADS) void quantize_rows_kernel(
+    const float *__restrict__ w, int k, int64_t rank_i, double frac_f,
+    int8_t *__restrict__ q, uint16_t *__restrict__ scales)
+{
+    __shared__ QuantShared<THREADS> sh;
+    const int64_t row = blockIdx.x;
+    const int nvec = k >> 2;
+    const float4_t *src = reinterpret_cast<const float4_t *>(w + row * (int64_t)k);
+
+    float v[VPT * 4];
+    bool valid[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int idx = threadIdx.x + j * THREADS;
+        valid[j] = idx < nvec;
+        float4_t f = {0.f, 0.f, 0.f, 0.f};
+        if (valid[j])
+            f = __builtin_nontemporal_load(src + idx);
+        v[j * 4 + 0] = f.x;
+        v[j * 4 + 1] = f.y;
+        v[j * 4 + 2] = f.z;
+        v[j * 4 + 3] = f.w;
+    }
+    float t;
+    if (!PERCENTILE) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int e = 0; e < VPT * 4; ++e) {
+            const uint32_t x = abs_bits(v[e]);
+            m = x > m ? x : m;
+        }
+        t = __builtin_bit_cast(float, block_max_u32<THREADS>(m, sh));
+    } else {
+        const uint32_t ai = block_select_rank<THREADS, VPT>(v, valid, (uint32_t)rank_i, sh);
+        uint32_t le = 0, gt_min = 0xffffffffu;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            if (!valid[j])
+                continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t x = abs_bits(v[j * 4 + e]);
+                le += x <= ai ? 1u : 0u;
+                if (x > ai && x < gt_min)
+                    gt_min = x;
+            }
+        }
+        uint32_t count_le, next_up;
+        block_sum_min_u32<THREADS>(le, gt_min, sh, count_le, next_up);
+        // a[i+1] equals a[i] when more than i+1 values are <= a[i]
+        const uint32_t ai1 = ((uint64_t)rank_i + 1 < (uint64_t)count_le) ? ai : next_up;
+        const double lo = (double)__builtin_bit_cast(float, ai);
+        const double hi = (double)__builtin_bit_cast(float, ai1);
+        const double gap = __dsub_rn(hi, lo);
+        const double step = __dmul_rn(frac_f, gap);
+        t = (float)__dadd_rn(lo, step);
+    }
+
+    const float s32 = __fdiv_rn(t, 127.0f);
+    const uint16_t s16 = f32_to_f16_bits(s32);
+    const float s = f16_bits_to_f32(s16);
+    if (threadIdx.x == 0)
+        scales[row] = s16;
+
+    uint32_t *dst = reinterpret_cast<uint32_t *>(q + row * (int64_t)k);
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int idx = threadIdx.x + j * THREADS;
+        if (!valid[j])
+            continue;
+        uint32_t packed = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            int code = 0;
+            if (s != 0.0f) {
+                float r = __builtin_rintf(__fdiv_rn(v[j * 4 + e], s));
+                r = r > 127.0f ? 127.0f : r;
+                r = r < -127.0f ? -127.0f : r;
+                code = (int)r;
+            }
+            packed |= ((uint32_t)code & 0xffu) << (8 * e);
+        }
+        __builtin_nontemporal_store(packed, dst + idx);
+    }
+}
+
+template <int THREADS, int VPT>
+hipError_t launch_cfg(const float *w, int64_t n, int64_t k, int mode, int64_t rank_i, double frac_f,
+                      int8_t *q, uint16_t *scales, hipStream_t stream)
+{
+    const dim3 grid((unsigned)n), block(THREADS);
+    if (mode == 0)
+        hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, false>), grid, block, 0, stream,
+                           w, (int)k, rank_i, frac_f, q, scales);
+    else
+        hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, true>), grid, block, 0, stream,
+                           w, (int)k, rank_i, frac_f, q, scales);
+    return hipGetLastError();
+}
+
+} // namespace
+
+hipError_t launch_quantize(const float *w, int64_t n, int64_t k, int mode, int64_t rank_i,
+                           double frac_f, int8_t *q, uint16_t *scales, hipStream_t stream)
+{
+    // float4 slots per row; a workgroup of THREADS holds THREADS * VPT of them
+    const int64_t nvec = k / 4;
+    if (nvec <= 256 * 1)
+        return launch_cfg<256, 1>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
+    if (nvec <= 256 * 2)
+        return launch_cfg<256, 2>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
+    if (nvec <= 256 * 4)
+        return launch_cfg<256, 4>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
+    if (nvec <= 256 * 8)
+        return launch_cfg<256, 8>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
+    if (nvec <= 256 * 16)
+        return launch_cfg<256, 16>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
+    if (nvec <= 1024 * 8)
+        return launch_cfg<1024, 8>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
+    return launch_cfg<1024, 16>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
+}
+
+} // namespace qw

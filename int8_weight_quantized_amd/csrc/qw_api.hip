@@ -1,0 +1,175 @@
+// qw_api.hip -- the C ABI of libqw: argument checks, kernel selection and
+// launch on the caller's stream.  No device memory is allocated here or in
+// any kernel launcher; every check runs on the host before anything is
+// enqueued, so a rejected call launches nothing and writes nothing.
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+#include <mutex>
+
+#include "qw.h"
+#include "qw_internal.h"
+
+namespace qw {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+} // namespace
+
+int device_cu_count()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return 256;
+    int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0)
+        return cached;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    g_cu_count[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+} // namespace qw
+
+namespace {
+
+constexpr int64_t kMaxDim = 0x7fffffff;
+
+bool misaligned(const void *p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 15u) != 0;
+}
+
+// Half-open byte ranges [a, a + na) and [b, b + nb) intersect.
+bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb)
+{
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+qw_status launch_status(hipError_t e)
+{
+    return e == hipSuccess ? QW_SUCCESS : QW_ERROR_LAUNCH;
+}
+
+qw_status check_gemm_args(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
+                          int64_t m, int64_t n, int64_t k, bool &noop)
+{
+    noop = false;
+    if (m < 0 || n < 0 || k <= 0)
+        return QW_ERROR_INVALID_VALUE;
+    if (m == 0 || n == 0) {
+        noop = true;
+        return QW_SUCCESS;
+    }
+    if (!x || !q || !scales || !y)
+        return QW_ERROR_INVALID_VALUE;
+    if (k % 16 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim)
+        return QW_ERROR_UNSUPPORTED;
+    if (misaligned(x) || misaligned(q) || misaligned(scales) || misaligned(y))
+        return QW_ERROR_MISALIGNED;
+    const uint64_t ybytes = (uint64_t)m * (uint64_t)n * 2u;
+    if (overlaps(y, ybytes, x, (uint64_t)m * (uint64_t)k * 2u) ||
+        overlaps(y, ybytes, q, (uint64_t)n * (uint64_t)k) ||
+        overlaps(y, ybytes, scales, (uint64_t)n * 2u))
+        return QW_ERROR_INVALID_VALUE;
+    return QW_SUCCESS;
+}
+
+} // namespace
+
+extern "C" {
+
+QW_API qw_status qw_quantize_weights(const float *w, int64_t n, int64_t k, double clip_percentile,
+                                     int8_t *q, uint16_t *scales, void *stream)
+{
+    if (n < 0 || k <= 0)
+        return QW_ERROR_INVALID_VALUE;
+    if (!(clip_percentile > 0.0 && clip_percentile <= 100.0)) // also rejects NaN
+        return QW_ERROR_INVALID_VALUE;
+    if (n == 0)
+        return QW_SUCCESS;
+    if (!w || !q || !scales)
+        return QW_ERROR_INVALID_VALUE;
+    if (k % 16 != 0 || k > QW_QUANTIZE_MAX_K || n > kMaxDim)
+        return QW_ERROR_UNSUPPORTED;
+    if (misaligned(w) || misaligned(q) || misaligned(scales))
+        return QW_ERROR_MISALIGNED;
+    const uint64_t elems = (uint64_t)n * (uint64_t)k;
+    if (overlaps(q, elems, w, elems * 4u) || overlaps(scales, (uint64_t)n * 2u, w, elems * 4u) ||
+        overlaps(scales, (uint64_t)n * 2u, q, elems))
+        return QW_ERROR_INVALID_VALUE;
+
+    // Clip position of the type-7 percentile, in binary64 on the host:
+    // pos = (pct / 100) * (k - 1), i = floor(pos), f = pos - i.
+    int mode = 0;
+    int64_t rank_i = k - 1;
+    double frac_f = 0.0;
+    if (clip_percentile != 100.0) {
+        const double frac_of_range = clip_percentile / 100.0;
+        const double pos = frac_of_range * (double)(k - 1); // no FMA: built with -ffp-contract=off
+        const double i_floor = floor(pos);
+        if ((int64_t)i_floor < k - 1) {
+            mode = 1;
+            rank_i = (int64_t)i_floor;
+            frac_f = pos - i_floor;
+        }
+    }
+    return launch_status(qw::launch_quantize(w, n, k, mode, rank_i, frac_f, q, scales,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+QW_API qw_status qw_w8a16_gemm_path(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                                    uint16_t *y, int64_t m, int64_t n, int64_t k, int path,
+                                    void *stream)
+{
+    if (path != QW_PATH_AUTO && path != QW_PATH_GEMV && path != QW_PATH_MFMA)
+        return QW_ERROR_INVALID_VALUE;
+    bool noop = false;
+    const qw_status st = check_gemm_args(x, q, scales, y, m, n, k, noop);
+    if (st != QW_SUCCESS || noop)
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (path == QW_PATH_AUTO)
+        path = qw::gemv_supported(m, k) ? QW_PATH_GEMV : QW_PATH_MFMA;
+    if (path == QW_PATH_GEMV) {
+        if (!qw::gemv_supported(m, k))
+            return QW_ERROR_UNSUPPORTED;
+        return launch_status(qw::launch_gemv(x, q, scales, y, m, n, k, s));
+    }
+    return launch_status(qw::launch_mfma_gemm(x, q, scales, y, m, n, k, s));
+}
+
+QW_API qw_status qw_w8a16_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                               uint16_t *y, int64_t m, int64_t n, int64_t k, void *stream)
+{
+    return qw_w8a16_gemm_path(x, q, scales, y, m, n, k, QW_PATH_AUTO, stream);
+}
+
+QW_API const char *qw_status_string(qw_status status)
+{
+    switch (status) {
+    case QW_SUCCESS:
+        return "success";
+    case QW_ERROR_INVALID_VALUE:
+        return "invalid value (null pointer, negative size, k == 0, bad percentile or overlapping buffers)";
+    case QW_ERROR_MISALIGNED:
+        return "misaligned pointer (16-byte alignment required)";
+    case QW_ERROR_UNSUPPORTED:
+        return "unsupported size (k % 16 != 0 or a size beyond the documented maximum)";
+    case QW_ERROR_LAUNCH:
+        return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+QW_API int qw_version(void)
+{
+    return 100; // 0.1.0
+}
+
+} // extern "C"

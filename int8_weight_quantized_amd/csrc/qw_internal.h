@@ -1,0 +1,33 @@
+// qw_internal.h -- host-side launchers shared between the translation units
+// of libqw.  Arguments reaching these functions have been validated by the
+// C ABI layer (qw_api.hip); the launchers only pick a kernel configuration
+// and enqueue it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qw {
+
+// Per-row quantizer.  mode 0: absmax bound; mode 1: percentile bound with
+// the rank i (0-based, ascending) and interpolation fraction f computed on
+// the host in binary64 (i < k - 1 in mode 1).
+hipError_t launch_quantize(const float *w, int64_t n, int64_t k, int mode,
+                           int64_t rank_i, double frac_f, int8_t *q,
+                           uint16_t *scales, hipStream_t stream);
+
+// Decode GEMV (VALU dot products).  Requires m <= 8 and
+// m * ceil(k / 1024) <= 32 (the activations fit the LDS budget).
+bool gemv_supported(int64_t m, int64_t k);
+hipError_t launch_gemv(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                       uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream);
+
+// MFMA tiled GEMM, any m, n, k with k % 16 == 0.
+hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                            uint16_t *y, int64_t m, int64_t n, int64_t k,
+                            hipStream_t stream);
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+} // namespace qw

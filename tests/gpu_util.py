@@ -1,0 +1,74 @@
+"""Helpers for the GPU parity tests: move seeded host buffers to the device,
+call the library through its C ABI, bring results back, and compare with the
+oracle on exactly the same host buffers."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+TOL_REL = 2e-3
+TOL_ABS = 1e-3
+
+
+def say(msg: str):
+    """Name the case before each GPU step (flushed, so it survives a crash)."""
+    print("[gpu] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def dev(a: np.ndarray):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def host(t) -> np.ndarray:
+    torch = torch_mod()
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def gpu_quantize(w: np.ndarray, pct: float):
+    """Quantize on the GPU through the C ABI; returns (q int8, scale bits uint16)."""
+    import int8_weight_quantized_amd as qw
+    torch = torch_mod()
+    n, k = w.shape
+    wd = dev(w)
+    qd = torch.full((n, k), 99, dtype=torch.int8, device="cuda:0")
+    sd = torch.full((n,), 0x5555, dtype=torch.int16, device="cuda:0")
+    st = qw.quantize_weights_raw(wd.data_ptr(), n, k, pct, qd.data_ptr(), sd.data_ptr(),
+                                 int(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, qw.status_string(st)
+    return host(qd), host(sd).view(np.uint16)
+
+
+def gpu_gemm(x: np.ndarray, q: np.ndarray, s_bits: np.ndarray, path: int = 0):
+    """W8A16 GEMM on the GPU through the C ABI; returns Y as float16."""
+    import int8_weight_quantized_amd as qw
+    torch = torch_mod()
+    m, k = x.shape
+    n = q.shape[0]
+    xd = dev(np.ascontiguousarray(x, dtype=np.float16).view(np.int16))
+    qd = dev(q)
+    sd = dev(np.ascontiguousarray(s_bits, dtype=np.uint16).view(np.int16))
+    yd = torch.full((m, n), 0x7e00, dtype=torch.int16, device="cuda:0")  # NaN canary
+    st = qw.w8a16_gemm_raw(xd.data_ptr(), qd.data_ptr(), sd.data_ptr(), yd.data_ptr(), m, n, k,
+                           int(torch.cuda.current_stream().cuda_stream), path)
+    assert st == 0, qw.status_string(st)
+    return host(yd).view(np.float16)
+
+
+def assert_gemm_close(y: np.ndarray, ref: np.ndarray, what: str = ""):
+    """max |Y - ref| <= 2e-3 * max|ref| + 1e-3, with ref the binary64 oracle."""
+    y64 = y.astype(np.float64)
+    assert np.all(np.isfinite(y64)), "%s: non-finite output" % what
+    err = np.abs(y64 - ref).max() if ref.size else 0.0
+    tol = TOL_REL * (np.abs(ref).max() if ref.size else 0.0) + TOL_ABS
+    assert err <= tol, "%s: max err %.3g > tol %.3g" % (what, err, tol)
+    return err, tol

@@ -1,0 +1,136 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every symbol the
+header declares, and rejects every invalid call with the documented status
+before touching the GPU (no compute call is made here)."""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qw.h")
+
+qw = pytest.importorskip("int8_weight_quantized_amd")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"QW_API\s+[\w\s\*]+?\b(qw_\w+)\s*\(", text)))
+
+
+def _exported_symbols():
+    out = subprocess.run(["nm", "-D", "--defined-only", qw.LIBRARY_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    return {line.split()[-1] for line in out.splitlines() if line.strip()}
+
+
+def test_header_declares_the_entry_points():
+    decl = _declared_functions()
+    for name in ("qw_quantize_weights", "qw_w8a16_gemm", "qw_w8a16_gemm_path",
+                 "qw_status_string", "qw_version"):
+        assert name in decl
+
+
+def test_library_exports_every_declared_symbol():
+    exported = _exported_symbols()
+    missing = [f for f in _declared_functions() if f not in exported]
+    assert not missing, missing
+    lib = qw.library()
+    for f in _declared_functions():
+        assert hasattr(lib, f)
+
+
+def test_library_is_independent_of_the_oracle():
+    exported = _exported_symbols()
+    assert not any(s.startswith("oracle_") for s in exported)
+    deps = subprocess.run(["ldd", qw.LIBRARY_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in deps
+
+
+def test_status_strings_and_version():
+    assert qw.version() >= 100
+    for st in range(5):
+        assert qw.status_string(st)
+    assert qw.status_string(99) == "unknown status"
+
+
+# Fake, never-dereferenced addresses: every call below must be rejected on the
+# host before anything is enqueued.
+A = 1 << 20      # 16-byte aligned
+B = 2 << 20
+C = 3 << 20
+D = 4 << 20
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, -1, 16, 100.0, B, C), qw.QW_ERROR_INVALID_VALUE),          # n < 0
+    ((A, 4, 0, 100.0, B, C), qw.QW_ERROR_INVALID_VALUE),            # k == 0
+    ((A, 4, -16, 100.0, B, C), qw.QW_ERROR_INVALID_VALUE),          # k < 0
+    ((A, 4, 16, 0.0, B, C), qw.QW_ERROR_INVALID_VALUE),             # pct == 0
+    ((A, 4, 16, 100.0001, B, C), qw.QW_ERROR_INVALID_VALUE),        # pct > 100
+    ((A, 4, 16, float("nan"), B, C), qw.QW_ERROR_INVALID_VALUE),    # pct NaN
+    ((0, 4, 16, 100.0, B, C), qw.QW_ERROR_INVALID_VALUE),           # null w
+    ((A, 4, 16, 100.0, 0, C), qw.QW_ERROR_INVALID_VALUE),           # null q
+    ((A, 4, 16, 100.0, B, 0), qw.QW_ERROR_INVALID_VALUE),           # null scales
+    ((A, 4, 24, 100.0, B, C), qw.QW_ERROR_UNSUPPORTED),             # k % 16
+    ((A, 4, 65536 + 16, 100.0, B, C), qw.QW_ERROR_UNSUPPORTED),     # k too large
+    ((A, 1 << 31, 16, 100.0, B, C), qw.QW_ERROR_UNSUPPORTED),       # n too large
+    ((A + 4, 4, 16, 100.0, B, C), qw.QW_ERROR_MISALIGNED),
+    ((A, 4, 16, 100.0, B + 8, C), qw.QW_ERROR_MISALIGNED),
+    ((A, 4, 16, 100.0, B, C + 2), qw.QW_ERROR_MISALIGNED),
+    ((A, 4, 16, 100.0, A + 64, C), qw.QW_ERROR_INVALID_VALUE),      # q overlaps w
+    ((A, 4, 16, 100.0, B, A + 16), qw.QW_ERROR_INVALID_VALUE),      # scales overlap w
+    ((A, 4, 16, 100.0, B, B + 32), qw.QW_ERROR_INVALID_VALUE),      # scales overlap q
+])
+def test_quantize_rejects(args, status):
+    assert qw.quantize_weights_raw(*args) == status
+
+
+def test_quantize_empty_is_noop():
+    # n == 0: nothing to do, null pointers allowed
+    assert qw.quantize_weights_raw(0, 0, 16, 100.0, 0, 0) == qw.QW_SUCCESS
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, B, C, D, -1, 4, 16), qw.QW_ERROR_INVALID_VALUE),
+    ((A, B, C, D, 1, -4, 16), qw.QW_ERROR_INVALID_VALUE),
+    ((A, B, C, D, 1, 4, 0), qw.QW_ERROR_INVALID_VALUE),
+    ((0, B, C, D, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),
+    ((A, 0, C, D, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),
+    ((A, B, 0, D, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),
+    ((A, B, C, 0, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),
+    ((A, B, C, D, 1, 4, 24), qw.QW_ERROR_UNSUPPORTED),
+    ((A, B, C, D, 1 << 31, 4, 16), qw.QW_ERROR_UNSUPPORTED),
+    ((A, B, C, D, 1, 1 << 31, 16), qw.QW_ERROR_UNSUPPORTED),
+    ((A + 2, B, C, D, 1, 4, 16), qw.QW_ERROR_MISALIGNED),
+    ((A, B + 1, C, D, 1, 4, 16), qw.QW_ERROR_MISALIGNED),
+    ((A, B, C + 8, D, 1, 4, 16), qw.QW_ERROR_MISALIGNED),
+    ((A, B, C, D + 4, 1, 4, 16), qw.QW_ERROR_MISALIGNED),
+    ((A, B, C, A + 16, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),       # y overlaps x
+    ((A, B, C, B, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),            # y overlaps q
+    ((A, B, C, C - 16, 2, 8, 16), qw.QW_ERROR_INVALID_VALUE),       # y overlaps scales
+])
+def test_gemm_rejects(args, status):
+    assert qw.w8a16_gemm_raw(*args) == status
+
+
+def test_gemm_path_checks():
+    assert qw.w8a16_gemm_raw(A, B, C, D, 1, 4, 16, 0, 7) == qw.QW_ERROR_INVALID_VALUE
+    # the GEMV path refuses shapes beyond its LDS budget: m > 8, or m * ceil(k/1024) > 32
+    assert qw.w8a16_gemm_raw(A, B, C, D, 9, 4, 16, 0, 1) == qw.QW_ERROR_UNSUPPORTED
+    assert qw.w8a16_gemm_raw(A, B, C, D, 8, 4, 5 * 1024, 0, 1) == qw.QW_ERROR_UNSUPPORTED
+
+
+def test_gemm_empty_is_noop():
+    assert qw.w8a16_gemm_raw(0, 0, 0, 0, 0, 4, 16) == qw.QW_SUCCESS
+    assert qw.w8a16_gemm_raw(0, 0, 0, 0, 3, 0, 16) == qw.QW_SUCCESS
+
+
+def test_torch_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        qw.quantize_weights(torch.zeros(4, 16))
+    with pytest.raises((TypeError, ValueError)):
+        qw.w8a16_gemm(torch.zeros(1, 16), torch.zeros(4, 16, dtype=torch.int8),
+                      torch.zeros(4, dtype=torch.float16))

@@ -1,0 +1,259 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same
+seeded host buffers.
+
+  * quantizer: int8 codes and fp16 scale bits must be identical (bit-exact);
+  * GEMM: max |Y - ref| <= 2e-3 * max|ref| + 1e-3 against the binary64
+    oracle computed from the same (already bit-identical) codes and scales;
+    the exact-arithmetic case must be bit-exact.
+
+Full workload sizes run in the launch configuration the benchmark times
+(the automatic kernel choice); where the binary64 reference is too slow to
+compute in full, whole output rows, whole output columns and scattered
+points are sampled and computed one by one.
+"""
+
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from gpu_util import assert_gemm_close, gpu_gemm, gpu_quantize, say
+
+pytestmark = pytest.mark.gpu
+
+GEMV, MFMA = 1, 2
+
+
+@functools.lru_cache(maxsize=2)
+def workload_data(name):
+    wl = synthetic.BY_NAME[name]
+    x, w = synthetic.make_inputs(wl)
+    q, s, t = oracle.quantize(w, wl.clip_percentile)
+    return wl, x, w, q, s
+
+
+NAMES = [w.name for w in synthetic.WORKLOADS]
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_quantize_workload_bitexact(name):
+    wl, x, w, q_ref, s_ref = workload_data(name)
+    say("quantize %s n=%d k=%d pct=%g" % (name, wl.n, wl.k, wl.clip_percentile))
+    q, s = gpu_quantize(w, wl.clip_percentile)
+    bad_s = np.nonzero(s != s_ref)[0]
+    assert bad_s.size == 0, "scale mismatch rows %s gpu %s oracle %s" % (bad_s[:5], s[bad_s[:5]], s_ref[bad_s[:5]])
+    bad = np.argwhere(q != q_ref)
+    assert bad.size == 0, "code mismatch at %s" % (bad[:5],)
+
+
+def _sample_indices(m, n, rng, rows=6, cols=6, points=4096):
+    # whole output rows, whole output columns, scattered points
+    mr = np.unique(np.r_[0, m - 1, rng.integers(0, m, rows)])
+    mi = [np.repeat(mr, n)]
+    ni = [np.tile(np.arange(n), len(mr))]
+    nc = np.unique(np.r_[0, n - 1, rng.integers(0, n, cols)])
+    mi.append(np.tile(np.arange(m), len(nc)))
+    ni.append(np.repeat(nc, m))
+    mi.append(rng.integers(0, m, points))
+    ni.append(rng.integers(0, n, points))
+    return np.concatenate(mi), np.concatenate(ni)
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_gemm_workload(name):
+    wl, x, w, q, s = workload_data(name)
+    say("gemm auto %s m=%d n=%d k=%d" % (name, wl.m, wl.n, wl.k))
+    y = gpu_gemm(x, q, s)
+    if wl.m * wl.n * wl.k <= 4e8:
+        ref = oracle.gemm(x, q, s)
+        assert_gemm_close(y, ref, name)
+    else:
+        mi, ni = _sample_indices(wl.m, wl.n, np.random.default_rng(123))
+        ref = oracle.gemm_sampled(x, q, s, mi, ni)
+        assert_gemm_close(y[mi, ni], ref, name + " (sampled)")
+        assert np.all(np.isfinite(y.astype(np.float32))), "non-finite output outside the sample"
+
+
+# Shapes spanning several tiles with ragged tails in m, n and k.
+SMALL_SHAPES = [
+    (1, 1000, 272), (1, 129, 1040), (2, 300, 2064), (3, 257, 528), (4, 64, 16),
+    (5, 77, 4096), (7, 130, 1024), (8, 517, 2064), (4, 33, 4112),
+]
+MFMA_SHAPES = SMALL_SHAPES + [
+    (9, 200, 272), (16, 128, 64), (17, 300, 528), (31, 129, 80), (33, 257, 1024),
+    (64, 256, 256), (65, 130, 96), (100, 390, 656), (128, 128, 4096), (130, 260, 4112),
+    (257, 129, 144), (300, 513, 1040),
+]
+
+
+def _small_case(m, n, k, seed):
+    x = synthetic.random_x(m, k, seed)
+    w = synthetic.random_w(n, k, seed + 1)
+    q, s, _ = oracle.quantize(w, 100.0)
+    return x, q, s
+
+
+@pytest.mark.parametrize("m,n,k", SMALL_SHAPES)
+def test_gemv_small_shapes(m, n, k):
+    x, q, s = _small_case(m, n, k, seed=m * 1000 + n)
+    say("gemm gemv m=%d n=%d k=%d" % (m, n, k))
+    y = gpu_gemm(x, q, s, path=GEMV)
+    assert_gemm_close(y, oracle.gemm(x, q, s), "gemv %dx%dx%d" % (m, n, k))
+
+
+@pytest.mark.parametrize("m,n,k", MFMA_SHAPES)
+def test_mfma_small_shapes(m, n, k):
+    x, q, s = _small_case(m, n, k, seed=m * 1000 + n)
+    say("gemm mfma m=%d n=%d k=%d" % (m, n, k))
+    y = gpu_gemm(x, q, s, path=MFMA)
+    assert_gemm_close(y, oracle.gemm(x, q, s), "mfma %dx%dx%d" % (m, n, k))
+
+
+@pytest.mark.parametrize("path", [GEMV, MFMA])
+@pytest.mark.parametrize("m,n,k", [(1, 96, 512), (4, 200, 1024), (8, 130, 2048)])
+def test_gemm_exact_arithmetic_bitexact(path, m, n, k):
+    """X in {-1,0,1}, power-of-two scales: every partial sum is exact in fp32,
+    so Y must be the fp16 rounding of the exact value, bit for bit."""
+    rng = np.random.default_rng(m + n + k)
+    x = rng.integers(-1, 2, size=(m, k)).astype(np.float16)
+    q = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+    e = rng.integers(0, 11, size=n)
+    s = (2.0 ** (-e)).astype(np.float16).view(np.uint16)
+    say("gemm exact path=%d m=%d n=%d k=%d" % (path, m, n, k))
+    y = gpu_gemm(x, q, s, path=path)
+    want = oracle.f64_to_f16_bits(oracle.gemm(x, q, s))
+    assert np.array_equal(y.view(np.uint16), want)
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 8])
+def test_paths_agree_with_oracle_at_same_m(m):
+    wl = synthetic.BY_NAME["small_batch_m8_k4096_n4608"]
+    x = synthetic.random_x(m, wl.k, 77)
+    _, _, _, q, s = workload_data(wl.name)
+    ref = oracle.gemm(x, q, s)
+    for path in (GEMV, MFMA):
+        say("gemm path=%d m=%d n=%d k=%d" % (path, m, wl.n, wl.k))
+        assert_gemm_close(gpu_gemm(x, q, s, path=path), ref, "path %d m %d" % (path, m))
+
+
+def test_gemm_deterministic():
+    wl, x, w, q, s = workload_data("small_batch_m8_k4096_n4608")
+    say("gemm determinism")
+    for path in (GEMV, MFMA):
+        a = gpu_gemm(x, q, s, path=path)
+        b = gpu_gemm(x, q, s, path=path)
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_gemm_zero_activation_and_zero_rows():
+    rng = np.random.default_rng(5)
+    m, n, k = 5, 70, 320
+    w = synthetic.random_w(n, k, 9)
+    w[3] = 0.0
+    q, s, _ = oracle.quantize(w, 100.0)
+    x = rng.standard_normal((m, k)).astype(np.float16)
+    x[2] = 0.0
+    for path in (GEMV, MFMA):
+        say("gemm zeros path=%d" % path)
+        y = gpu_gemm(x, q, s, path=path)
+        assert np.all(y[2].view(np.uint16) == 0) and np.all(y[:, 3].view(np.uint16) == 0)
+        assert_gemm_close(y, oracle.gemm(x, q, s), "zeros")
+
+
+# ---------------------------------------------------------------------------
+# quantizer edge cases
+# ---------------------------------------------------------------------------
+
+def _check_quant(w, pct, what):
+    say("quantize %s n=%d k=%d pct=%r" % (what, w.shape[0], w.shape[1], pct))
+    q_ref, s_ref, _ = oracle.quantize(w, pct)
+    q, s = gpu_quantize(w, pct)
+    assert np.array_equal(s, s_ref), "%s: scales differ at rows %s" % (what, np.nonzero(s != s_ref)[0][:5])
+    assert np.array_equal(q, q_ref), "%s: codes differ at %s" % (what, np.argwhere(q != q_ref)[:5])
+
+
+def test_quantize_degenerate_rows():
+    k = 64
+    w = np.zeros((8, k), dtype=np.float32)
+    w[1, 5] = -3.0e-3
+    w[2, :] = 7.0e-2
+    w[3, :4] = np.float32(1e-9)          # scale underflows fp16 -> 0
+    w[4, :] = np.float32(2.0**-10)       # subnormal fp16 scale
+    w[4, ::3] = -np.float32(3 * 2.0**-12)
+    w[5, 0] = np.float32(1.0e7)          # scale overflows fp16 -> inf, codes 0
+    w[5, 1] = np.float32(1.0)
+    w[6, :] = -0.0                       # negative zeros
+    w[7, :] = np.float32(1.5e-41)        # binary32 subnormal weights
+    for pct in (100.0, 99.0, 50.0, 1.0):
+        _check_quant(w, pct, "degenerate")
+
+
+def test_quantize_exact_ties():
+    """Weights exactly on (j + 1/2) * S: round-half-to-even decides."""
+    js = np.arange(-127, 127, dtype=np.float64)
+    rows = []
+    for sv in (0.000634, 0.0009766, 0.00047, 0.0008):
+        s16 = float(np.float16(sv))
+        row = np.concatenate([(js + 0.5) * s16, [127.0 * s16], np.zeros(17)]).astype(np.float32)
+        rows.append(row)
+    _check_quant(np.stack(rows), 100.0, "ties")
+
+
+@pytest.mark.parametrize("k", [16, 32, 1040, 4096 + 16, 16384, 65536])
+@pytest.mark.parametrize("pct", [100.0, 99.99, 90.0, 50.0, 0.5])
+def test_quantize_sizes_and_percentiles(k, pct):
+    n = 37 if k <= 16384 else 5
+    w = synthetic.random_w(n, k, seed=k)
+    rng = np.random.default_rng(k)
+    # heavy-tailed entries so the percentile clips something
+    idx = rng.choice(n * k, size=max(1, n * k // 500), replace=False)
+    w.reshape(-1)[idx] *= np.float32(10.0)
+    w[0, : k // 2] = 0.0  # a row whose low ranks are all equal
+    _check_quant(w, pct, "sizes")
+
+
+@pytest.mark.parametrize("pct", [99.9999999, 100.0 - 1e-13, 33.333333333, 1e-6])
+def test_quantize_percentile_position_edges(pct):
+    w = synthetic.random_w(9, 48, seed=3)
+    _check_quant(w, pct, "pct-edge")
+
+
+def test_quantize_deterministic():
+    wl, x, w, q, s = workload_data("transformer_big_ffn_outliers_m4096_k1024_n4096")
+    say("quantize determinism")
+    a = gpu_quantize(w, wl.clip_percentile)
+    b = gpu_quantize(w, wl.clip_percentile)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_empty_calls_write_nothing():
+    import int8_weight_quantized_amd as qw
+    torch = pytest.importorskip("torch")
+    say("empty calls")
+    y = torch.full((3, 5), 7, dtype=torch.int16, device="cuda:0")
+    x = torch.zeros((3, 16), dtype=torch.float16, device="cuda:0")
+    q = torch.zeros((5, 16), dtype=torch.int8, device="cuda:0")
+    s = torch.zeros((5,), dtype=torch.float16, device="cuda:0")
+    assert qw.w8a16_gemm_raw(x.data_ptr(), q.data_ptr(), s.data_ptr(), y.data_ptr(), 0, 5, 16) == 0
+    assert qw.w8a16_gemm_raw(x.data_ptr(), q.data_ptr(), s.data_ptr(), y.data_ptr(), 3, 0, 16) == 0
+    torch.cuda.synchronize()
+    assert torch.all(y == 7)
+
+
+def test_torch_binding_on_side_stream():
+    import int8_weight_quantized_amd as qw
+    torch = pytest.importorskip("torch")
+    say("torch binding on a side stream")
+    wl, x, w, q_ref, s_ref = workload_data("tiny_m1_k256_n512")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        wd = torch.from_numpy(w).to("cuda:0", non_blocking=False)
+        xd = torch.from_numpy(x).to("cuda:0")
+        q, s = qw.quantize_weights(wd)
+        y = qw.w8a16_gemm(xd, q, s)
+    stream.synchronize()
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(s.cpu().numpy().view(np.uint16), s_ref)
+    assert_gemm_close(y.cpu().numpy(), oracle.gemm(x, q_ref, s_ref), "binding")
