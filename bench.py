@@ -44,6 +44,7 @@ KERNEL_SOURCES = {
     "quantize": ["quantize.hip", "qw_device.h"],
     "gemv": ["gemv.hip", "qw_device.h"],
     "mfma": ["gemm_mfma.hip", "qw_device.h"],
+    "skinny": ["gemm_skinny.hip", "qw_device.h"],
 }
 
 
@@ -83,13 +84,9 @@ def measured_traffic(kernel, workload):
     return ent.get("hbm_bytes_per_launch")
 
 
-def gemm_kernel_name(m, k):
-    import int8_weight_quantized_amd  # noqa: F401  (path choice mirrors the library's rule)
-    chunks = -(-k // 1024)
-    mt = 1
-    while mt < m:
-        mt <<= 1
-    return "gemv" if (1 <= m <= 8 and mt * chunks <= 32) else "mfma"
+def gemm_kernel_name(m, n, k):
+    import int8_weight_quantized_amd as qw
+    return qw.auto_path(m, n, k)
 
 
 def rotation_count(bytes_per_set, minimum=2, cap=64):
@@ -210,6 +207,53 @@ def cpu_baseline(wl, target_s=10.0, max_s=30.0):
                       % (steps, wl.name, el, per_step)}
 
 
+def sweep_paths(ms=(1, 2, 4, 8, 16, 32, 64, 128, 256, 512),
+                shapes=((4096, 27392), (4096, 4608), (1024, 4096))):
+    """Cold timing of each GEMM kernel across m (random codes; timing only)."""
+    import torch
+
+    import int8_weight_quantized_amd as qw
+    stream = int(torch.cuda.current_stream().cuda_stream)
+    for (k, n) in shapes:
+        for m in ms:
+            gbytes = gemm_bytes(m, n, k)
+            sets = rotation_count(gbytes)
+            g = torch.Generator(device="cuda:0").manual_seed(m)
+            q = [torch.randint(-127, 128, (n, k), dtype=torch.int8, device="cuda:0", generator=g)
+                 for _ in range(sets)]
+            s = [torch.rand((n,), device="cuda:0", generator=g).half() * 1e-3 for _ in range(sets)]
+            x = [torch.randn((m, k), device="cuda:0", generator=g).half() for _ in range(sets)]
+            y = [torch.empty((m, n), dtype=torch.float16, device="cuda:0") for _ in range(sets)]
+            for name, path in (("gemv", 1), ("skinny", 3), ("mfma", 2)):
+                if name == "skinny" and m > 64:
+                    continue
+
+                def launch(i):
+                    return qw.w8a16_gemm_raw(x[i].data_ptr(), q[i].data_ptr(), s[i].data_ptr(),
+                                             y[i].data_ptr(), m, n, k, stream, path)
+                if launch(0) != 0:
+                    continue
+                for it in range(5):
+                    launch(it % sets)
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(30)]
+                torch.cuda.synchronize()
+                for it in range(30):
+                    ev[it][0].record()
+                    launch(it % sets)
+                    ev[it][1].record()
+                torch.cuda.synchronize()
+                ms_ = sorted(a.elapsed_time(b) for a, b in ev)
+                avg = sum(ms_) / len(ms_)
+                print(json.dumps({"sweep": "gemm_paths", "k": k, "n": n, "m": m, "kernel": name,
+                                  "auto": qw.auto_path(m, n, k), "avg_us": avg * 1e3,
+                                  "median_us": ms_[len(ms_) // 2] * 1e3,
+                                  "TBps": gbytes / (avg * 1e-3) / 1e12,
+                                  "TFLOPs": gemm_flops(m, n, k) / (avg * 1e-3) / 1e12}), flush=True)
+            del q, s, x, y
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,6 +263,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the cold GEMM-only figures")
     ap.add_argument("--only-step", action="store_true", help="time the full steps only (for profiling)")
+    ap.add_argument("--sweep-paths", action="store_true",
+                    help="only time every GEMM kernel over a range of m (decode -> prefill "
+                         "crossover), one JSON line per (shape, m, kernel)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain elementwise copy of MIB MiB (fp16 negate, 5 launches) so "
+                         "that HBM counters can be scaled against a kernel of known traffic")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -233,6 +283,21 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
+    if args.calibrate_copy:
+        nbytes = args.calibrate_copy << 20
+        src = torch.ones(nbytes // 2, dtype=torch.float16, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": nbytes, "calibrate_copy_bytes_written": nbytes,
+                          "launches": 5}), flush=True)
+        return
+
+    if args.sweep_paths:
+        sweep_paths()
+        return
+
     wl = synthetic.BY_NAME[args.workload]
     per_set = quant_bytes(wl.n, wl.k) + gemm_bytes(wl.m, wl.n, wl.k)
     sets = rotation_count(per_set)
@@ -240,7 +305,7 @@ def main():
     ms_step, q_ms, g_ms = time_full_steps(runner, args.steps, args.warmup)
 
     qb, gb = quant_bytes(wl.n, wl.k), gemm_bytes(wl.m, wl.n, wl.k)
-    gname = gemm_kernel_name(wl.m, wl.k)
+    gname = gemm_kernel_name(wl.m, wl.n, wl.k)
     value = (qb + gb) / (ms_step * 1e-3) / 1e12
     kernels = {
         "quantize": {"avg_us": q_ms * 1e3, "algorithmic_bytes": qb,
@@ -267,7 +332,7 @@ def main():
             r = StepRunner(other, rotation_count(gbytes), with_weights=False)
             avg_ms, med_ms = time_gemm_only(r, launches=40, warmup=10)
             fl = gemm_flops(other.m, other.n, other.k)
-            kname = gemm_kernel_name(other.m, other.k)
+            kname = gemm_kernel_name(other.m, other.n, other.k)
             ent = {"workload": other.name, "kernel": kname, "cold_sets": r.sets,
                    "avg_us": avg_ms * 1e3, "median_us": med_ms * 1e3,
                    "TBps": gbytes / (avg_ms * 1e-3) / 1e12,

@@ -124,8 +124,9 @@ QW_API qw_status qw_quantize_weights(const float *w, int64_t n, int64_t k,
  *   k       reduction length, k >= 16, k % 16 == 0, k <= INT32_MAX
  *   stream  hipStream_t
  *
- * The kernel is chosen from m (and k): a bandwidth-bound GEMV for decode
- * shapes, MFMA tiled GEMM for prefill shapes.
+ * The kernel is chosen from m (and k): a bandwidth-bound VALU GEMV for
+ * decode (m <= 2), a skinny MFMA kernel on register-dequantized weights for
+ * a few activation rows (m <= 32), and the LDS-tiled MFMA GEMM for prefill.
  *
  * Errors: QW_ERROR_INVALID_VALUE (null pointer with m, n > 0, negative
  * size, k <= 0, y overlapping x, q or scales), QW_ERROR_UNSUPPORTED
@@ -138,9 +139,10 @@ QW_API qw_status qw_w8a16_gemm(const uint16_t *x, const int8_t *q,
 
 /* Kernel selection for qw_w8a16_gemm_path. */
 typedef enum qw_gemm_path {
-    QW_PATH_AUTO = 0,  /* what qw_w8a16_gemm does */
-    QW_PATH_GEMV = 1,  /* VALU dot products, weights streamed once (m <= 8) */
-    QW_PATH_MFMA = 2   /* MFMA tiled GEMM, int8 tiles dequantized into LDS */
+    QW_PATH_AUTO = 0,   /* what qw_w8a16_gemm does */
+    QW_PATH_GEMV = 1,   /* VALU dot products, weights streamed once (m <= 8) */
+    QW_PATH_MFMA = 2,   /* MFMA tiled GEMM, int8 tiles dequantized into LDS */
+    QW_PATH_SKINNY = 3  /* MFMA on weights dequantized in registers, 16 activation rows per pass */
 } qw_gemm_path;
 
 /*
@@ -155,6 +157,13 @@ QW_API qw_status qw_w8a16_gemm_path(const uint16_t *x, const int8_t *q,
                                     const uint16_t *scales, uint16_t *y,
                                     int64_t m, int64_t n, int64_t k, int path,
                                     void *stream);
+
+/*
+ * qw_w8a16_gemm_auto_path -- the QW_PATH_* kernel qw_w8a16_gemm would run
+ * for this shape (for benchmarks and logs).  Returns -1 for shapes the GEMM
+ * rejects (m, n < 0, k <= 0, k % 16 != 0).
+ */
+QW_API int qw_w8a16_gemm_auto_path(int64_t m, int64_t n, int64_t k);
 
 /* A static, human-readable name for a status code (never NULL). */
 QW_API const char *qw_status_string(qw_status status);

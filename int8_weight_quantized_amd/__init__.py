@@ -32,7 +32,7 @@ QW_ERROR_MISALIGNED = 2
 QW_ERROR_UNSUPPORTED = 3
 QW_ERROR_LAUNCH = 4
 
-PATHS = {"auto": 0, "gemv": 1, "mfma": 2}
+PATHS = {"auto": 0, "gemv": 1, "mfma": 2, "skinny": 3}
 QUANTIZE_MAX_K = 65536
 
 
@@ -64,6 +64,8 @@ def _load():
     lib.qw_w8a16_gemm_path.restype = ctypes.c_int
     lib.qw_status_string.argtypes = [ctypes.c_int]
     lib.qw_status_string.restype = ctypes.c_char_p
+    lib.qw_w8a16_gemm_auto_path.argtypes = [i64, i64, i64]
+    lib.qw_w8a16_gemm_auto_path.restype = ctypes.c_int
     lib.qw_version.argtypes = []
     lib.qw_version.restype = ctypes.c_int
     _lib_handle = lib
@@ -81,6 +83,17 @@ def status_string(status: int) -> str:
 
 def version() -> int:
     return int(library().qw_version())
+
+
+PATH_NAMES = {0: "auto", 1: "gemv", 2: "mfma", 3: "skinny"}
+
+
+def auto_path(m: int, n: int, k: int) -> str:
+    """Name of the kernel qw_w8a16_gemm runs for this shape."""
+    p = int(library().qw_w8a16_gemm_auto_path(m, n, k))
+    if p < 0:
+        raise ValueError("unsupported GEMM shape m=%d n=%d k=%d" % (m, n, k))
+    return PATH_NAMES[p]
 
 
 # ---------------------------------------------------------------------------
@@ -153,7 +166,7 @@ def quantize_weights(w, clip_percentile: float = 100.0, out=None):
 
 def w8a16_gemm(x, q, scales, out=None, path: str = "auto"):
     """Y = X * dequant(q)^T: x cuda fp16 [M, K], q int8 [N, K], scales fp16 [N]
-    -> fp16 [M, N].  ``path`` forces a kernel ("gemv" or "mfma")."""
+    -> fp16 [M, N].  ``path`` forces a kernel ("gemv", "skinny" or "mfma")."""
     torch = _torch()
     _check(x, "x", torch.float16, 2)
     _check(q, "q", torch.int8, 2)
@@ -180,4 +193,5 @@ def w8a16_gemm(x, q, scales, out=None, path: str = "auto"):
 
 
 __all__ = ["quantize_weights", "w8a16_gemm", "QwError", "status_string", "version", "library",
+           "auto_path",
            "quantize_weights_raw", "w8a16_gemm_raw", "PATHS", "LIBRARY_PATH"]

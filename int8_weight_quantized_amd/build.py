@@ -40,6 +40,7 @@ UNITS = {
     "quantize.hip": ["-ffp-contract=off"],
     "gemv.hip": [],
     "gemm_mfma.hip": [],
+    "gemm_skinny.hip": [],
 }
 
 

@@ -1,0 +1,124 @@
+// gemm_skinny.hip -- W8A16 skinny GEMM (a few activation rows) on the matrix
+// cores (gfx950).
+//
+// Between decode (one token) and prefill (max_length tokens) the matmul has
+// a handful of activation rows: the weight stream from HBM still sets the
+// time ("探索ChatGLM2在算能BM1684X上INT8量化部署", section 4: small left
+// matrix => bound by loading the right matrix), but the per-row VALU dot
+// products of the GEMV path grow with m.  Here the contraction runs on
+// v_mfma_f32_16x16x32_f16 instead: the int8 weights go straight from HBM
+// into registers (16-byte nontemporal loads), are cast to fp16 exactly in
+// registers and used as the MFMA "A" operand; the activations are the "B"
+// operand (16 columns, rows beyond m are zero).  No LDS staging of weights.
+//
+// Work split: a workgroup of KSPLIT waves owns 16 weight rows; wave w walks
+// the k range [w*K/KSPLIT, (w+1)*K/KSPLIT) (64-aligned) in steps of 64.  In
+// one step lane l (row r = l % 16, group g = l / 16) loads bytes
+// [k + 16 g, +16) of row r: the first 8 codes feed one MFMA (k slots
+// 8 g .. 8 g + 7 of a 32-wide k block), the last 8 feed a second one, and
+// the activation operand is loaded with the same k assignment, so each MFMA
+// contracts exactly the 32 k values its two operands agree on.  UNROLL
+// steps are issued before any is consumed to keep enough bytes in flight.
+// The KSPLIT partial tiles are summed in LDS in wave order (deterministic),
+// then scaled, rounded to fp16 and stored.
+#include "qw_device.h"
+#include "qw_internal.h"
+
+namespace qw {
+namespace {
+
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+constexpr int kSkinnyKSplit = 4;
+constexpr int kSkinnyThreads = kSkinnyKSplit * kWave;
+constexpr int kSkinnyUnroll = 4;
+
+template <int MT>
+__global__ __launch_bounds__(kSkinnyThreads) void skinny_gemm_kernel(
+    const uint16_t *__restrict__ x, const int8_t *__restrict__ q,
+    const uint16_t *__restrict__ scales, uint16_t *__restrict__ y,
+    int m, int n, int k)
+{
+    static_assert(MT == 16, "one 16-column MFMA tile of activations");
+    __shared__ float4v partial[kSkinnyKSplit][kWave];
+
+    const int lane = __lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int r = lane % 16;
+    const int g = lane / 16;
+    const int n0 = blockIdx.x * 16;
+    const int m0 = blockIdx.y * 16;
+    const int row = n0 + r;
+    const int col = m0 + r; // activation row this lane feeds into the B operand
+
+    // k range of this wave, in whole 64-wide steps
+    const int steps_total = (k + 63) / 64;
+    const int s_begin = (int)(((int64_t)wave * steps_total) / kSkinnyKSplit);
+    const int s_end = (int)(((int64_t)(wave + 1) * steps_total) / kSkinnyKSplit);
+
+    const int8_t *qrow = q + (int64_t)(row < n ? row : 0) * k;
+    const uint16_t *xrow = x + (int64_t)(col < m ? col : 0) * k;
+    const bool row_ok = row < n;
+    const bool col_ok = col < m;
+
+    float4v acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = s_begin; s < s_end; s += kSkinnyUnroll) {
+        u32x4_t wv[kSkinnyUnroll];
+        u32x4_t xa[kSkinnyUnroll], xb[kSkinnyUnroll];
+#pragma unroll
+        for (int u = 0; u < kSkinnyUnroll; ++u) {
+            const int kk = (s + u) * 64 + g * 16;
+            const bool ok = (s + u) < s_end && kk < k;
+            wv[u] = (u32x4_t){0u, 0u, 0u, 0u};
+            xa[u] = (u32x4_t){0u, 0u, 0u, 0u};
+            xb[u] = (u32x4_t){0u, 0u, 0u, 0u};
+            if (ok && row_ok)
+                wv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(qrow + kk));
+            if (ok && col_ok) {
+                xa[u] = *reinterpret_cast<const u32x4_t *>(xrow + kk);
+                xb[u] = *reinterpret_cast<const u32x4_t *>(xrow + kk + 8);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kSkinnyUnroll; ++u) {
+            const half8_t a0 = i8x8_to_half8(wv[u].x, wv[u].y);
+            const half8_t a1 = i8x8_to_half8(wv[u].z, wv[u].w);
+            const half8_t b0 = __builtin_bit_cast(half8_t, xa[u]);
+            const half8_t b1 = __builtin_bit_cast(half8_t, xb[u]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, acc, 0, 0, 0);
+        }
+    }
+
+    partial[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0)
+        return;
+    float4v sum = partial[0][lane];
+#pragma unroll
+    for (int w = 1; w < kSkinnyKSplit; ++w)
+        sum += partial[w][lane];
+    // lane holds rows n0 + 4 g + i (i = 0..3) of activation column m0 + r
+    const int ym = m0 + r;
+    if (ym >= m)
+        return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int yn = n0 + 4 * g + i;
+        if (yn < n)
+            y[(int64_t)ym * n + yn] = f32_to_f16_bits(sum[i] * f16_bits_to_f32(scales[yn]));
+    }
+}
+
+} // namespace
+
+hipError_t launch_skinny_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                              uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((n + 15) / 16), (unsigned)((m + 15) / 16));
+    hipLaunchKernelGGL((skinny_gemm_kernel<16>), grid, dim3(kSkinnyThreads), 0, stream,
+                       x, q, scales, y, (int)m, (int)n, (int)k);
+    return hipGetLastError();
+}
+
+} // namespace qw

@@ -9,18 +9,27 @@
 // byte-permute trick, and dotted with fp16 activations on v_dot2_f32_f16
 // (fp32 accumulation).  The per-channel scale multiplies the fp32 sum.
 //
-// Work split: a workgroup of 4 waves stages X (m rows, fp16) in LDS once;
-// each wave then owns groups of RU consecutive weight rows and walks the
-// whole k range of those rows: lane l reads bytes [c*1024 + 16 l, +16) of
-// each row for chunk c, i.e. every load instruction of the wave covers 1 KiB
-// of one row, fully coalesced.  The RU*M per-lane partial sums are combined
-// with a transposing butterfly (about RU*M shuffles instead of 6*RU*M).
+// Work split.  The grid is sized to what the chip holds at once; wave w
+// owns the contiguous weight rows [w*N/W, (w+1)*N/W) (balanced to one row),
+// walked in groups of RU rows.  For one group, lane l reads bytes
+// [c*1024 + 16 l, +16) of each row for every 1 KiB chunk c, so each load
+// instruction of the wave covers 1 KiB of one row, fully coalesced.  Loads
+// are software-pipelined: the next item's RU x CH 16-byte loads (CH chunks
+// of RU rows) are issued before the current item is dequantized and
+// multiplied, so every wave keeps two items in flight.  X (m rows, fp16) is
+// staged once per workgroup in LDS, after the first loads have been issued.
+// The RU*M per-lane partial sums are combined with a transposing butterfly
+// (about RU*M shuffles instead of 6*RU*M).
 //
 // LDS layout of X: [m][chunk][half h][lane] x 16 bytes, where entry
 // (m, c, h, l) holds x[m][c*1024 + 16 l + 8 h .. +7].  Lane l reads
 // consecutive 16-byte slots for h = 0 and h = 1: no bank conflicts.
 #include "qw_device.h"
 #include "qw_internal.h"
+
+#ifndef QW_GEMV_WAVES_PER_CU
+#define QW_GEMV_WAVES_PER_CU 8
+#endif
 
 namespace qw {
 namespace {
@@ -30,18 +39,54 @@ constexpr int kGemvWaves = kGemvThreads / kWave;
 constexpr int kChunkK = kWave * 16; // k values covered by one wave-wide 16-byte load
 constexpr int kGemvMaxMChunks = 32; // LDS budget: 32 * 2 KiB = 64 KiB
 
-template <int MT, int RU>
+template <int MT, int RU, int CH>
+struct GemvItem {
+    u32x4_t w[RU][CH];
+};
+
+template <int MT, int RU, int CH>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     const uint16_t *__restrict__ x, const int8_t *__restrict__ q,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y,
-    int m, int n, int k, int chunks, int groups)
+    int m, int n, int k, int chunks, int total_waves)
 {
     extern __shared__ u32x4_t xs[];
     const int tid = threadIdx.x;
     const int lane = __lane_id();
     const int wave = tid / kWave;
+    const int gw = blockIdx.x * kGemvWaves + wave;
 
-    // ---- stage X into LDS (rows m..MT-1 are zero) ----
+    // this wave's rows and items (an item = RU rows x CH chunks)
+    const int row_begin = (int)(((int64_t)gw * n) / total_waves);
+    const int row_end = (int)(((int64_t)(gw + 1) * n) / total_waves);
+    const int groups = (row_end - row_begin + RU - 1) / RU;
+    const int batches = (chunks + CH - 1) / CH;
+    const int items = gw < total_waves ? groups * batches : 0;
+
+    auto issue = [&](int it, GemvItem<MT, RU, CH> &dst) {
+        const int g = it / batches;
+        const int b = it - g * batches;
+        const int row0 = row_begin + g * RU;
+#pragma unroll
+        for (int r = 0; r < RU; ++r) {
+#pragma unroll
+            for (int cc = 0; cc < CH; ++cc) {
+                const int c = b * CH + cc;
+                const int kk = c * kChunkK + lane * 16;
+                const int row = row0 + r;
+                dst.w[r][cc] = (u32x4_t){0u, 0u, 0u, 0u};
+                if (row < row_end && kk < k)
+                    dst.w[r][cc] = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4_t *>(q + (int64_t)row * k + kk));
+            }
+        }
+    };
+
+    GemvItem<MT, RU, CH> buf0, buf1;
+    if (items > 0)
+        issue(0, buf0);
+
+    // ---- stage X into LDS (rows m..MT-1 are zero) while the loads fly ----
     const int entries = MT * chunks * 2 * kWave;
     for (int e = tid; e < entries; e += kGemvThreads) {
         const int l = e % kWave;
@@ -58,44 +103,38 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     __syncthreads();
 
     constexpr int R = RU * MT;
-    for (int g = blockIdx.x * kGemvWaves + wave; g < groups; g += gridDim.x * kGemvWaves) {
-        const int row0 = g * RU;
-        float acc[R];
-#pragma unroll
-        for (int i = 0; i < R; ++i)
-            acc[i] = 0.0f;
+    float acc[R];
 
-#pragma unroll 2
-        for (int c = 0; c < chunks; ++c) {
-            const int kk = c * kChunkK + lane * 16;
-            if (kk < k) {
-                u32x4_t wv[RU];
+    auto consume = [&](int it, const GemvItem<MT, RU, CH> &cur) {
+        const int g = it / batches;
+        const int b = it - g * batches;
+        if (b == 0) {
 #pragma unroll
-                for (int r = 0; r < RU; ++r) {
-                    const int row = row0 + r;
-                    wv[r] = (u32x4_t){0u, 0u, 0u, 0u};
-                    if (row < n)
-                        wv[r] = __builtin_nontemporal_load(
-                            reinterpret_cast<const u32x4_t *>(q + (int64_t)row * k + kk));
-                }
+            for (int i = 0; i < R; ++i)
+                acc[i] = 0.0f;
+        }
+#pragma unroll
+        for (int cc = 0; cc < CH; ++cc) {
+            const int c = b * CH + cc;
+            if (c < chunks) {
                 half2_t xv[MT][8];
 #pragma unroll
                 for (int mm = 0; mm < MT; ++mm) {
                     const u32x4_t a = xs[((mm * chunks + c) * 2 + 0) * kWave + lane];
-                    const u32x4_t b = xs[((mm * chunks + c) * 2 + 1) * kWave + lane];
+                    const u32x4_t bb = xs[((mm * chunks + c) * 2 + 1) * kWave + lane];
                     xv[mm][0] = as_half2(a.x);
                     xv[mm][1] = as_half2(a.y);
                     xv[mm][2] = as_half2(a.z);
                     xv[mm][3] = as_half2(a.w);
-                    xv[mm][4] = as_half2(b.x);
-                    xv[mm][5] = as_half2(b.y);
-                    xv[mm][6] = as_half2(b.z);
-                    xv[mm][7] = as_half2(b.w);
+                    xv[mm][4] = as_half2(bb.x);
+                    xv[mm][5] = as_half2(bb.y);
+                    xv[mm][6] = as_half2(bb.z);
+                    xv[mm][7] = as_half2(bb.w);
                 }
 #pragma unroll
                 for (int r = 0; r < RU; ++r) {
                     half2_t hw[8];
-                    i8x16_to_half2x8(wv[r], hw);
+                    i8x16_to_half2x8(cur.w[r][cc], hw);
 #pragma unroll
                     for (int mm = 0; mm < MT; ++mm) {
                         float a = acc[r * MT + mm];
@@ -107,34 +146,48 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
                 }
             }
         }
-
-        butterfly_reduce<R>(acc);
-        if ((lane & (kWave / R - 1)) == 0) {
-            const int idx = butterfly_index<R>(lane);
-            const int r = idx / MT;
-            const int mm = idx % MT;
-            const int row = row0 + r;
-            if (row < n && mm < m) {
-                const float s = f16_bits_to_f32(scales[row]);
-                y[(int64_t)mm * n + row] = f32_to_f16_bits(acc[0] * s);
+        if (b == batches - 1) {
+            butterfly_reduce<R>(acc);
+            if ((lane & (kWave / R - 1)) == 0) {
+                const int idx = butterfly_index<R>(lane);
+                const int r = idx / MT;
+                const int mm = idx % MT;
+                const int row = row_begin + g * RU + r;
+                if (row < row_end && mm < m) {
+                    const float s = f16_bits_to_f32(scales[row]);
+                    y[(int64_t)mm * n + row] = f32_to_f16_bits(acc[0] * s);
+                }
             }
+        }
+    };
+
+    // two-slot software pipeline; the slot index is static in each half
+    for (int it = 0; it < items; it += 2) {
+        if (it + 1 < items)
+            issue(it + 1, buf1);
+        consume(it, buf0);
+        if (it + 1 < items) {
+            if (it + 2 < items)
+                issue(it + 2, buf0);
+            consume(it + 1, buf1);
         }
     }
 }
 
-template <int MT, int RU>
+template <int MT, int RU, int CH>
 hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
                       int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
     const int chunks = (int)((k + kChunkK - 1) / kChunkK);
-    const int groups = (int)((n + RU - 1) / RU);
     const size_t lds = (size_t)MT * chunks * 2 * kWave * sizeof(u32x4_t);
-    int blocks = (groups + kGemvWaves - 1) / kGemvWaves;
-    const int cap = device_cu_count() * 8;
-    if (blocks > cap)
-        blocks = cap;
-    hipLaunchKernelGGL((gemv_kernel<MT, RU>), dim3(blocks), dim3(kGemvThreads), lds, stream,
-                       x, q, scales, y, (int)m, (int)n, (int)k, chunks, groups);
+    // one wave per RU rows at most; otherwise as many waves as the chip keeps resident
+    int64_t waves = (n + RU - 1) / RU;
+    const int64_t cap = (int64_t)device_cu_count() * QW_GEMV_WAVES_PER_CU;
+    if (waves > cap)
+        waves = cap;
+    const int blocks = (int)((waves + kGemvWaves - 1) / kGemvWaves);
+    hipLaunchKernelGGL((gemv_kernel<MT, RU, CH>), dim3(blocks), dim3(kGemvThreads), lds, stream,
+                       x, q, scales, y, (int)m, (int)n, (int)k, chunks, (int)waves);
     return hipGetLastError();
 }
 
@@ -155,12 +208,12 @@ hipError_t launch_gemv(const uint16_t *x, const int8_t *q, const uint16_t *scale
                        int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
     if (m <= 1)
-        return launch_cfg<1, 4>(x, q, scales, y, m, n, k, stream);
+        return launch_cfg<1, 4, 4>(x, q, scales, y, m, n, k, stream);
     if (m <= 2)
-        return launch_cfg<2, 4>(x, q, scales, y, m, n, k, stream);
+        return launch_cfg<2, 4, 2>(x, q, scales, y, m, n, k, stream);
     if (m <= 4)
-        return launch_cfg<4, 4>(x, q, scales, y, m, n, k, stream);
-    return launch_cfg<8, 4>(x, q, scales, y, m, n, k, stream);
+        return launch_cfg<4, 2, 2>(x, q, scales, y, m, n, k, stream);
+    return launch_cfg<8, 2, 2>(x, q, scales, y, m, n, k, stream);
 }
 
 } // namespace qw

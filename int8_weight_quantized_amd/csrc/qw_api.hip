@@ -33,6 +33,21 @@ int device_cu_count()
     return cus;
 }
 
+// Kernel choice by shape.  Decode (one or two activation rows): the VALU
+// GEMV streams the weights once with the fewest instructions per byte.  A
+// few rows: the skinny MFMA kernel keeps the weight stream at full rate
+// while the VALU dot products would grow with m.  Prefill: the LDS-tiled
+// MFMA GEMM, whose weight tiles are reused across activation rows.
+int auto_path(int64_t m, int64_t n, int64_t k)
+{
+    (void)n;
+    if (m <= 2 && gemv_supported(m, k))
+        return QW_PATH_GEMV;
+    if (m <= 32)
+        return QW_PATH_SKINNY;
+    return QW_PATH_MFMA;
+}
+
 } // namespace qw
 
 namespace {
@@ -127,7 +142,8 @@ QW_API qw_status qw_w8a16_gemm_path(const uint16_t *x, const int8_t *q, const ui
                                     uint16_t *y, int64_t m, int64_t n, int64_t k, int path,
                                     void *stream)
 {
-    if (path != QW_PATH_AUTO && path != QW_PATH_GEMV && path != QW_PATH_MFMA)
+    if (path != QW_PATH_AUTO && path != QW_PATH_GEMV && path != QW_PATH_MFMA &&
+        path != QW_PATH_SKINNY)
         return QW_ERROR_INVALID_VALUE;
     bool noop = false;
     const qw_status st = check_gemm_args(x, q, scales, y, m, n, k, noop);
@@ -135,12 +151,14 @@ QW_API qw_status qw_w8a16_gemm_path(const uint16_t *x, const int8_t *q, const ui
         return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (path == QW_PATH_AUTO)
-        path = qw::gemv_supported(m, k) ? QW_PATH_GEMV : QW_PATH_MFMA;
+        path = qw::auto_path(m, n, k);
     if (path == QW_PATH_GEMV) {
         if (!qw::gemv_supported(m, k))
             return QW_ERROR_UNSUPPORTED;
         return launch_status(qw::launch_gemv(x, q, scales, y, m, n, k, s));
     }
+    if (path == QW_PATH_SKINNY)
+        return launch_status(qw::launch_skinny_gemm(x, q, scales, y, m, n, k, s));
     return launch_status(qw::launch_mfma_gemm(x, q, scales, y, m, n, k, s));
 }
 
@@ -148,6 +166,13 @@ QW_API qw_status qw_w8a16_gemm(const uint16_t *x, const int8_t *q, const uint16_
                                uint16_t *y, int64_t m, int64_t n, int64_t k, void *stream)
 {
     return qw_w8a16_gemm_path(x, q, scales, y, m, n, k, QW_PATH_AUTO, stream);
+}
+
+QW_API int qw_w8a16_gemm_auto_path(int64_t m, int64_t n, int64_t k)
+{
+    if (m < 0 || n < 0 || k <= 0 || k % 16 != 0)
+        return -1;
+    return qw::auto_path(m, n, k);
 }
 
 QW_API const char *qw_status_string(qw_status status)

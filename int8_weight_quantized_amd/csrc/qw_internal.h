@@ -22,6 +22,14 @@ bool gemv_supported(int64_t m, int64_t k);
 hipError_t launch_gemv(const uint16_t *x, const int8_t *q, const uint16_t *scales,
                        uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
+// Skinny MFMA GEMM: weights dequantized in registers, any m (intended for
+// m <= 32), n, k with k % 16 == 0.
+hipError_t launch_skinny_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                              uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream);
+
+// Kernel the automatic path picks for a shape (QW_PATH_* value).
+int auto_path(int64_t m, int64_t n, int64_t k);
+
 // MFMA tiled GEMM, any m, n, k with k % 16 == 0.
 hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
                             uint16_t *y, int64_t m, int64_t n, int64_t k,

@@ -28,7 +28,7 @@ def _exported_symbols():
 def test_header_declares_the_entry_points():
     decl = _declared_functions()
     for name in ("qw_quantize_weights", "qw_w8a16_gemm", "qw_w8a16_gemm_path",
-                 "qw_status_string", "qw_version"):
+                 "qw_w8a16_gemm_auto_path", "qw_status_string", "qw_version"):
         assert name in decl
 
 
@@ -120,6 +120,15 @@ def test_gemm_path_checks():
     # the GEMV path refuses shapes beyond its LDS budget: m > 8, or m * ceil(k/1024) > 32
     assert qw.w8a16_gemm_raw(A, B, C, D, 9, 4, 16, 0, 1) == qw.QW_ERROR_UNSUPPORTED
     assert qw.w8a16_gemm_raw(A, B, C, D, 8, 4, 5 * 1024, 0, 1) == qw.QW_ERROR_UNSUPPORTED
+
+
+def test_auto_path_choice():
+    assert qw.auto_path(1, 27392, 4096) == "gemv"
+    assert qw.auto_path(8, 4608, 4096) == "skinny"
+    assert qw.auto_path(512, 27392, 4096) == "mfma"
+    assert qw.auto_path(4096, 4096, 1024) == "mfma"
+    with pytest.raises(ValueError):
+        qw.auto_path(1, 4, 24)
 
 
 def test_gemm_empty_is_noop():

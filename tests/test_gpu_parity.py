@@ -23,7 +23,7 @@ from gpu_util import assert_gemm_close, gpu_gemm, gpu_quantize, say
 
 pytestmark = pytest.mark.gpu
 
-GEMV, MFMA = 1, 2
+GEMV, MFMA, SKINNY = 1, 2, 3
 
 
 @functools.lru_cache(maxsize=2)
@@ -104,6 +104,14 @@ def test_gemv_small_shapes(m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", MFMA_SHAPES)
+def test_skinny_small_shapes(m, n, k):
+    x, q, s = _small_case(m, n, k, seed=m * 1000 + n + 7)
+    say("gemm skinny m=%d n=%d k=%d" % (m, n, k))
+    y = gpu_gemm(x, q, s, path=SKINNY)
+    assert_gemm_close(y, oracle.gemm(x, q, s), "skinny %dx%dx%d" % (m, n, k))
+
+
+@pytest.mark.parametrize("m,n,k", MFMA_SHAPES)
 def test_mfma_small_shapes(m, n, k):
     x, q, s = _small_case(m, n, k, seed=m * 1000 + n)
     say("gemm mfma m=%d n=%d k=%d" % (m, n, k))
@@ -111,7 +119,7 @@ def test_mfma_small_shapes(m, n, k):
     assert_gemm_close(y, oracle.gemm(x, q, s), "mfma %dx%dx%d" % (m, n, k))
 
 
-@pytest.mark.parametrize("path", [GEMV, MFMA])
+@pytest.mark.parametrize("path", [GEMV, SKINNY, MFMA])
 @pytest.mark.parametrize("m,n,k", [(1, 96, 512), (4, 200, 1024), (8, 130, 2048)])
 def test_gemm_exact_arithmetic_bitexact(path, m, n, k):
     """X in {-1,0,1}, power-of-two scales: every partial sum is exact in fp32,
@@ -133,7 +141,7 @@ def test_paths_agree_with_oracle_at_same_m(m):
     x = synthetic.random_x(m, wl.k, 77)
     _, _, _, q, s = workload_data(wl.name)
     ref = oracle.gemm(x, q, s)
-    for path in (GEMV, MFMA):
+    for path in (GEMV, SKINNY, MFMA):
         say("gemm path=%d m=%d n=%d k=%d" % (path, m, wl.n, wl.k))
         assert_gemm_close(gpu_gemm(x, q, s, path=path), ref, "path %d m %d" % (path, m))
 
@@ -141,7 +149,7 @@ def test_paths_agree_with_oracle_at_same_m(m):
 def test_gemm_deterministic():
     wl, x, w, q, s = workload_data("small_batch_m8_k4096_n4608")
     say("gemm determinism")
-    for path in (GEMV, MFMA):
+    for path in (GEMV, SKINNY, MFMA):
         a = gpu_gemm(x, q, s, path=path)
         b = gpu_gemm(x, q, s, path=path)
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
@@ -155,7 +163,7 @@ def test_gemm_zero_activation_and_zero_rows():
     q, s, _ = oracle.quantize(w, 100.0)
     x = rng.standard_normal((m, k)).astype(np.float16)
     x[2] = 0.0
-    for path in (GEMV, MFMA):
+    for path in (GEMV, SKINNY, MFMA):
         say("gemm zeros path=%d" % path)
         y = gpu_gemm(x, q, s, path=path)
         assert np.all(y[2].view(np.uint16) == 0) and np.all(y[:, 3].view(np.uint16) == 0)
