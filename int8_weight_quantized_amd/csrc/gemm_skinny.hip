@@ -11,16 +11,18 @@
 // registers and used as the MFMA "A" operand; the activations are the "B"
 // operand (16 columns, rows beyond m are zero).  No LDS staging of weights.
 //
-// Work split: a workgroup of KSPLIT waves owns 16 weight rows; wave w walks
-// the k range [w*K/KSPLIT, (w+1)*K/KSPLIT) (64-aligned) in steps of 64.  In
-// one step lane l (row r = l % 16, group g = l / 16) loads bytes
-// [k + 16 g, +16) of row r: the first 8 codes feed one MFMA (k slots
-// 8 g .. 8 g + 7 of a 32-wide k block), the last 8 feed a second one, and
-// the activation operand is loaded with the same k assignment, so each MFMA
-// contracts exactly the 32 k values its two operands agree on.  UNROLL
-// steps are issued before any is consumed to keep enough bytes in flight.
-// The KSPLIT partial tiles are summed in LDS in wave order (deterministic),
-// then scaled, rounded to fp16 and stored.
+// Work split: a workgroup of KSPLIT waves owns 16 weight rows x 16
+// activation rows; wave w walks the k steps [w*S/KSPLIT, (w+1)*S/KSPLIT)
+// of the S = ceil(k/64) steps of 64.  In one step lane l (row r = l % 16,
+// group g = l / 16) loads bytes [64 s + 16 g, +16) of row r: the first 8
+// codes feed one MFMA (k slots 8 g .. 8 g + 7 of a 32-wide k block), the
+// last 8 feed a second one, and the activation operand is loaded with the
+// same k assignment, so each MFMA contracts exactly the 32 k values its two
+// operands agree on.  UNROLL steps are issued before any is consumed.
+// KSPLIT is chosen so the grid has enough waves to keep HBM busy (a small
+// weight matrix gets a finer k split).  The KSPLIT partial tiles are summed
+// in LDS in wave order (deterministic), then scaled, rounded to fp16 and
+// stored.
 #include "qw_device.h"
 #include "qw_internal.h"
 
@@ -29,18 +31,16 @@ namespace {
 
 typedef float float4v __attribute__((ext_vector_type(4)));
 
-constexpr int kSkinnyKSplit = 4;
-constexpr int kSkinnyThreads = kSkinnyKSplit * kWave;
-constexpr int kSkinnyUnroll = 4;
+constexpr int kSkinnyUnroll = 8;
+constexpr int kSkinnyTargetWaves = 2048; // enough in-flight loads to fill HBM
 
-template <int MT>
-__global__ __launch_bounds__(kSkinnyThreads) void skinny_gemm_kernel(
+template <int KSPLIT>
+__global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
     const uint16_t *__restrict__ x, const int8_t *__restrict__ q,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y,
     int m, int n, int k)
 {
-    static_assert(MT == 16, "one 16-column MFMA tile of activations");
-    __shared__ float4v partial[kSkinnyKSplit][kWave];
+    __shared__ float4v partial[KSPLIT][kWave];
 
     const int lane = __lane_id();
     const int wave = threadIdx.x / kWave;
@@ -51,10 +51,9 @@ __global__ __launch_bounds__(kSkinnyThreads) void skinny_gemm_kernel(
     const int row = n0 + r;
     const int col = m0 + r; // activation row this lane feeds into the B operand
 
-    // k range of this wave, in whole 64-wide steps
     const int steps_total = (k + 63) / 64;
-    const int s_begin = (int)(((int64_t)wave * steps_total) / kSkinnyKSplit);
-    const int s_end = (int)(((int64_t)(wave + 1) * steps_total) / kSkinnyKSplit);
+    const int s_begin = (int)(((int64_t)wave * steps_total) / KSPLIT);
+    const int s_end = (int)(((int64_t)(wave + 1) * steps_total) / KSPLIT);
 
     const int8_t *qrow = q + (int64_t)(row < n ? row : 0) * k;
     const uint16_t *xrow = x + (int64_t)(col < m ? col : 0) * k;
@@ -70,10 +69,15 @@ __global__ __launch_bounds__(kSkinnyThreads) void skinny_gemm_kernel(
             const int kk = (s + u) * 64 + g * 16;
             const bool ok = (s + u) < s_end && kk < k;
             wv[u] = (u32x4_t){0u, 0u, 0u, 0u};
-            xa[u] = (u32x4_t){0u, 0u, 0u, 0u};
-            xb[u] = (u32x4_t){0u, 0u, 0u, 0u};
             if (ok && row_ok)
                 wv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(qrow + kk));
+        }
+#pragma unroll
+        for (int u = 0; u < kSkinnyUnroll; ++u) {
+            const int kk = (s + u) * 64 + g * 16;
+            const bool ok = (s + u) < s_end && kk < k;
+            xa[u] = (u32x4_t){0u, 0u, 0u, 0u};
+            xb[u] = (u32x4_t){0u, 0u, 0u, 0u};
             if (ok && col_ok) {
                 xa[u] = *reinterpret_cast<const u32x4_t *>(xrow + kk);
                 xb[u] = *reinterpret_cast<const u32x4_t *>(xrow + kk + 8);
@@ -90,14 +94,16 @@ __global__ __launch_bounds__(kSkinnyThreads) void skinny_gemm_kernel(
         }
     }
 
-    partial[wave][lane] = acc;
-    __syncthreads();
-    if (wave != 0)
-        return;
-    float4v sum = partial[0][lane];
+    if (KSPLIT > 1) {
+        partial[wave][lane] = acc;
+        __syncthreads();
+        if (wave != 0)
+            return;
+        acc = partial[0][lane];
 #pragma unroll
-    for (int w = 1; w < kSkinnyKSplit; ++w)
-        sum += partial[w][lane];
+        for (int w = 1; w < KSPLIT; ++w)
+            acc += partial[w][lane];
+    }
     // lane holds rows n0 + 4 g + i (i = 0..3) of activation column m0 + r
     const int ym = m0 + r;
     if (ym >= m)
@@ -106,8 +112,18 @@ __global__ __launch_bounds__(kSkinnyThreads) void skinny_gemm_kernel(
     for (int i = 0; i < 4; ++i) {
         const int yn = n0 + 4 * g + i;
         if (yn < n)
-            y[(int64_t)ym * n + yn] = f32_to_f16_bits(sum[i] * f16_bits_to_f32(scales[yn]));
+            y[(int64_t)ym * n + yn] = f32_to_f16_bits(acc[i] * f16_bits_to_f32(scales[yn]));
     }
+}
+
+template <int KSPLIT>
+hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
+                      int64_t m, int64_t n, int64_t k, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((n + 15) / 16), (unsigned)((m + 15) / 16));
+    hipLaunchKernelGGL((skinny_gemm_kernel<KSPLIT>), grid, dim3(KSPLIT * kWave), 0, stream,
+                       x, q, scales, y, (int)m, (int)n, (int)k);
+    return hipGetLastError();
 }
 
 } // namespace
@@ -115,10 +131,23 @@ __global__ __launch_bounds__(kSkinnyThreads) void skinny_gemm_kernel(
 hipError_t launch_skinny_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
                               uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((n + 15) / 16), (unsigned)((m + 15) / 16));
-    hipLaunchKernelGGL((skinny_gemm_kernel<16>), grid, dim3(kSkinnyThreads), 0, stream,
-                       x, q, scales, y, (int)m, (int)n, (int)k);
-    return hipGetLastError();
+    // split k until the grid holds about kSkinnyTargetWaves waves, keeping
+    // at least one 64-wide step per wave
+    const int64_t tiles = ((n + 15) / 16) * ((m + 15) / 16);
+    const int64_t steps = (k + 63) / 64;
+    int ksplit = 1;
+    while (ksplit < 8 && tiles * ksplit < kSkinnyTargetWaves && steps >= 2 * ksplit)
+        ksplit *= 2;
+    switch (ksplit) {
+    case 1:
+        return launch_cfg<1>(x, q, scales, y, m, n, k, stream);
+    case 2:
+        return launch_cfg<2>(x, q, scales, y, m, n, k, stream);
+    case 4:
+        return launch_cfg<4>(x, q, scales, y, m, n, k, stream);
+    default:
+        return launch_cfg<8>(x, q, scales, y, m, n, k, stream);
+    }
 }
 
 } // namespace qw

@@ -9,17 +9,17 @@
 // byte-permute trick, and dotted with fp16 activations on v_dot2_f32_f16
 // (fp32 accumulation).  The per-channel scale multiplies the fp32 sum.
 //
-// Work split.  The grid is sized to what the chip holds at once; wave w
-// owns the contiguous weight rows [w*N/W, (w+1)*N/W) (balanced to one row),
-// walked in groups of RU rows.  For one group, lane l reads bytes
-// [c*1024 + 16 l, +16) of each row for every 1 KiB chunk c, so each load
-// instruction of the wave covers 1 KiB of one row, fully coalesced.  Loads
-// are software-pipelined: the next item's RU x CH 16-byte loads (CH chunks
-// of RU rows) are issued before the current item is dequantized and
-// multiplied, so every wave keeps two items in flight.  X (m rows, fp16) is
-// staged once per workgroup in LDS, after the first loads have been issued.
-// The RU*M per-lane partial sums are combined with a transposing butterfly
-// (about RU*M shuffles instead of 6*RU*M).
+// Work split.  The grid is sized to what the chip holds at once (W waves);
+// wave w owns rows w, w + W, w + 2W, ... (balanced to one row), walked RU
+// rows at a time, so at any moment the waves of the chip read one compact
+// window of rows (DRAM page locality) instead of W scattered streams.  For
+// one row, lane l reads bytes [c*1024 + 16 l, +16) for every 1 KiB chunk c:
+// each load instruction of the wave covers 1 KiB of one row, fully
+// coalesced.  An item is RU rows x CH chunks: its RU x CH 16-byte loads are
+// all issued before any is consumed; the grid keeps 16 waves per CU so the
+// chip holds plenty of bytes in flight.  X (m rows, fp16) is staged once
+// per workgroup in LDS, after the first item's loads have been issued.  The RU*M per-lane partial sums are combined with a
+// transposing butterfly (about RU*M shuffles instead of 6*RU*M).
 //
 // LDS layout of X: [m][chunk][half h][lane] x 16 bytes, where entry
 // (m, c, h, l) holds x[m][c*1024 + 16 l + 8 h .. +7].  Lane l reads
@@ -28,7 +28,7 @@
 #include "qw_internal.h"
 
 #ifndef QW_GEMV_WAVES_PER_CU
-#define QW_GEMV_WAVES_PER_CU 8
+#define QW_GEMV_WAVES_PER_CU 16
 #endif
 
 namespace qw {
@@ -56,35 +56,35 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     const int wave = tid / kWave;
     const int gw = blockIdx.x * kGemvWaves + wave;
 
-    // this wave's rows and items (an item = RU rows x CH chunks)
-    const int row_begin = (int)(((int64_t)gw * n) / total_waves);
-    const int row_end = (int)(((int64_t)(gw + 1) * n) / total_waves);
-    const int groups = (row_end - row_begin + RU - 1) / RU;
+    // this wave's rows gw + j * total_waves, j < my_rows; an item is RU of
+    // them x CH chunks
+    const int my_rows = gw < n ? (n - 1 - gw) / total_waves + 1 : 0;
+    const int groups = (my_rows + RU - 1) / RU;
     const int batches = (chunks + CH - 1) / CH;
     const int items = gw < total_waves ? groups * batches : 0;
 
     auto issue = [&](int it, GemvItem<MT, RU, CH> &dst) {
         const int g = it / batches;
         const int b = it - g * batches;
-        const int row0 = row_begin + g * RU;
 #pragma unroll
         for (int r = 0; r < RU; ++r) {
 #pragma unroll
             for (int cc = 0; cc < CH; ++cc) {
                 const int c = b * CH + cc;
                 const int kk = c * kChunkK + lane * 16;
-                const int row = row0 + r;
+                const int j = g * RU + r;
+                const int64_t row = gw + (int64_t)j * total_waves;
                 dst.w[r][cc] = (u32x4_t){0u, 0u, 0u, 0u};
-                if (row < row_end && kk < k)
+                if (j < my_rows && kk < k)
                     dst.w[r][cc] = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4_t *>(q + (int64_t)row * k + kk));
+                        reinterpret_cast<const u32x4_t *>(q + row * k + kk));
             }
         }
     };
 
-    GemvItem<MT, RU, CH> buf0, buf1;
+    GemvItem<MT, RU, CH> buf;
     if (items > 0)
-        issue(0, buf0);
+        issue(0, buf);
 
     // ---- stage X into LDS (rows m..MT-1 are zero) while the loads fly ----
     const int entries = MT * chunks * 2 * kWave;
@@ -152,8 +152,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
                 const int idx = butterfly_index<R>(lane);
                 const int r = idx / MT;
                 const int mm = idx % MT;
-                const int row = row_begin + g * RU + r;
-                if (row < row_end && mm < m) {
+                const int j = g * RU + r;
+                const int64_t row = gw + (int64_t)j * total_waves;
+                if (j < my_rows && mm < m) {
                     const float s = f16_bits_to_f32(scales[row]);
                     y[(int64_t)mm * n + row] = f32_to_f16_bits(acc[0] * s);
                 }
@@ -161,16 +162,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
         }
     };
 
-    // two-slot software pipeline; the slot index is static in each half
-    for (int it = 0; it < items; it += 2) {
-        if (it + 1 < items)
-            issue(it + 1, buf1);
-        consume(it, buf0);
-        if (it + 1 < items) {
-            if (it + 2 < items)
-                issue(it + 2, buf0);
-            consume(it + 1, buf1);
-        }
+    // one item in flight per wave; the chip-wide occupancy (many resident
+    // waves) keeps HBM busy, which measured faster than a two-deep per-wave
+    // pipeline with fewer waves
+    for (int it = 0; it < items; ++it) {
+        if (it > 0)
+            issue(it, buf);
+        consume(it, buf);
     }
 }
 

@@ -157,8 +157,11 @@ QW_API qw_status qw_w8a16_gemm_path(const uint16_t *x, const int8_t *q, const ui
             return QW_ERROR_UNSUPPORTED;
         return launch_status(qw::launch_gemv(x, q, scales, y, m, n, k, s));
     }
-    if (path == QW_PATH_SKINNY)
+    if (path == QW_PATH_SKINNY) {
+        if (m > 16 * 65535) // grid.y holds one 16-row activation tile per block row
+            return QW_ERROR_UNSUPPORTED;
         return launch_status(qw::launch_skinny_gemm(x, q, scales, y, m, n, k, s));
+    }
     return launch_status(qw::launch_mfma_gemm(x, q, scales, y, m, n, k, s));
 }
 
