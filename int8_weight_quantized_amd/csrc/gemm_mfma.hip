@@ -35,12 +35,26 @@
 #include "qw_device.h"
 #include "qw_internal.h"
 
+#include <type_traits>
+
 namespace qw {
 namespace {
 
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
 
 constexpr int kGemmThreads = 256; // 2 x 2 waves
+
+// Big-tile configuration: 256 x 128 tiles with a 2-stage ring fit two
+// workgroups per CU (64 KiB LDS, <= 256 registers per lane each), which
+// measured faster than one 256 x 256 workgroup with a 3-stage ring: the
+// second workgroup's MFMAs overlap the first one's copy/LDS phases.
+#ifndef QW_DMA_BM
+#define QW_DMA_BM 128
+#endif
+#ifndef QW_DMA_STAGES
+#define QW_DMA_STAGES 2
+#endif
 constexpr int kBK = 64;            // k per step
 constexpr int kWRow = kBK + 16;    // LDS bytes per int8 weight row (padded)
 constexpr int kXRow = 2 * kBK + 16; // LDS bytes per fp16 activation row (padded)
@@ -260,15 +274,26 @@ hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales
 // outputs are never stored); k chunks beyond k are zero-filled with
 // ordinary LDS stores.
 // ---------------------------------------------------------------------------
-constexpr int kDmaBN = 256, kDmaBM = 256;
-constexpr int kDmaWBytes = kDmaBN * kBK;     // 16 KiB int8
-constexpr int kDmaXBytes = kDmaBM * kBK * 2; // 32 KiB fp16
-constexpr int kDmaStage = kDmaWBytes + kDmaXBytes;
-constexpr int kDmaStages = 3;
-constexpr int kDmaWInstr = kDmaWBytes / 1024 / 4; // per wave per stage
-constexpr int kDmaXInstr = kDmaXBytes / 1024 / 4;
-constexpr int kDmaInstr = kDmaWInstr + kDmaXInstr;
-constexpr int kDmaSN = 8, kDmaSM = 8; // 16 x 16 MFMA tiles per wave
+constexpr int kDmaBN = 256;                // output channels per workgroup
+constexpr int kDmaWBytes = kDmaBN * kBK;   // 16 KiB int8 weight tile per stage
+constexpr int kDmaSI = 4; // 32 x 32 MFMA tiles per wave along n (128 rows)
+
+// NW waves per workgroup in a 2 (n) x NW/2 (m) grid; each wave owns 128
+// output channels x BM/(NW/2) activation rows.  STAGES-deep LDS ring.
+template <int NW, int BM, int STAGES>
+struct DmaCfg {
+    static constexpr int kThreads = NW * kWave;
+    static constexpr int kXBytes = BM * kBK * 2;             // fp16 activation tile per stage
+    static constexpr int kStage = kDmaWBytes + kXBytes;
+    static constexpr int kWInstr = kDmaWBytes / 1024 / NW;   // copies per wave per stage
+    static constexpr int kXInstr = kXBytes / 1024 / NW;
+    static constexpr int kInstr = kWInstr + kXInstr;
+    static constexpr int kWaveM = BM / (NW / 2);
+    static constexpr int kSJ = kWaveM / 32;                   // 32 x 32 MFMA tiles along m
+    static constexpr int kAhead = STAGES - 1;                 // tiles copied ahead
+    static_assert(kWInstr * 64 * 16 * NW == kDmaWBytes && kXInstr * 64 * 16 * NW == kXBytes, "copy split");
+    static_assert(kSJ >= 1 && kAhead >= 1 && kAhead <= 2, "tile config");
+};
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
@@ -279,18 +304,6 @@ typedef __attribute__((address_space(3))) void *lds_ptr_t;
 __device__ __forceinline__ void wait_lgkmcnt0()
 {
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
-}
-
-// Wait until at most `tiles` tiles' worth of this wave's copies are in
-// flight (0, 1 or 2 tiles).
-__device__ __forceinline__ void wait_tiles_in_flight(int tiles)
-{
-    if (tiles >= 2)
-        QW_WAIT_VMCNT(2 * kDmaInstr);
-    else if (tiles == 1)
-        QW_WAIT_VMCNT(kDmaInstr);
-    else
-        QW_WAIT_VMCNT(0);
 }
 
 // Barrier without a memory fence: a workgroup fence would make the compiler
@@ -316,17 +329,16 @@ __device__ __forceinline__ int xslot(int row)
     return (r16 ^ (r16 >> 3)) & 7;
 }
 
-struct DmaOperands {
-    u32x4_t codes[kDmaSN];
-    half8_t b0[kDmaSM];
-};
-
-__global__ __launch_bounds__(kGemmThreads) void mfma_gemm_dma_kernel(
+template <int NW, int BM, int STAGES>
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(BM <= 128 ? 2 : 1))) void mfma_gemm_dma_kernel(
     const uint16_t *__restrict__ x, const int8_t *__restrict__ q,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y,
     int m, int n, int k, int tiles_m, int tiles_n)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kDmaStages * kDmaStage];
+    using C = DmaCfg<NW, BM, STAGES>;
+    constexpr int kSJ = C::kSJ;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * C::kStage];
 
     const int tid = threadIdx.x;
     const int lane = __lane_id();
@@ -338,14 +350,14 @@ __global__ __launch_bounds__(kGemmThreads) void mfma_gemm_dma_kernel(
     const int tn = tile / tiles_m;
     const int tm = tile % tiles_m;
     const int n0 = tn * kDmaBN;
-    const int m0 = tm * kDmaBM;
+    const int m0 = tm * BM;
     const int ktiles = (k + kBK - 1) / kBK;
     // the last tile issues fewer copies when k is ragged; waits then drain
     const int full_tiles = (k % kBK) != 0 ? ktiles - 1 : ktiles;
 
     // DMA source mapping.  Weight copy i of this wave covers tile rows
-    // (wave * kDmaWInstr + i) * 16 + [0, 16): lane -> row + lane / 4, slot
-    // lane % 4; activation copy i covers rows (wave * kDmaXInstr + i) * 8 +
+    // (wave * kWInstr + i) * 16 + [0, 16): lane -> row + lane / 4, slot
+    // lane % 4; activation copy i covers rows (wave * kXInstr + i) * 8 +
     // [0, 8): lane -> row + lane / 8, slot lane % 8.  The logical chunk a
     // slot holds depends only on the row within its group of 16, so it is
     // the same for every weight copy and alternates for activation copies.
@@ -353,158 +365,171 @@ __global__ __launch_bounds__(kGemmThreads) void mfma_gemm_dma_kernel(
     const int xchunk_even = (lane % 8) ^ xslot(lane / 8);
     const int xchunk_odd = (lane % 8) ^ xslot(8 + lane / 8);
 
-    auto issue = [&](int kt) {
-        uint8_t *st = lds + (kt % kDmaStages) * kDmaStage;
+    // copy tile kt into its stage; FULL: every chunk lies inside k
+    auto issue = [&](int kt, auto full) {
+        uint8_t *st = lds + (kt % STAGES) * C::kStage;
         const int k0 = kt * kBK;
 #pragma unroll
-        for (int i = 0; i < kDmaWInstr; ++i) {
-            uint8_t *dst = st + (wave * kDmaWInstr + i) * 1024;
-            const int row = (wave * kDmaWInstr + i) * 16 + lane / 4;
+        for (int i = 0; i < C::kWInstr; ++i) {
+            uint8_t *dst = st + (wave * C::kWInstr + i) * 1024;
+            const int row = (wave * C::kWInstr + i) * 16 + lane / 4;
             const int gn = min(n0 + row, n - 1);
             const int gk = k0 + wchunk * 16;
-            if (gk < k)
+            if (decltype(full)::value || gk < k)
                 __builtin_amdgcn_global_load_lds(q + (int64_t)gn * k + gk, (lds_ptr_t)dst, 16, 0, 0);
             else
                 *reinterpret_cast<u32x4_t *>(dst + lane * 16) = (u32x4_t){0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int i = 0; i < kDmaXInstr; ++i) {
-            uint8_t *dst = st + kDmaWBytes + (wave * kDmaXInstr + i) * 1024;
-            const int row = (wave * kDmaXInstr + i) * 8 + lane / 8;
+        for (int i = 0; i < C::kXInstr; ++i) {
+            uint8_t *dst = st + kDmaWBytes + (wave * C::kXInstr + i) * 1024;
+            const int row = (wave * C::kXInstr + i) * 8 + lane / 8;
             const int gm = min(m0 + row, m - 1);
             const int gk = k0 + ((i & 1) ? xchunk_odd : xchunk_even) * 8;
-            if (gk < k)
+            if (decltype(full)::value || gk < k)
                 __builtin_amdgcn_global_load_lds(x + (int64_t)gm * k + gk, (lds_ptr_t)dst, 16, 0, 0);
             else
                 *reinterpret_cast<u32x4_t *>(dst + lane * 16) = (u32x4_t){0u, 0u, 0u, 0u};
         }
     };
-    // copies still in flight behind tile t when tile t is waited for (tile
-    // t+1 if it exists); a ragged tail tile may issue fewer copies, so a
-    // wait that would leave it outstanding drains completely instead
-    auto tiles_behind = [&](int t) {
-        const int last_issued = min(t + 1, ktiles - 1);
-        const int behind = last_issued - t;
-        return last_issued >= full_tiles ? 0 : behind;
-    };
+    using full_t = std::integral_constant<bool, true>;
+    using partial_t = std::integral_constant<bool, false>;
 
-    const int lrow = lane % 16;
-    const int lgrp = lane / 16;
-    // this lane's operand slices inside a stage (rows base + 16 i + lrow)
-    const int wrow = wave_n * 128 + lrow;
-    const int w_off = wrow * kBK + 16 * (lgrp ^ wslot(wrow));
-    const int xrow = wave_m * 128 + lrow;
-    const int x_off0 = kDmaWBytes + xrow * 2 * kBK + 16 * ((2 * lgrp) ^ xslot(xrow));
-    const int x_off1 = kDmaWBytes + xrow * 2 * kBK + 16 * ((2 * lgrp + 1) ^ xslot(xrow));
+    // v_mfma_f32_32x32x16_f16: lane l feeds row (l % 32) of A (a weight row)
+    // and column (l % 32) of B (an activation row), 8 k values each; lane
+    // group g = l / 32 takes k slots [8 g, 8 g + 8).  One 64-wide k step is
+    // four MFMAs s = 0..3; in MFMA s, group g covers k = 32 g + 8 s + [0, 8),
+    // so a lane reads 32 consecutive codes (two 16-byte chunks) of its
+    // weight row and 32 consecutive activations (four chunks) of its
+    // activation row per step.
+    const int lrow = lane % 32;
+    const int lgrp = lane / 32;
+    const int wrow = wave_n * 128 + lrow;       // + 32 i
+    const int w_off0 = wrow * kBK + 16 * ((2 * lgrp) ^ wslot(wrow));
+    const int w_off1 = wrow * kBK + 16 * ((2 * lgrp + 1) ^ wslot(wrow));
+    const int xrow = wave_m * C::kWaveM + lrow; // + 32 j
+    int x_off[4];
+#pragma unroll
+    for (int sidx = 0; sidx < 4; ++sidx)
+        x_off[sidx] = kDmaWBytes + xrow * 2 * kBK + 16 * ((4 * lgrp + sidx) ^ xslot(xrow));
 
-    // codes (both k halves) and first-half activations of tile kt
-    auto read_operands = [&](int kt, DmaOperands &op) {
-        const uint8_t *st = lds + (kt % kDmaStages) * kDmaStage;
+    float16v acc[kDmaSI][kSJ];
 #pragma unroll
-        for (int i = 0; i < kDmaSN; ++i)
-            op.codes[i] = *reinterpret_cast<const u32x4_t *>(st + w_off + i * 16 * kBK);
+    for (int i = 0; i < kDmaSI; ++i)
 #pragma unroll
-        for (int j = 0; j < kDmaSM; ++j)
-            op.b0[j] = *reinterpret_cast<const half8_t *>(st + x_off0 + j * 16 * 2 * kBK);
-    };
-    // second-half activations of tile kt
-    auto read_b1 = [&](int kt, half8_t (&b1)[kDmaSM]) {
-        const uint8_t *st = lds + (kt % kDmaStages) * kDmaStage;
-#pragma unroll
-        for (int j = 0; j < kDmaSM; ++j)
-            b1[j] = *reinterpret_cast<const half8_t *>(st + x_off1 + j * 16 * 2 * kBK);
-    };
+        for (int j = 0; j < kSJ; ++j)
+            acc[i][j] = (float16v){};
 
-    float4v acc[kDmaSN][kDmaSM];
+    auto compute = [&](int t) {
+        const uint8_t *st = lds + (t % STAGES) * C::kStage;
+        u32x4_t clo[kDmaSI], chi[kDmaSI];
 #pragma unroll
-    for (int i = 0; i < kDmaSN; ++i)
-#pragma unroll
-        for (int j = 0; j < kDmaSM; ++j)
-            acc[i][j] = (float4v){0.f, 0.f, 0.f, 0.f};
-
-    // prologue: two tiles in flight
-    issue(0);
-    if (ktiles > 1)
-        issue(1);
-
-    for (int t = 0; t < ktiles; ++t) {
-        // my copies of tile t are done once at most one tile's copies remain
-        // outstanding; then the barrier publishes everyone's copies and
-        // certifies that the stage tile t+2 goes to (tile t-1's) is no
-        // longer being read
-        wait_tiles_in_flight(tiles_behind(t) > 0 ? 1 : 0);
-        ring_barrier();
-        if (t + 2 < ktiles)
-            issue(t + 2);
-
-        DmaOperands op;
-        half8_t b1[kDmaSM];
-        read_operands(t, op);
-        read_b1(t, b1);
-        half8_t a0 = i8x8_to_half8(op.codes[0].x, op.codes[0].y);
-        half8_t a1 = i8x8_to_half8(op.codes[0].z, op.codes[0].w);
-#pragma unroll
-        for (int i = 0; i < kDmaSN; ++i) {
-            // cast the next weight sub-tile while this one's MFMAs run
-            half8_t n0v = a0, n1v = a1;
-            if (i + 1 < kDmaSN) {
-                n0v = i8x8_to_half8(op.codes[i + 1].x, op.codes[i + 1].y);
-                n1v = i8x8_to_half8(op.codes[i + 1].z, op.codes[i + 1].w);
-            }
-#pragma unroll
-            for (int j = 0; j < kDmaSM; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, op.b0[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-            for (int j = 0; j < kDmaSM; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1[j], acc[i][j], 0, 0, 0);
-            a0 = n0v;
-            a1 = n1v;
+        for (int i = 0; i < kDmaSI; ++i) {
+            clo[i] = *reinterpret_cast<const u32x4_t *>(st + w_off0 + i * 32 * kBK);
+            chi[i] = *reinterpret_cast<const u32x4_t *>(st + w_off1 + i * 32 * kBK);
         }
+        half8_t b[kSJ][4];
+#pragma unroll
+        for (int j = 0; j < kSJ; ++j)
+#pragma unroll
+            for (int sidx = 0; sidx < 4; ++sidx)
+                b[j][sidx] = *reinterpret_cast<const half8_t *>(st + x_off[sidx] + j * 32 * 2 * kBK);
+#pragma unroll
+        for (int sidx = 0; sidx < 4; ++sidx) {
+#pragma unroll
+            for (int i = 0; i < kDmaSI; ++i) {
+                const u32x4_t c = sidx < 2 ? clo[i] : chi[i];
+                const half8_t a = (sidx & 1) ? i8x8_to_half8(c.z, c.w) : i8x8_to_half8(c.x, c.y);
+#pragma unroll
+                for (int j = 0; j < kSJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[j][sidx], acc[i][j], 0, 0, 0);
+            }
+        }
+    };
+
+    // prologue: kAhead tiles in flight
+#pragma unroll
+    for (int a = 0; a < C::kAhead; ++a)
+        if (a < ktiles)
+            issue(a, partial_t{});
+
+    // Steady state: every tile involved is full, the loop body has no
+    // branches.  Step t waits for its own copies of tile t (leaving the
+    // kAhead - 1 newer tiles in flight), the barrier publishes everyone's
+    // copies and certifies that tile t-1's stage is no longer read, then
+    // tile t + kAhead is copied into that stage while tile t is multiplied.
+    int t = 0;
+    const int steady = full_tiles - C::kAhead > 0 ? full_tiles - C::kAhead : 0;
+    for (; t < steady; ++t) {
+        QW_WAIT_VMCNT((C::kAhead - 1) * C::kInstr);
+        ring_barrier();
+        issue(t + C::kAhead, full_t{});
+        compute(t);
+    }
+    // Drain: the remaining tiles (and the ragged one) with exact waits.
+    for (; t < ktiles; ++t) {
+        const int newest = min(t + C::kAhead - 1, ktiles - 1);
+        if (newest > t && newest < full_tiles)
+            QW_WAIT_VMCNT((C::kAhead - 1) * C::kInstr);
+        else
+            QW_WAIT_VMCNT(0);
+        ring_barrier();
+        if (t + C::kAhead < ktiles)
+            issue(t + C::kAhead, partial_t{});
+        compute(t);
     }
 
     // ---- epilogue: scale, round to fp16, store ----
+    // 32 x 32 output layout: accumulator r of lane l is row
+    // 8 (r / 4) + 4 (l / 32) + (r % 4), column l % 32 of the MFMA tile, so
+    // each group of 4 registers is 4 consecutive output channels of one
+    // activation row: one 8-byte store.
     const bool vec_ok = (n % 4) == 0;
 #pragma unroll
-    for (int i = 0; i < kDmaSN; ++i) {
-        const int gn = n0 + wave_n * 128 + i * 16 + lgrp * 4;
-        float s[4];
+    for (int i = 0; i < kDmaSI; ++i) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            s[r] = (gn + r < n) ? f16_bits_to_f32(scales[gn + r]) : 0.0f;
-#pragma unroll
-        for (int j = 0; j < kDmaSM; ++j) {
-            const int gm = m0 + wave_m * 128 + j * 16 + lrow;
-            if (gm >= m)
-                continue;
-            uint16_t out[4];
+        for (int qd = 0; qd < 4; ++qd) {
+            const int gn = n0 + wave_n * 128 + i * 32 + 8 * qd + 4 * lgrp;
+            float sc[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                out[r] = f32_to_f16_bits(acc[i][j][r] * s[r]);
-            uint16_t *dst = y + (int64_t)gm * n + gn;
-            if (vec_ok && gn + 3 < n) {
-                u32x2_t pk = {(uint32_t)out[0] | ((uint32_t)out[1] << 16),
-                              (uint32_t)out[2] | ((uint32_t)out[3] << 16)};
-                *reinterpret_cast<u32x2_t *>(dst) = pk;
-            } else {
+                sc[r] = (gn + r < n) ? f16_bits_to_f32(scales[gn + r]) : 0.0f;
+#pragma unroll
+            for (int j = 0; j < kSJ; ++j) {
+                const int gm = m0 + wave_m * C::kWaveM + j * 32 + lrow;
+                if (gm >= m)
+                    continue;
+                uint16_t out[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (gn + r < n)
-                        dst[r] = out[r];
+                    out[r] = f32_to_f16_bits(acc[i][j][4 * qd + r] * sc[r]);
+                uint16_t *dst = y + (int64_t)gm * n + gn;
+                if (vec_ok && gn + 3 < n) {
+                    u32x2_t pk = {(uint32_t)out[0] | ((uint32_t)out[1] << 16),
+                                  (uint32_t)out[2] | ((uint32_t)out[3] << 16)};
+                    *reinterpret_cast<u32x2_t *>(dst) = pk;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (gn + r < n)
+                            dst[r] = out[r];
+                }
             }
         }
     }
 }
 
+template <int NW, int BM, int STAGES>
 hipError_t launch_dma(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
                       int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
-    const int64_t tiles_m = (m + kDmaBM - 1) / kDmaBM;
+    const int64_t tiles_m = (m + BM - 1) / BM;
     const int64_t tiles_n = (n + kDmaBN - 1) / kDmaBN;
     const int64_t blocks = tiles_m * tiles_n;
     if (blocks > 0x7fffffff)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(mfma_gemm_dma_kernel, dim3((unsigned)blocks), dim3(kGemmThreads), 0, stream,
-                       x, q, scales, y, (int)m, (int)n, (int)k, (int)tiles_m, (int)tiles_n);
+    hipLaunchKernelGGL((mfma_gemm_dma_kernel<NW, BM, STAGES>), dim3((unsigned)blocks), dim3(NW * kWave),
+                       0, stream, x, q, scales, y, (int)m, (int)n, (int)k, (int)tiles_m, (int)tiles_n);
     return hipGetLastError();
 }
 
@@ -517,9 +542,7 @@ hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *
         return launch_cfg<128, 32>(x, q, scales, y, m, n, k, stream);
     if (m <= 64)
         return launch_cfg<128, 64>(x, q, scales, y, m, n, k, stream);
-    if (m <= 128)
-        return launch_cfg<256, 128>(x, q, scales, y, m, n, k, stream);
-    return launch_dma(x, q, scales, y, m, n, k, stream);
+    return launch_dma<4, QW_DMA_BM, QW_DMA_STAGES>(x, q, scales, y, m, n, k, stream);
 }
 
 } // namespace qw
