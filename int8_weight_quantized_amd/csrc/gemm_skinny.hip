@@ -11,18 +11,18 @@
 // registers and used as the MFMA "A" operand; the activations are the "B"
 // operand (16 columns, rows beyond m are zero).  No LDS staging of weights.
 //
-// Work split: a workgroup of KSPLIT waves owns 16 weight rows x 16
+// Work split: a workgroup of KSPLIT waves owns RT x 16 weight rows x 16
 // activation rows; wave w walks the k steps [w*S/KSPLIT, (w+1)*S/KSPLIT)
 // of the S = ceil(k/64) steps of 64.  In one step lane l (row r = l % 16,
-// group g = l / 16) loads bytes [64 s + 16 g, +16) of row r: the first 8
-// codes feed one MFMA (k slots 8 g .. 8 g + 7 of a 32-wide k block), the
-// last 8 feed a second one, and the activation operand is loaded with the
-// same k assignment, so each MFMA contracts exactly the 32 k values its two
-// operands agree on.  UNROLL steps are issued before any is consumed.
-// KSPLIT is chosen so the grid has enough waves to keep HBM busy (a small
-// weight matrix gets a finer k split).  The KSPLIT partial tiles are summed
-// in LDS in wave order (deterministic), then scaled, rounded to fp16 and
-// stored.
+// group g = l / 16) loads bytes [64 s + 16 g, +16) of row r of each of the
+// RT row tiles: the first 8 codes feed one MFMA (k slots 8 g .. 8 g + 7 of
+// a 32-wide k block), the last 8 feed a second one, and the activation
+// operand is loaded once with the same k assignment and reused by all RT
+// row tiles (activation traffic from L2 is 2/RT of the weight traffic).
+// UNROLL steps are issued before any is consumed.  KSPLIT is chosen so the
+// grid has enough waves to keep HBM busy.  The KSPLIT partial tiles are
+// summed in LDS in wave order (deterministic), then scaled, rounded to fp16
+// and stored.
 #include "qw_device.h"
 #include "qw_internal.h"
 
@@ -31,46 +31,58 @@ namespace {
 
 typedef float float4v __attribute__((ext_vector_type(4)));
 
-constexpr int kSkinnyUnroll = 8;
+constexpr int kSkinnyUnroll = 4;
 constexpr int kSkinnyTargetWaves = 2048; // enough in-flight loads to fill HBM
 
-template <int KSPLIT>
+template <int RT, int KSPLIT>
 __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
     const uint16_t *__restrict__ x, const int8_t *__restrict__ q,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y,
     int m, int n, int k)
 {
-    __shared__ float4v partial[KSPLIT][kWave];
+    __shared__ float4v partial[KSPLIT > 1 ? KSPLIT - 1 : 1][RT][kWave];
 
     const int lane = __lane_id();
     const int wave = threadIdx.x / kWave;
     const int r = lane % 16;
     const int g = lane / 16;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * 16 * RT;
     const int m0 = blockIdx.y * 16;
-    const int row = n0 + r;
     const int col = m0 + r; // activation row this lane feeds into the B operand
 
     const int steps_total = (k + 63) / 64;
     const int s_begin = (int)(((int64_t)wave * steps_total) / KSPLIT);
     const int s_end = (int)(((int64_t)(wave + 1) * steps_total) / KSPLIT);
 
-    const int8_t *qrow = q + (int64_t)(row < n ? row : 0) * k;
+    const int8_t *qrow[RT];
+    bool row_ok[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const int row = n0 + 16 * t + r;
+        row_ok[t] = row < n;
+        qrow[t] = q + (int64_t)(row_ok[t] ? row : 0) * k;
+    }
     const uint16_t *xrow = x + (int64_t)(col < m ? col : 0) * k;
-    const bool row_ok = row < n;
     const bool col_ok = col < m;
 
-    float4v acc = {0.f, 0.f, 0.f, 0.f};
+    float4v acc[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+        acc[t] = (float4v){0.f, 0.f, 0.f, 0.f};
+
     for (int s = s_begin; s < s_end; s += kSkinnyUnroll) {
-        u32x4_t wv[kSkinnyUnroll];
+        u32x4_t wv[kSkinnyUnroll][RT];
         u32x4_t xa[kSkinnyUnroll], xb[kSkinnyUnroll];
 #pragma unroll
         for (int u = 0; u < kSkinnyUnroll; ++u) {
             const int kk = (s + u) * 64 + g * 16;
             const bool ok = (s + u) < s_end && kk < k;
-            wv[u] = (u32x4_t){0u, 0u, 0u, 0u};
-            if (ok && row_ok)
-                wv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(qrow + kk));
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                wv[u][t] = (u32x4_t){0u, 0u, 0u, 0u};
+                if (ok && row_ok[t])
+                    wv[u][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(qrow[t] + kk));
+            }
         }
 #pragma unroll
         for (int u = 0; u < kSkinnyUnroll; ++u) {
@@ -85,45 +97,81 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
         }
 #pragma unroll
         for (int u = 0; u < kSkinnyUnroll; ++u) {
-            const half8_t a0 = i8x8_to_half8(wv[u].x, wv[u].y);
-            const half8_t a1 = i8x8_to_half8(wv[u].z, wv[u].w);
             const half8_t b0 = __builtin_bit_cast(half8_t, xa[u]);
             const half8_t b1 = __builtin_bit_cast(half8_t, xb[u]);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, acc, 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                const half8_t a0 = i8x8_to_half8(wv[u][t].x, wv[u][t].y);
+                const half8_t a1 = i8x8_to_half8(wv[u][t].z, wv[u][t].w);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, acc[t], 0, 0, 0);
+            }
         }
     }
 
     if (KSPLIT > 1) {
-        partial[wave][lane] = acc;
+        if (wave > 0) {
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+                partial[wave - 1][t][lane] = acc[t];
+        }
         __syncthreads();
         if (wave != 0)
             return;
-        acc = partial[0][lane];
 #pragma unroll
-        for (int w = 1; w < KSPLIT; ++w)
-            acc += partial[w][lane];
+        for (int w = 0; w < KSPLIT - 1; ++w)
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+                acc[t] += partial[w][t][lane];
     }
-    // lane holds rows n0 + 4 g + i (i = 0..3) of activation column m0 + r
+    // lane holds rows n0 + 16 t + 4 g + i (i = 0..3) of activation column m0 + r
     const int ym = m0 + r;
     if (ym >= m)
         return;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int yn = n0 + 4 * g + i;
-        if (yn < n)
-            y[(int64_t)ym * n + yn] = f32_to_f16_bits(acc[i] * f16_bits_to_f32(scales[yn]));
+    for (int t = 0; t < RT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int yn = n0 + 16 * t + 4 * g + i;
+            if (yn < n)
+                y[(int64_t)ym * n + yn] = f32_to_f16_bits(acc[t][i] * f16_bits_to_f32(scales[yn]));
+        }
     }
 }
 
-template <int KSPLIT>
+template <int RT, int KSPLIT>
 hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
                       int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((n + 15) / 16), (unsigned)((m + 15) / 16));
-    hipLaunchKernelGGL((skinny_gemm_kernel<KSPLIT>), grid, dim3(KSPLIT * kWave), 0, stream,
+    const dim3 grid((unsigned)((n + 16 * RT - 1) / (16 * RT)), (unsigned)((m + 15) / 16));
+    hipLaunchKernelGGL((skinny_gemm_kernel<RT, KSPLIT>), grid, dim3(KSPLIT * kWave), 0, stream,
                        x, q, scales, y, (int)m, (int)n, (int)k);
     return hipGetLastError();
+}
+
+template <int RT>
+hipError_t launch_rt(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
+                     int64_t m, int64_t n, int64_t k, hipStream_t stream)
+{
+    // split k until the grid holds about kSkinnyTargetWaves waves, keeping
+    // at least one 64-wide step per wave
+    const int64_t tiles = ((n + 16 * RT - 1) / (16 * RT)) * ((m + 15) / 16);
+    const int64_t steps = (k + 63) / 64;
+    int ksplit = 1;
+    while (ksplit < 16 && tiles * ksplit < kSkinnyTargetWaves && steps >= 2 * ksplit)
+        ksplit *= 2;
+    switch (ksplit) {
+    case 1:
+        return launch_cfg<RT, 1>(x, q, scales, y, m, n, k, stream);
+    case 2:
+        return launch_cfg<RT, 2>(x, q, scales, y, m, n, k, stream);
+    case 4:
+        return launch_cfg<RT, 4>(x, q, scales, y, m, n, k, stream);
+    case 8:
+        return launch_cfg<RT, 8>(x, q, scales, y, m, n, k, stream);
+    default:
+        return launch_cfg<RT, 16>(x, q, scales, y, m, n, k, stream);
+    }
 }
 
 } // namespace
@@ -131,23 +179,10 @@ hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales
 hipError_t launch_skinny_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
                               uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
-    // split k until the grid holds about kSkinnyTargetWaves waves, keeping
-    // at least one 64-wide step per wave
-    const int64_t tiles = ((n + 15) / 16) * ((m + 15) / 16);
-    const int64_t steps = (k + 63) / 64;
-    int ksplit = 1;
-    while (ksplit < 8 && tiles * ksplit < kSkinnyTargetWaves && steps >= 2 * ksplit)
-        ksplit *= 2;
-    switch (ksplit) {
-    case 1:
-        return launch_cfg<1>(x, q, scales, y, m, n, k, stream);
-    case 2:
-        return launch_cfg<2>(x, q, scales, y, m, n, k, stream);
-    case 4:
-        return launch_cfg<4>(x, q, scales, y, m, n, k, stream);
-    default:
-        return launch_cfg<8>(x, q, scales, y, m, n, k, stream);
-    }
+    // two 16-row weight tiles per wave: the activation operand is reused
+    // twice; four tiles measured slower (fewer waves, longer dependent
+    // MFMA chains)
+    return launch_rt<2>(x, q, scales, y, m, n, k, stream);
 }
 
 } // namespace qw
