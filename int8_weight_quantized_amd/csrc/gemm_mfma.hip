@@ -52,9 +52,6 @@ constexpr int kGemmThreads = 256; // 2 x 2 waves
 #ifndef QW_DMA_BM
 #define QW_DMA_BM 128
 #endif
-#ifndef QW_DMA_STAGES
-#define QW_DMA_STAGES 2
-#endif
 constexpr int kBK = 64;            // k per step
 constexpr int kWRow = kBK + 16;    // LDS bytes per int8 weight row (padded)
 constexpr int kXRow = 2 * kBK + 16; // LDS bytes per fp16 activation row (padded)
@@ -245,22 +242,27 @@ hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales
 }
 
 // ---------------------------------------------------------------------------
-// Big-tile variant for prefill-sized m: 256 x 256 output tile per
-// workgroup, one wave per SIMD, each wave 128 x 128 (256 fp32 accumulators
-// in AGPRs).  Operands are copied from global memory straight into LDS by
+// Big-tile variant for prefill-sized m: a 256 x BM output tile per
+// workgroup of 4 waves (one per SIMD), each wave 128 output channels x BM/2
+// activation rows on v_mfma_f32_32x32x16_f16 with fp32 accumulators in
+// registers.  Operands are copied from global memory straight into LDS by
 // the gfx950 LDS-DMA loads (global_load_lds_dwordx4: each lane's 16 bytes
-// land at LDS base + 16 * lane) through a 3-stage ring:
+// land at LDS base + 16 * lane) into two LDS stages:
 //
-//   iteration t:
+//   step t:
 //     wait for my copies of tile t; barrier (everyone's copies landed,
 //       everyone done reading tile t-1)
-//     start copying tile t+2 into tile t-1's stage
-//     LDS -> registers: operands of tile t; MFMAs of tile t
+//     start copying tile t + 1 into tile t-1's stage
+//     LDS -> registers: operands of tile t; dequantize; MFMAs of tile t
 //
-// so up to two tiles are in flight while one is multiplied; one barrier
-// per k step.  (Measured: prefetching the next tile's operands into a
-// second register set during the MFMAs was slower here; the register
-// copies it needs stall on MFMA source-operand hazards.)
+// one barrier per k step.  (Two workgroups of 67 KiB share a CU, so the
+// second one's MFMAs fill the first one's copy and LDS phases; a third
+// stage would not fit twice.)  Each stage is a separate LDS array and the
+// steady-state loop is unrolled by two so that every access names its
+// array at compile time: the compiler then sees that the LDS reads of
+// tile t cannot alias the copies in flight into other stages and does not
+// wait for them (with one array it drains every copy before the first LDS
+// read of each step, which exposes the full copy latency per k step).
 //
 // LDS-DMA writes 1 KiB contiguous per wave instruction, so rows cannot be
 // padded; instead 16-byte chunks are XOR-swizzled within a row, with a
@@ -279,8 +281,8 @@ constexpr int kDmaWBytes = kDmaBN * kBK;   // 16 KiB int8 weight tile per stage
 constexpr int kDmaSI = 4; // 32 x 32 MFMA tiles per wave along n (128 rows)
 
 // NW waves per workgroup in a 2 (n) x NW/2 (m) grid; each wave owns 128
-// output channels x BM/(NW/2) activation rows.  STAGES-deep LDS ring.
-template <int NW, int BM, int STAGES>
+// output channels x BM/(NW/2) activation rows.
+template <int NW, int BM>
 struct DmaCfg {
     static constexpr int kThreads = NW * kWave;
     static constexpr int kXBytes = BM * kBK * 2;             // fp16 activation tile per stage
@@ -290,9 +292,15 @@ struct DmaCfg {
     static constexpr int kInstr = kWInstr + kXInstr;
     static constexpr int kWaveM = BM / (NW / 2);
     static constexpr int kSJ = kWaveM / 32;                   // 32 x 32 MFMA tiles along m
-    static constexpr int kAhead = STAGES - 1;                 // tiles copied ahead
+    // epilogue: the fp16 output tile, [BM][kDmaBN] with rows padded by 16
+    // bytes; rows [0, BM/2) go to stage 0's array, [BM/2, BM) to stage 1's
+    static constexpr int kYRow = kDmaBN * 2 + 16;
+    static constexpr int kYHalf = (BM / 2) * kYRow;
+    static constexpr int kStageAlloc = kStage > kYHalf ? kStage : kYHalf;
     static_assert(kWInstr * 64 * 16 * NW == kDmaWBytes && kXInstr * 64 * 16 * NW == kXBytes, "copy split");
-    static_assert(kSJ >= 1 && kAhead >= 1 && kAhead <= 2, "tile config");
+    static_assert(kSJ >= 1, "tile config");
+    static_assert(kDmaBN % kThreads == 0, "scale staging");
+    static_assert(NW == 4, "epilogue image halves follow the two m-waves");
 };
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
@@ -329,16 +337,27 @@ __device__ __forceinline__ int xslot(int row)
     return (r16 ^ (r16 >> 3)) & 7;
 }
 
-template <int NW, int BM, int STAGES>
+template <int I>
+using stage_t = std::integral_constant<int, I>;
+
+template <int NW, int BM>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(BM <= 128 ? 2 : 1))) void mfma_gemm_dma_kernel(
     const uint16_t *__restrict__ x, const int8_t *__restrict__ q,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y,
     int m, int n, int k, int tiles_m, int tiles_n)
 {
-    using C = DmaCfg<NW, BM, STAGES>;
+    using C = DmaCfg<NW, BM>;
     constexpr int kSJ = C::kSJ;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * C::kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring0[C::kStageAlloc];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring1[C::kStageAlloc];
+    __shared__ __attribute__((aligned(16))) float scale_lds[kDmaBN];
+    auto ring = [&](auto s) -> uint8_t * {
+        if constexpr (decltype(s)::value == 0)
+            return ring0;
+        else
+            return ring1;
+    };
 
     const int tid = threadIdx.x;
     const int lane = __lane_id();
@@ -365,9 +384,8 @@ __attribute__((amdgpu_waves_per_eu(BM <= 128 ? 2 : 1))) void mfma_gemm_dma_kerne
     const int xchunk_even = (lane % 8) ^ xslot(lane / 8);
     const int xchunk_odd = (lane % 8) ^ xslot(8 + lane / 8);
 
-    // copy tile kt into its stage; FULL: every chunk lies inside k
-    auto issue = [&](int kt, auto full) {
-        uint8_t *st = lds + (kt % STAGES) * C::kStage;
+    // copy tile kt into stage array st; FULL: every chunk lies inside k
+    auto issue = [&](int kt, uint8_t *st, auto full) {
         const int k0 = kt * kBK;
 #pragma unroll
         for (int i = 0; i < C::kWInstr; ++i) {
@@ -420,8 +438,7 @@ __attribute__((amdgpu_waves_per_eu(BM <= 128 ? 2 : 1))) void mfma_gemm_dma_kerne
         for (int j = 0; j < kSJ; ++j)
             acc[i][j] = (float16v){};
 
-    auto compute = [&](int t) {
-        const uint8_t *st = lds + (t % STAGES) * C::kStage;
+    auto compute = [&](const uint8_t *st) {
         u32x4_t clo[kDmaSI], chi[kDmaSI];
 #pragma unroll
         for (int i = 0; i < kDmaSI; ++i) {
@@ -447,79 +464,97 @@ __attribute__((amdgpu_waves_per_eu(BM <= 128 ? 2 : 1))) void mfma_gemm_dma_kerne
         }
     };
 
-    // prologue: kAhead tiles in flight
+    // prologue: tile 0 in flight
+    if (0 < ktiles)
+        issue(0, ring0, partial_t{});
+
+    // this tile's per-channel scales, staged once in LDS for the epilogue;
+    // the first barrier of the main loop publishes the LDS writes
 #pragma unroll
-    for (int a = 0; a < C::kAhead; ++a)
-        if (a < ktiles)
-            issue(a, partial_t{});
+    for (int c = tid; c < kDmaBN; c += C::kThreads)
+        scale_lds[c] = n0 + c < n ? f16_bits_to_f32(scales[n0 + c]) : 0.0f;
 
-    // Steady state: every tile involved is full, the loop body has no
-    // branches.  Step t waits for its own copies of tile t (leaving the
-    // kAhead - 1 newer tiles in flight), the barrier publishes everyone's
-    // copies and certifies that tile t-1's stage is no longer read, then
-    // tile t + kAhead is copied into that stage while tile t is multiplied.
+    // Step t (stage t % 2) waits for its own copies of tile t, the barrier
+    // publishes everyone's copies and certifies that tile t-1's stage is no
+    // longer read, tile t + 1 is copied into that stage while tile t is
+    // multiplied.  FULL: tile t + 1 lies inside k (no per-chunk checks).
+    auto step = [&](int t, auto s, auto full) {
+        constexpr int S = decltype(s)::value;
+        QW_WAIT_VMCNT(0);
+        ring_barrier();
+        if (decltype(full)::value || t + 1 < ktiles)
+            issue(t + 1, ring(stage_t<1 - S>{}), full);
+        compute(ring(s));
+    };
+    // steady state: pairs of steps whose next tile is full
     int t = 0;
-    const int steady = full_tiles - C::kAhead > 0 ? full_tiles - C::kAhead : 0;
-    for (; t < steady; ++t) {
-        QW_WAIT_VMCNT((C::kAhead - 1) * C::kInstr);
-        ring_barrier();
-        issue(t + C::kAhead, full_t{});
-        compute(t);
+    for (; t + 2 < full_tiles; t += 2) {
+        step(t, stage_t<0>{}, full_t{});
+        step(t + 1, stage_t<1>{}, full_t{});
     }
-    // Drain: the remaining tiles (and the ragged one) with exact waits.
-    for (; t < ktiles; ++t) {
-        const int newest = min(t + C::kAhead - 1, ktiles - 1);
-        if (newest > t && newest < full_tiles)
-            QW_WAIT_VMCNT((C::kAhead - 1) * C::kInstr);
+    // at most three tiles remain: the last full pair's, and a ragged one
+    for (int d = 0; d < 3; ++d) {
+        if (t + d >= ktiles)
+            break;
+        if (d == 1)
+            step(t + d, stage_t<1>{}, partial_t{});
         else
-            QW_WAIT_VMCNT(0);
-        ring_barrier();
-        if (t + C::kAhead < ktiles)
-            issue(t + C::kAhead, partial_t{});
-        compute(t);
+            step(t + d, stage_t<0>{}, partial_t{});
     }
 
-    // ---- epilogue: scale, round to fp16, store ----
+    // ---- epilogue: scale, round to fp16, transpose through LDS, store ----
     // 32 x 32 output layout: accumulator r of lane l is row
     // 8 (r / 4) + 4 (l / 32) + (r % 4), column l % 32 of the MFMA tile, so
     // each group of 4 registers is 4 consecutive output channels of one
-    // activation row: one 8-byte store.
-    const bool vec_ok = (n % 4) == 0;
+    // activation row.  They are scaled, rounded and written as 8 bytes into
+    // the tile's [activation row][channel] image in LDS (row stride
+    // 2 * kDmaBN + 16 bytes: the 32 rows one instruction touches fall on
+    // distinct bank pairs); then the workgroup copies the image out in
+    // 16-byte pieces, so every wave writes whole 512-byte row segments of Y
+    // instead of scattered 8-byte pieces of 32 rows.
+    ring_barrier(); // every wave is done reading the ring
+    // a wave's kWaveM = BM / 2 activation rows all fall in one half
+    uint8_t *img_base = (wave_m == 0 ? ring0 : ring1) + lrow * C::kYRow;
 #pragma unroll
     for (int i = 0; i < kDmaSI; ++i) {
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
-            const int gn = n0 + wave_n * 128 + i * 32 + 8 * qd + 4 * lgrp;
-            float sc[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sc[r] = (gn + r < n) ? f16_bits_to_f32(scales[gn + r]) : 0.0f;
+            const int nl = wave_n * 128 + i * 32 + 8 * qd + 4 * lgrp;
+            const float4v sc = *reinterpret_cast<const float4v *>(scale_lds + nl);
 #pragma unroll
             for (int j = 0; j < kSJ; ++j) {
-                const int gm = m0 + wave_m * C::kWaveM + j * 32 + lrow;
-                if (gm >= m)
-                    continue;
-                uint16_t out[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    out[r] = f32_to_f16_bits(acc[i][j][4 * qd + r] * sc[r]);
-                uint16_t *dst = y + (int64_t)gm * n + gn;
-                if (vec_ok && gn + 3 < n) {
-                    u32x2_t pk = {(uint32_t)out[0] | ((uint32_t)out[1] << 16),
-                                  (uint32_t)out[2] | ((uint32_t)out[3] << 16)};
-                    *reinterpret_cast<u32x2_t *>(dst) = pk;
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (gn + r < n)
-                            dst[r] = out[r];
-                }
+                uint8_t *img = img_base + (j * 32) * C::kYRow;
+                const uint32_t o0 = f32_to_f16_bits(acc[i][j][4 * qd + 0] * sc[0]);
+                const uint32_t o1 = f32_to_f16_bits(acc[i][j][4 * qd + 1] * sc[1]);
+                const uint32_t o2 = f32_to_f16_bits(acc[i][j][4 * qd + 2] * sc[2]);
+                const uint32_t o3 = f32_to_f16_bits(acc[i][j][4 * qd + 3] * sc[3]);
+                *reinterpret_cast<u32x2_t *>(img + nl * 2) = (u32x2_t){o0 | (o1 << 16), o2 | (o3 << 16)};
             }
+        }
+    }
+    ring_barrier();
+    constexpr int kRowChunks = kDmaBN / 8; // 16-byte pieces per output row
+    const bool vec_ok = (n % 8) == 0 && n0 + kDmaBN <= n;
+    const int rows = min(BM, m - m0);
+    for (int c = tid; c < rows * kRowChunks; c += C::kThreads) {
+        const int row = c / kRowChunks;
+        const int cc = c % kRowChunks;
+        const uint8_t *img = row < BM / 2 ? ring0 + row * C::kYRow : ring1 + (row - BM / 2) * C::kYRow;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(img + cc * 16);
+        uint16_t *dst = y + (int64_t)(m0 + row) * n + n0 + cc * 8;
+        if (vec_ok) {
+            *reinterpret_cast<u32x4_t *>(dst) = v;
+        } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n0 + cc * 8 + e < n)
+                    dst[e] = (uint16_t)(w[e / 2] >> (16 * (e % 2)));
         }
     }
 }
 
-template <int NW, int BM, int STAGES>
+template <int NW, int BM>
 hipError_t launch_dma(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
                       int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
@@ -528,7 +563,7 @@ hipError_t launch_dma(const uint16_t *x, const int8_t *q, const uint16_t *scales
     const int64_t blocks = tiles_m * tiles_n;
     if (blocks > 0x7fffffff)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((mfma_gemm_dma_kernel<NW, BM, STAGES>), dim3((unsigned)blocks), dim3(NW * kWave),
+    hipLaunchKernelGGL((mfma_gemm_dma_kernel<NW, BM>), dim3((unsigned)blocks), dim3(NW * kWave),
                        0, stream, x, q, scales, y, (int)m, (int)n, (int)k, (int)tiles_m, (int)tiles_n);
     return hipGetLastError();
 }
@@ -542,7 +577,7 @@ hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *
         return launch_cfg<128, 32>(x, q, scales, y, m, n, k, stream);
     if (m <= 64)
         return launch_cfg<128, 64>(x, q, scales, y, m, n, k, stream);
-    return launch_dma<4, QW_DMA_BM, QW_DMA_STAGES>(x, q, scales, y, m, n, k, stream);
+    return launch_dma<4, QW_DMA_BM>(x, q, scales, y, m, n, k, stream);
 }
 
 } // namespace qw

@@ -84,7 +84,7 @@ SMALL_SHAPES = [
 MFMA_SHAPES = SMALL_SHAPES + [
     (9, 200, 272), (16, 128, 64), (17, 300, 528), (31, 129, 80), (33, 257, 1024),
     (64, 256, 256), (65, 130, 96), (100, 390, 656), (128, 128, 4096), (130, 260, 4112),
-    (257, 129, 144), (300, 513, 1040),
+    (257, 129, 144), (300, 513, 1040), (129, 600, 528), (256, 1024, 336),
 ]
 
 
