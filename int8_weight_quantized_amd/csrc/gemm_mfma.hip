@@ -52,6 +52,9 @@ constexpr int kGemmThreads = 256; // 2 x 2 waves
 #ifndef QW_DMA_BM
 #define QW_DMA_BM 128
 #endif
+#ifndef QW_DMA_NW
+#define QW_DMA_NW 4
+#endif
 constexpr int kBK = 64;            // k per step
 constexpr int kWRow = kBK + 16;    // LDS bytes per int8 weight row (padded)
 constexpr int kXRow = 2 * kBK + 16; // LDS bytes per fp16 activation row (padded)
@@ -243,9 +246,11 @@ hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales
 
 // ---------------------------------------------------------------------------
 // Big-tile variant for prefill-sized m: a 256 x BM output tile per
-// workgroup of 4 waves (one per SIMD), each wave 128 output channels x BM/2
+// workgroup of 4 waves (one per SIMD), each wave 64 output channels x all BM
 // activation rows on v_mfma_f32_32x32x16_f16 with fp32 accumulators in
-// registers.  Operands are copied from global memory straight into LDS by
+// registers.  (Splitting the channels rather than the rows halves the
+// per-wave int8 -> fp16 casts, each cast weight operand feeding BM / 32
+// MFMAs; the price is that every wave reads the whole activation tile.)  Operands are copied from global memory straight into LDS by
 // the gfx950 LDS-DMA loads (global_load_lds_dwordx4: each lane's 16 bytes
 // land at LDS base + 16 * lane) into two LDS stages:
 //
@@ -278,10 +283,9 @@ hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales
 // ---------------------------------------------------------------------------
 constexpr int kDmaBN = 256;                // output channels per workgroup
 constexpr int kDmaWBytes = kDmaBN * kBK;   // 16 KiB int8 weight tile per stage
-constexpr int kDmaSI = 4; // 32 x 32 MFMA tiles per wave along n (128 rows)
 
-// NW waves per workgroup in a 2 (n) x NW/2 (m) grid; each wave owns 128
-// output channels x BM/(NW/2) activation rows.
+// NW waves per workgroup side by side along n; each wave owns kDmaBN / NW
+// output channels x all BM activation rows.
 template <int NW, int BM>
 struct DmaCfg {
     static constexpr int kThreads = NW * kWave;
@@ -290,17 +294,16 @@ struct DmaCfg {
     static constexpr int kWInstr = kDmaWBytes / 1024 / NW;   // copies per wave per stage
     static constexpr int kXInstr = kXBytes / 1024 / NW;
     static constexpr int kInstr = kWInstr + kXInstr;
-    static constexpr int kWaveM = BM / (NW / 2);
-    static constexpr int kSJ = kWaveM / 32;                   // 32 x 32 MFMA tiles along m
+    static constexpr int kWaveN = kDmaBN / NW;               // output channels per wave
+    static constexpr int kSI = kWaveN / 32;                   // 32 x 32 MFMA tiles along n
+    static constexpr int kSJ = BM / 32;                       // 32 x 32 MFMA tiles along m
     // epilogue: the fp16 output tile, [BM][kDmaBN] with rows padded by 16
     // bytes; rows [0, BM/2) go to stage 0's array, [BM/2, BM) to stage 1's
     static constexpr int kYRow = kDmaBN * 2 + 16;
     static constexpr int kYHalf = (BM / 2) * kYRow;
     static constexpr int kStageAlloc = kStage > kYHalf ? kStage : kYHalf;
     static_assert(kWInstr * 64 * 16 * NW == kDmaWBytes && kXInstr * 64 * 16 * NW == kXBytes, "copy split");
-    static_assert(kSJ >= 1, "tile config");
-    static_assert(kDmaBN % kThreads == 0, "scale staging");
-    static_assert(NW == 4, "epilogue image halves follow the two m-waves");
+    static_assert(kSI >= 1 && kWaveN % 32 == 0 && BM % 64 == 0, "tile config");
 };
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
@@ -342,7 +345,7 @@ using stage_t = std::integral_constant<int, I>;
 
 template <int NW, int BM>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(BM <= 128 ? 2 : 1))) void mfma_gemm_dma_kernel(
+__attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm_dma_kernel(
     const uint16_t *__restrict__ x, const int8_t *__restrict__ q,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y,
     int m, int n, int k, int tiles_m, int tiles_n)
@@ -362,8 +365,6 @@ __attribute__((amdgpu_waves_per_eu(BM <= 128 ? 2 : 1))) void mfma_gemm_dma_kerne
     const int tid = threadIdx.x;
     const int lane = __lane_id();
     const int wave = tid / kWave;
-    const int wave_n = wave % 2;
-    const int wave_m = wave / 2;
 
     const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
     const int tn = tile / tiles_m;
@@ -422,26 +423,26 @@ __attribute__((amdgpu_waves_per_eu(BM <= 128 ? 2 : 1))) void mfma_gemm_dma_kerne
     // activation row per step.
     const int lrow = lane % 32;
     const int lgrp = lane / 32;
-    const int wrow = wave_n * 128 + lrow;       // + 32 i
+    const int wrow = wave * C::kWaveN + lrow;   // + 32 i
     const int w_off0 = wrow * kBK + 16 * ((2 * lgrp) ^ wslot(wrow));
     const int w_off1 = wrow * kBK + 16 * ((2 * lgrp + 1) ^ wslot(wrow));
-    const int xrow = wave_m * C::kWaveM + lrow; // + 32 j
+    const int xrow = lrow;                      // + 32 j
     int x_off[4];
 #pragma unroll
     for (int sidx = 0; sidx < 4; ++sidx)
         x_off[sidx] = kDmaWBytes + xrow * 2 * kBK + 16 * ((4 * lgrp + sidx) ^ xslot(xrow));
 
-    float16v acc[kDmaSI][kSJ];
+    float16v acc[C::kSI][kSJ];
 #pragma unroll
-    for (int i = 0; i < kDmaSI; ++i)
+    for (int i = 0; i < C::kSI; ++i)
 #pragma unroll
         for (int j = 0; j < kSJ; ++j)
             acc[i][j] = (float16v){};
 
     auto compute = [&](const uint8_t *st) {
-        u32x4_t clo[kDmaSI], chi[kDmaSI];
+        u32x4_t clo[C::kSI], chi[C::kSI];
 #pragma unroll
-        for (int i = 0; i < kDmaSI; ++i) {
+        for (int i = 0; i < C::kSI; ++i) {
             clo[i] = *reinterpret_cast<const u32x4_t *>(st + w_off0 + i * 32 * kBK);
             chi[i] = *reinterpret_cast<const u32x4_t *>(st + w_off1 + i * 32 * kBK);
         }
@@ -454,7 +455,7 @@ __attribute__((amdgpu_waves_per_eu(BM <= 128 ? 2 : 1))) void mfma_gemm_dma_kerne
 #pragma unroll
         for (int sidx = 0; sidx < 4; ++sidx) {
 #pragma unroll
-            for (int i = 0; i < kDmaSI; ++i) {
+            for (int i = 0; i < C::kSI; ++i) {
                 const u32x4_t c = sidx < 2 ? clo[i] : chi[i];
                 const half8_t a = (sidx & 1) ? i8x8_to_half8(c.z, c.w) : i8x8_to_half8(c.x, c.y);
 #pragma unroll
@@ -484,6 +485,10 @@ __attribute__((amdgpu_waves_per_eu(BM <= 128 ? 2 : 1))) void mfma_gemm_dma_kerne
         ring_barrier();
         if (decltype(full)::value || t + 1 < ktiles)
             issue(t + 1, ring(stage_t<1 - S>{}), full);
+        // keep the copies at the top of the step: nothing ties them to the
+        // MFMAs, and the scheduler would otherwise sink them below the
+        // whole step, right before the wait for them
+        __builtin_amdgcn_sched_barrier(0);
         compute(ring(s));
     };
     // steady state: pairs of steps whose next tile is full
@@ -513,17 +518,17 @@ __attribute__((amdgpu_waves_per_eu(BM <= 128 ? 2 : 1))) void mfma_gemm_dma_kerne
     // 16-byte pieces, so every wave writes whole 512-byte row segments of Y
     // instead of scattered 8-byte pieces of 32 rows.
     ring_barrier(); // every wave is done reading the ring
-    // a wave's kWaveM = BM / 2 activation rows all fall in one half
-    uint8_t *img_base = (wave_m == 0 ? ring0 : ring1) + lrow * C::kYRow;
 #pragma unroll
-    for (int i = 0; i < kDmaSI; ++i) {
+    for (int i = 0; i < C::kSI; ++i) {
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
-            const int nl = wave_n * 128 + i * 32 + 8 * qd + 4 * lgrp;
+            const int nl = wave * C::kWaveN + i * 32 + 8 * qd + 4 * lgrp;
             const float4v sc = *reinterpret_cast<const float4v *>(scale_lds + nl);
 #pragma unroll
             for (int j = 0; j < kSJ; ++j) {
-                uint8_t *img = img_base + (j * 32) * C::kYRow;
+                // rows [0, BM/2) of the image live in stage 0's array
+                uint8_t *img = j < kSJ / 2 ? ring0 + (j * 32 + lrow) * C::kYRow
+                                           : ring1 + (j * 32 - BM / 2 + lrow) * C::kYRow;
                 const uint32_t o0 = f32_to_f16_bits(acc[i][j][4 * qd + 0] * sc[0]);
                 const uint32_t o1 = f32_to_f16_bits(acc[i][j][4 * qd + 1] * sc[1]);
                 const uint32_t o2 = f32_to_f16_bits(acc[i][j][4 * qd + 2] * sc[2]);
@@ -543,7 +548,9 @@ __attribute__((amdgpu_waves_per_eu(BM <= 128 ? 2 : 1))) void mfma_gemm_dma_kerne
         const u32x4_t v = *reinterpret_cast<const u32x4_t *>(img + cc * 16);
         uint16_t *dst = y + (int64_t)(m0 + row) * n + n0 + cc * 8;
         if (vec_ok) {
-            *reinterpret_cast<u32x4_t *>(dst) = v;
+            // streamed past the caches: Y is not read again here, and dirty
+            // lines left in L2 would be written back at the end of the kernel
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst));
         } else {
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -577,7 +584,7 @@ hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *
         return launch_cfg<128, 32>(x, q, scales, y, m, n, k, stream);
     if (m <= 64)
         return launch_cfg<128, 64>(x, q, scales, y, m, n, k, stream);
-    return launch_dma<4, QW_DMA_BM>(x, q, scales, y, m, n, k, stream);
+    return launch_dma<QW_DMA_NW, QW_DMA_BM>(x, q, scales, y, m, n, k, stream);
 }
 
 } // namespace qw
