@@ -9,9 +9,10 @@
 // byte-permute trick, and dotted with fp16 activations on v_dot2_f32_f16
 // (fp32 accumulation).  The per-channel scale multiplies the fp32 sum.
 //
-// Work split.  The grid is sized to what the chip holds at once (W waves);
-// wave w owns rows w, w + W, w + 2W, ... (balanced to one row), walked RU
-// rows at a time, so at any moment the waves of the chip read one compact
+// Work split.  The grid is sized to what the chip holds at once (W waves,
+// at most WPC per CU, W chosen so that every wave gets the same number of
+// RU-row groups); wave w owns rows w, w + W, w + 2W, ..., walked RU rows at
+// a time, so at any moment the waves of the chip read one compact
 // window of rows (DRAM page locality) instead of W scattered streams.  For
 // one row, lane l reads bytes [c*1024 + 16 l, +16) for every 1 KiB chunk c:
 // each load instruction of the wave covers 1 KiB of one row, fully
@@ -27,10 +28,6 @@
 #include "qw_device.h"
 #include "qw_internal.h"
 
-#ifndef QW_GEMV_WAVES_PER_CU
-#define QW_GEMV_WAVES_PER_CU 16
-#endif
-
 namespace qw {
 namespace {
 
@@ -38,6 +35,7 @@ constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;
 constexpr int kChunkK = kWave * 16; // k values covered by one wave-wide 16-byte load
 constexpr int kGemvMaxMChunks = 32; // LDS budget: 32 * 2 KiB = 64 KiB
+constexpr int64_t kLdsPerCu = 160 * 1024;
 
 template <int MT, int RU, int CH>
 struct GemvItem {
@@ -172,17 +170,26 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     }
 }
 
-template <int MT, int RU, int CH>
+template <int MT, int RU, int CH, int WPC>
 hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
                       int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
     const int chunks = (int)((k + kChunkK - 1) / kChunkK);
     const size_t lds = (size_t)MT * chunks * 2 * kWave * sizeof(u32x4_t);
-    // one wave per RU rows at most; otherwise as many waves as the chip keeps resident
-    int64_t waves = (n + RU - 1) / RU;
-    const int64_t cap = (int64_t)device_cu_count() * QW_GEMV_WAVES_PER_CU;
-    if (waves > cap)
-        waves = cap;
+    // one wave per RU rows at most; otherwise about as many waves as the chip
+    // keeps resident (WPC per CU), trimmed so that every wave walks the same
+    // number of RU-row groups (no half-empty last round)
+    const int64_t groups = (n + RU - 1) / RU;
+    int64_t waves = groups;
+    int64_t wpc = WPC;
+    const int64_t lds_wgs = kLdsPerCu / (int64_t)lds; // workgroups one CU's LDS holds
+    if (wpc > lds_wgs * kGemvWaves)
+        wpc = lds_wgs * kGemvWaves;
+    const int64_t cap = (int64_t)device_cu_count() * wpc;
+    if (waves > cap) {
+        const int64_t per = (groups + cap - 1) / cap;
+        waves = (groups + per - 1) / per;
+    }
     const int blocks = (int)((waves + kGemvWaves - 1) / kGemvWaves);
     hipLaunchKernelGGL((gemv_kernel<MT, RU, CH>), dim3(blocks), dim3(kGemvThreads), lds, stream,
                        x, q, scales, y, (int)m, (int)n, (int)k, chunks, (int)waves);
@@ -205,13 +212,15 @@ bool gemv_supported(int64_t m, int64_t k)
 hipError_t launch_gemv(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
                        int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
+    // (MT, RU, CH, waves per CU) from measured sweeps; WPC stays within what
+    // each configuration's register use lets a CU hold at once
     if (m <= 1)
-        return launch_cfg<1, 4, 4>(x, q, scales, y, m, n, k, stream);
+        return launch_cfg<1, 2, 4, 28>(x, q, scales, y, m, n, k, stream);
     if (m <= 2)
-        return launch_cfg<2, 4, 2>(x, q, scales, y, m, n, k, stream);
+        return launch_cfg<2, 4, 2, 16>(x, q, scales, y, m, n, k, stream);
     if (m <= 4)
-        return launch_cfg<4, 2, 2>(x, q, scales, y, m, n, k, stream);
-    return launch_cfg<8, 2, 2>(x, q, scales, y, m, n, k, stream);
+        return launch_cfg<4, 2, 2, 16>(x, q, scales, y, m, n, k, stream);
+    return launch_cfg<8, 2, 2, 16>(x, q, scales, y, m, n, k, stream);
 }
 
 } // namespace qw
