@@ -21,8 +21,10 @@
 // row tiles (activation traffic from L2 is 2/RT of the weight traffic).
 // UNROLL steps are issued before any is consumed.  KSPLIT is chosen so the
 // grid has enough waves to keep HBM busy.  The KSPLIT partial tiles are
-// summed in LDS in wave order (deterministic), then scaled, rounded to fp16
-// and stored.
+// summed in LDS in wave order (deterministic), then scaled (the scales are
+// loaded at the start, so their latency hides under the main loop), rounded
+// to fp16 and transposed through LDS, so that Y is written in whole 16-byte
+// pieces of its rows.
 #include "qw_device.h"
 #include "qw_internal.h"
 
@@ -41,6 +43,8 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
     int m, int n, int k)
 {
     __shared__ float4v partial[KSPLIT > 1 ? KSPLIT - 1 : 1][RT][kWave];
+    // the finished fp16 tile, [activation row][channel], padded rows
+    __shared__ __attribute__((aligned(16))) uint16_t ytile[16][16 * RT + 8];
 
     const int lane = __lane_id();
     const int wave = threadIdx.x / kWave;
@@ -64,6 +68,18 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
     }
     const uint16_t *xrow = x + (int64_t)(col < m ? col : 0) * k;
     const bool col_ok = col < m;
+
+    // the scales of the outputs this lane ends up holding (channels
+    // n0 + 16 t + 4 g + i), loaded now so that they arrive during the main
+    // loop instead of stalling the epilogue
+    uint16_t sc[RT][4];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int yn = n0 + 16 * t + 4 * g + i;
+            sc[t][i] = yn < n ? scales[yn] : (uint16_t)0;
+        }
 
     float4v acc[RT];
 #pragma unroll
@@ -124,17 +140,34 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
             for (int t = 0; t < RT; ++t)
                 acc[t] += partial[w][t][lane];
     }
-    // lane holds rows n0 + 16 t + 4 g + i (i = 0..3) of activation column m0 + r
-    const int ym = m0 + r;
-    if (ym >= m)
-        return;
+    // lane holds channels n0 + 16 t + 4 g + i (i = 0..3) of activation row
+    // m0 + r: scale, round, and transpose through LDS so that the stores
+    // are whole 16-byte pieces of Y rows
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
+    for (int t = 0; t < RT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int yn = n0 + 16 * t + 4 * g + i;
-            if (yn < n)
-                y[(int64_t)ym * n + yn] = f32_to_f16_bits(acc[t][i] * f16_bits_to_f32(scales[yn]));
+        for (int i = 0; i < 4; ++i)
+            ytile[r][16 * t + 4 * g + i] = f32_to_f16_bits(acc[t][i] * f16_bits_to_f32(sc[t][i]));
+    // the tile is written and read back by the same wave: LDS keeps a
+    // wave's accesses in order; the barrier only stops the compiler from
+    // moving the reads above the writes
+    __builtin_amdgcn_wave_barrier();
+    constexpr int kPieces = 16 * RT / 8;  // 16-byte pieces per tile row
+    const bool vec_ok = (n % 8) == 0 && n0 + 16 * RT <= n;
+    for (int e = lane; e < 16 * kPieces; e += kWave) {
+        const int row = e / kPieces;
+        const int pc = e % kPieces;
+        const int ym = m0 + row;
+        if (ym >= m)
+            continue;
+        uint16_t *dst = y + (int64_t)ym * n + n0 + 8 * pc;
+        if (vec_ok) {
+            *reinterpret_cast<u32x4_t *>(dst) = *reinterpret_cast<const u32x4_t *>(&ytile[row][8 * pc]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (n0 + 8 * pc + j < n)
+                    dst[j] = ytile[row][8 * pc + j];
         }
     }
 }

@@ -111,6 +111,23 @@ def test_skinny_small_shapes(m, n, k):
     assert_gemm_close(y, oracle.gemm(x, q, s), "skinny %dx%dx%d" % (m, n, k))
 
 
+# Long rows: k beyond what the GEMV stages in LDS (it then falls back to the
+# skinny kernel), and long reductions on every path.
+LONG_K_SHAPES = [(1, 64, 65536), (2, 40, 32784), (9, 72, 16400), (70, 72, 16400)]
+
+
+@pytest.mark.parametrize("m,n,k", LONG_K_SHAPES)
+def test_gemm_long_k(m, n, k):
+    x, q, s = _small_case(m, n, k, seed=7 * m + n)
+    say("gemm long-k auto m=%d n=%d k=%d" % (m, n, k))
+    y = gpu_gemm(x, q, s)
+    assert_gemm_close(y, oracle.gemm(x, q, s), "long-k auto %dx%dx%d" % (m, n, k))
+    for path in (SKINNY, MFMA):
+        say("gemm long-k path=%d m=%d n=%d k=%d" % (path, m, n, k))
+        y = gpu_gemm(x, q, s, path=path)
+        assert_gemm_close(y, oracle.gemm(x, q, s), "long-k path %d %dx%dx%d" % (path, m, n, k))
+
+
 @pytest.mark.parametrize("m,n,k", MFMA_SHAPES)
 def test_mfma_small_shapes(m, n, k):
     x, q, s = _small_case(m, n, k, seed=m * 1000 + n)
