@@ -213,6 +213,19 @@ __global__ __launch_bounds__(THREADS) void quantize_rows_kernel(
     if (threadIdx.x == 0)
         scales[row] = s16;
 
+    // Codes.  The contract is rint(binary32(w / s)); a true division per
+    // weight costs about ten VALU instructions, so the quotient is first
+    // estimated as w * rs with rs = binary32(1 / s).  That estimate is within
+    // |w / s| * 2^-23 of the exact quotient (two roundings of 2^-24 each), so
+    // for |w / s| < 256 within 2^-15.  rint of the estimate and rint of the
+    // correctly rounded quotient can only differ when a half-integer lies
+    // between them or the quotient rounds onto one; both require the
+    // estimate to be within 2^-15 + ulp/2 of a half-integer.  Estimates
+    // closer than 2^-12 to a half-integer therefore take the true division
+    // (about one weight in four thousand).  |estimate| >= 256 clamps to
+    // +-127 either way, as does an infinite one.
+    const float rs = s != 0.0f ? __fdiv_rn(1.0f, s) : 0.0f;
+    constexpr float kNearHalf = 1.0f / 4096.0f;
     uint32_t *dst = reinterpret_cast<uint32_t *>(q + row * (int64_t)k);
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
@@ -224,7 +237,13 @@ __global__ __launch_bounds__(THREADS) void quantize_rows_kernel(
         for (int e = 0; e < 4; ++e) {
             int code = 0;
             if (s != 0.0f) {
-                float r = __builtin_rintf(__fdiv_rn(v[j * 4 + e], s));
+                const float est = v[j * 4 + e] * rs;
+                float r = __builtin_rintf(est);
+                // distance of est to the nearest half-integer (exact: est - r
+                // is exact for |est| < 2^23, and so is the subtraction of 0.5)
+                const float d = __builtin_fabsf(__builtin_fabsf(est - r) - 0.5f);
+                if (__builtin_expect(d < kNearHalf && __builtin_fabsf(est) < 256.0f, 0))
+                    r = __builtin_rintf(__fdiv_rn(v[j * 4 + e], s));
                 r = r > 127.0f ? 127.0f : r;
                 r = r < -127.0f ? -127.0f : r;
                 code = (int)r;
