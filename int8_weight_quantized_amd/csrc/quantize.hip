@@ -14,11 +14,15 @@
 //   absmax bound:      wave max-reductions of the |w| bit patterns (for
 //                      non-negative binary32 values the integer order is
 //                      the numeric order), then across waves through LDS.
-//   percentile bound:  exact radix select of rank i over the |w| bit
-//                      patterns, 4 passes of 8 bits with a 256-bin LDS
-//                      histogram; the neighbour a[i+1] follows from a count
-//                      of values <= a[i] and a min-reduction of the values
-//                      above it.  Interpolation in binary64 without FMA.
+//   percentile bound:  a[i] and a[i+1] of the sorted |w|.  Near the top
+//                      (k - 1 - i <= 12, e.g. 99.9 and 99.99 for k <= 8192)
+//                      by walking down the distinct values from the maximum,
+//                      one block reduction per value; otherwise by an exact
+//                      radix select of rank i over the |w| bit patterns, 4
+//                      passes of 8 bits with a 256-bin LDS histogram, and
+//                      a[i+1] from a count of values <= a[i] and a
+//                      min-reduction of the values above it.  Interpolation
+//                      in binary64 without FMA.
 //
 // Rounding contract: the scale is binary16(binary32(t / 127)) with true
 // IEEE division; codes are clamp(rint(binary32(w / S)), -127, 127) where
@@ -31,6 +35,9 @@
 
 namespace qw {
 namespace {
+
+// descending ranks up to which the top-down walk replaces the radix select
+constexpr uint32_t kTopDownMaxRank = 12;
 
 template <int THREADS>
 struct QuantShared {
@@ -83,6 +90,70 @@ __device__ __forceinline__ void block_sum_min_u32(uint32_t a, uint32_t b, QuantS
     __syncthreads();
 }
 
+// Inclusive prefix sum across the 64 lanes of a wave (log-step shuffles).
+__device__ __forceinline__ uint32_t wave_inclusive_scan_u32(uint32_t v)
+{
+    const int lane = __lane_id();
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t t = (uint32_t)__builtin_amdgcn_ds_bpermute(((lane - off) & (kWave - 1)) << 2, (int)v);
+        v += lane >= off ? t : 0u;
+    }
+    return v;
+}
+
+// Clip percentiles near 100 need the elements of descending rank r and
+// r - 1 (r = k - 1 - i small).  Walking down the distinct values from the
+// maximum takes one block reduction per distinct value passed, far fewer
+// barriers than a radix select: a level is the largest value below the
+// previous one, and the count of its copies tells which descending ranks it
+// covers.
+__device__ __forceinline__ uint32_t abs_bits(float v);
+template <int THREADS, int VPT>
+__device__ void block_top_pair(const float (&v)[VPT * 4], const bool (&valid)[VPT], uint32_t r,
+                               QuantShared<THREADS> &sh, uint32_t &ai, uint32_t &ai1)
+{
+    uint32_t mx = 0;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t x = valid[j] ? abs_bits(v[j * 4 + e]) : 0u;
+            mx = x > mx ? x : mx;
+        }
+    uint32_t level = block_max_u32<THREADS>(mx, sh);
+    uint32_t above = 0;       // elements strictly greater than `level`
+    uint32_t prev = level;    // the level before (the next larger value)
+    ai = ai1 = level;
+    // every pass covers at least one more descending rank, so at most r + 1
+    // passes run; the bound also caps the loop
+    for (uint32_t pass = 0; pass <= r; ++pass) {
+        uint32_t cnt = 0, below = 0;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            if (!valid[j])
+                continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t x = abs_bits(v[j * 4 + e]);
+                cnt += x == level ? 1u : 0u;
+                below = (x < level && x > below) ? x : below;
+            }
+        }
+        uint32_t total, inv_next;
+        block_sum_min_u32<THREADS>(cnt, ~below, sh, total, inv_next);
+        if (above + total > r) {
+            // descending ranks above .. above + total - 1 hold `level`
+            ai = level;
+            ai1 = r - 1 >= above ? level : prev;
+            return;
+        }
+        above += total;
+        prev = level;
+        level = ~inv_next;
+    }
+}
+
 // Bit pattern of the element of 0-based ascending rank `rank` among the
 // valid |w| patterns held by the block (radix select, 8 bits per pass).
 __device__ __forceinline__ uint32_t abs_bits(float v)
@@ -114,25 +185,19 @@ __device__ uint32_t block_select_rank(const float (&v)[VPT * 4], const bool (&va
             }
         }
         __syncthreads();
-        // inclusive scan of the 256 bins (Hillis-Steele in LDS)
-        uint32_t c = 0;
+        // inclusive scan of the 256 bins: each of the first four waves scans
+        // 64 bins in registers, then adds the totals of the waves before it
+        uint32_t c = 0, incl = 0;
         if (tid < 256) {
             c = sh.hist[tid];
-            sh.scan[tid] = c;
+            incl = wave_inclusive_scan_u32(c);
+            if (__lane_id() == kWave - 1)
+                sh.scan[tid / kWave] = incl;
         }
         __syncthreads();
-#pragma unroll
-        for (int off = 1; off < 256; off <<= 1) {
-            uint32_t add = 0;
-            if (tid < 256 && tid >= off)
-                add = sh.scan[tid - off];
-            __syncthreads();
-            if (tid < 256)
-                sh.scan[tid] += add;
-            __syncthreads();
-        }
         if (tid < 256) {
-            const uint32_t incl = sh.scan[tid];
+            for (int w = 0; w < tid / kWave; ++w)
+                incl += sh.scan[w];
             const uint32_t excl = incl - c;
             if (excl <= remaining && remaining < incl) {
                 sh.digit = (uint32_t)tid;
@@ -182,24 +247,31 @@ __global__ __launch_bounds__(THREADS) void quantize_rows_kernel(
         }
         t = __builtin_bit_cast(float, block_max_u32<THREADS>(m, sh));
     } else {
-        const uint32_t ai = block_select_rank<THREADS, VPT>(v, valid, (uint32_t)rank_i, sh);
-        uint32_t le = 0, gt_min = 0xffffffffu;
+        // rank_i < k - 1 here (the host sends i >= k - 1 down the absmax path)
+        const uint32_t r = (uint32_t)((int64_t)k - 1 - rank_i);
+        uint32_t ai, ai1;
+        if (r <= kTopDownMaxRank) {
+            block_top_pair<THREADS, VPT>(v, valid, r, sh, ai, ai1);
+        } else {
+            ai = block_select_rank<THREADS, VPT>(v, valid, (uint32_t)rank_i, sh);
+            uint32_t le = 0, gt_min = 0xffffffffu;
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            if (!valid[j])
-                continue;
+            for (int j = 0; j < VPT; ++j) {
+                if (!valid[j])
+                    continue;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t x = abs_bits(v[j * 4 + e]);
-                le += x <= ai ? 1u : 0u;
-                if (x > ai && x < gt_min)
-                    gt_min = x;
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t x = abs_bits(v[j * 4 + e]);
+                    le += x <= ai ? 1u : 0u;
+                    if (x > ai && x < gt_min)
+                        gt_min = x;
+                }
             }
+            uint32_t count_le, next_up;
+            block_sum_min_u32<THREADS>(le, gt_min, sh, count_le, next_up);
+            // a[i+1] equals a[i] when more than i+1 values are <= a[i]
+            ai1 = ((uint64_t)rank_i + 1 < (uint64_t)count_le) ? ai : next_up;
         }
-        uint32_t count_le, next_up;
-        block_sum_min_u32<THREADS>(le, gt_min, sh, count_le, next_up);
-        // a[i+1] equals a[i] when more than i+1 values are <= a[i]
-        const uint32_t ai1 = ((uint64_t)rank_i + 1 < (uint64_t)count_le) ? ai : next_up;
         const double lo = (double)__builtin_bit_cast(float, ai);
         const double hi = (double)__builtin_bit_cast(float, ai1);
         const double gap = __dsub_rn(hi, lo);

@@ -245,6 +245,32 @@ def test_quantize_percentile_position_edges(pct):
     _check_quant(w, pct, "pct-edge")
 
 
+@pytest.mark.parametrize("r", [1, 2, 3, 5, 8, 9, 12])
+def test_quantize_percentile_near_top_with_duplicates(r):
+    """Clip percentiles whose bound sits r ranks below the top, on rows whose
+    largest magnitudes repeat (1 to 6 copies) and mix signs: the bound pair
+    a[i], a[i+1] must come out the same whether it is found walking down
+    from the maximum (small r) or by the radix select (larger r)."""
+    k = 1024
+    rng = np.random.default_rng(100 + r)
+    rows = []
+    for j in range(48):
+        row = rng.integers(-40, 41, size=k).astype(np.float32) * np.float32(0.0005)
+        top = rng.permutation(k)
+        level = np.float32(0.05)
+        pos = 0
+        for copies in ((j % 6) + 1, (j // 6) % 4 + 1, 2, 1, 3):
+            for _ in range(copies):
+                row[top[pos]] = level if (pos % 2) == 0 else -level
+                pos += 1
+            level = np.float32(level * np.float32(0.9))
+        rows.append(row)
+    w = np.stack(rows)
+    # pct chosen so that floor(pct / 100 * (k - 1)) = k - 1 - r, mid-way
+    pct = 100.0 * ((k - 1 - r) + 0.5) / (k - 1)
+    _check_quant(w, pct, "near-top r=%d" % r)
+
+
 def test_quantize_deterministic():
     wl, x, w, q, s = workload_data("transformer_big_ffn_outliers_m4096_k1024_n4096")
     say("quantize determinism")
