@@ -217,7 +217,7 @@ hipError_t launch_gemv(const uint16_t *x, const int8_t *q, const uint16_t *scale
     if (m <= 1)
         return launch_cfg<1, 2, 4, 28>(x, q, scales, y, m, n, k, stream);
     if (m <= 2)
-        return launch_cfg<2, 4, 2, 16>(x, q, scales, y, m, n, k, stream);
+        return launch_cfg<2, 1, 4, 32>(x, q, scales, y, m, n, k, stream);
     if (m <= 4)
         return launch_cfg<4, 2, 2, 16>(x, q, scales, y, m, n, k, stream);
     return launch_cfg<8, 2, 2, 16>(x, q, scales, y, m, n, k, stream);
