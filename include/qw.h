@@ -124,9 +124,10 @@ QW_API qw_status qw_quantize_weights(const float *w, int64_t n, int64_t k,
  *   k       reduction length, k >= 16, k % 16 == 0, k <= INT32_MAX
  *   stream  hipStream_t
  *
- * The kernel is chosen from m (and k): a bandwidth-bound VALU GEMV for
+ * The kernel is chosen from m, n and k: a bandwidth-bound VALU GEMV for
  * decode (m <= 2), a skinny MFMA kernel on register-dequantized weights for
- * a few activation rows (m <= 32), and the LDS-tiled MFMA GEMM for prefill.
+ * a few activation rows (m <= 16, or m <= 64 when n <= 16384), and the
+ * LDS-tiled MFMA GEMM (tile shape picked from the grid it fills) otherwise.
  *
  * Errors: QW_ERROR_INVALID_VALUE (null pointer with m, n > 0, negative
  * size, k <= 0, y overlapping x, q or scales), QW_ERROR_UNSUPPORTED

@@ -1,32 +1,24 @@
-// gemm_mfma.hip -- W8A16 prefill GEMM on the matrix cores (gfx950).
+// gemm_mfma.hip -- W8A16 GEMM on the matrix cores (gfx950), for prefill and
+// other activation counts beyond the skinny kernel's range.
 //
 // Prefill multiplies max_length activation rows with every weight, so the
 // matmul itself dominates ("探索ChatGLM2在算能BM1684X上INT8量化部署",
 // section 4: the W8A16 gain shrinks as max_length grows).  Each workgroup
 // computes a BN x BM tile of Y^T (BN output channels x BM activation rows)
-// with v_mfma_f32_16x16x32_f16 and fp32 accumulators; the per-channel
-// scale multiplies the accumulators in the epilogue, which rounds to fp16
-// and stores.
+// with v_mfma_f32_32x32x16_f16 and fp32 accumulators; the per-channel scale
+// multiplies the accumulators in the epilogue, which rounds to fp16 and
+// stores.  The weight is the MFMA "A" operand (rows = output channels), the
+// activations the "B" operand (columns = activation rows).  The weight tile
+// stays int8 in LDS (half the bytes of fp16 through LDS) and is cast to fp16
+// exactly in registers right after the LDS read.
 //
-// Operands.  The MFMA "A" operand is the weight (rows = output channels),
-// "B" the activations (columns = activation rows), so every lane ends up
-// with 4 consecutive output channels of one activation row and stores 8
-// contiguous bytes of Y.  The weight tile stays int8 in LDS (half the bytes
-// of fp16 through LDS) and is cast to fp16 exactly in registers right
-// after the LDS read; the cast runs on the VALU alongside the MFMAs.
-//
-// k assignment.  One k step is 64 wide.  Lane l (r = l % 16, g = l / 16)
-// reads 16 codes [16 g, 16 g + 16) of weight row r: codes 0-7 feed one
-// MFMA, codes 8-15 a second one, and the activation operand of lane l is
-// read at the same k positions, so each MFMA contracts exactly the 32 k
-// values its two operands agree on.
-//
-// Pipeline.  256 threads = 2 x 2 waves, each owning a (BN/2) x (BM/2)
-// sub-tile (acc in AGPRs).  The next k tile is loaded from global memory
-// into registers before the current tile's MFMAs are issued, then copied
-// into the other half of a double-buffered LDS; one barrier per k step.
-// LDS rows are padded by 16 bytes so that the 16 lanes reading one 16-byte
-// column slice of 16 consecutive rows hit distinct banks.
+// Tile shapes.  BN x BM in {256 x 128, 256 x 64, 128 x 128, 128 x 64}: the
+// launcher takes the largest tile whose grid still fills three quarters of
+// the workgroup slots the chip holds at once (a tile's slot count is its
+// occupancy per CU times the CU count), else the smallest.  Measured on
+// MI355X: 256 x 128 for 512 x 4096 x 27392 and 4096 x 1024 x 4096, 128 x 128
+// for 256 rows, 128 x 64 for up to ~100 rows or narrow weights (N = 4608)
+// where larger tiles leave most CUs idle.
 //
 // Grid.  Workgroups are renumbered so that each XCD (dispatch is
 // round-robin over the 8 XCDs) walks a contiguous run of tiles; the
@@ -43,205 +35,13 @@ namespace {
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 
-constexpr int kGemmThreads = 256; // 2 x 2 waves
-
-// Big-tile configuration: 256 x 128 tiles with a 2-stage ring fit two
-// workgroups per CU (64 KiB LDS, <= 256 registers per lane each), which
-// measured faster than one 256 x 256 workgroup with a 3-stage ring: the
-// second workgroup's MFMAs overlap the first one's copy/LDS phases.
-#ifndef QW_DMA_BM
-#define QW_DMA_BM 128
-#endif
-#ifndef QW_DMA_NW
-#define QW_DMA_NW 4
-#endif
-constexpr int kBK = 64;            // k per step
-constexpr int kWRow = kBK + 16;    // LDS bytes per int8 weight row (padded)
-constexpr int kXRow = 2 * kBK + 16; // LDS bytes per fp16 activation row (padded)
-
-template <int BN, int BM>
-struct TileCfg {
-    static constexpr int kWaveN = BN / 2; // output channels per wave
-    static constexpr int kWaveM = BM / 2; // activation rows per wave
-    static constexpr int kSubN = kWaveN / 16;
-    static constexpr int kSubM = kWaveM / 16;
-    static constexpr int kWChunks = BN * kBK / 16;     // 16-byte chunks of the int8 W tile
-    static constexpr int kXChunks = BM * kBK * 2 / 16; // 16-byte chunks of the fp16 X tile
-    static constexpr int kWPerThread = kWChunks / kGemmThreads;
-    static constexpr int kXPerThread = kXChunks / kGemmThreads;
-    static constexpr int kWBytes = BN * kWRow;
-    static constexpr int kXBytes = BM * kXRow;
-    static constexpr int kStageBytes = kWBytes + kXBytes;
-    static_assert(kWChunks % kGemmThreads == 0 && kXChunks % kGemmThreads == 0, "tile/thread mismatch");
-    static_assert(kSubN >= 1 && kSubM >= 1, "wave tile below one MFMA tile");
-};
+constexpr int kBK = 64; // k per step
 
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks)
 {
     const int per = nblocks / 8, rem = nblocks % 8;
     const int xcd = bid % 8, local = bid / 8;
     return xcd * per + (xcd < rem ? xcd : rem) + local;
-}
-
-template <int BN, int BM>
-__global__ __launch_bounds__(kGemmThreads) void mfma_gemm_kernel(
-    const uint16_t *__restrict__ x, const int8_t *__restrict__ q,
-    const uint16_t *__restrict__ scales, uint16_t *__restrict__ y,
-    int m, int n, int k, int tiles_m, int tiles_n)
-{
-    using C = TileCfg<BN, BM>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::kStageBytes];
-
-    const int tid = threadIdx.x;
-    const int lane = __lane_id();
-    const int wave = tid / kWave;
-    const int wave_n = wave % 2;
-    const int wave_m = wave / 2;
-
-    const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
-    const int tn = tile / tiles_m;
-    const int tm = tile % tiles_m;
-    const int n0 = tn * BN;
-    const int m0 = tm * BM;
-    const int ktiles = (k + kBK - 1) / kBK;
-
-    u32x4_t wreg[C::kWPerThread];
-    u32x4_t xreg[C::kXPerThread];
-
-    auto load_tile = [&](int kt) {
-        const int k0 = kt * kBK;
-#pragma unroll
-        for (int i = 0; i < C::kWPerThread; ++i) {
-            const int c = tid + i * kGemmThreads;
-            const int row = c / (kBK / 16);
-            const int kc = c % (kBK / 16);
-            const int gn = n0 + row;
-            const int gk = k0 + kc * 16;
-            wreg[i] = (u32x4_t){0u, 0u, 0u, 0u};
-            if (gn < n && gk < k)
-                wreg[i] = *reinterpret_cast<const u32x4_t *>(q + (int64_t)gn * k + gk);
-        }
-#pragma unroll
-        for (int i = 0; i < C::kXPerThread; ++i) {
-            const int c = tid + i * kGemmThreads;
-            const int row = c / (kBK / 8);
-            const int kc = c % (kBK / 8);
-            const int gm = m0 + row;
-            const int gk = k0 + kc * 8;
-            xreg[i] = (u32x4_t){0u, 0u, 0u, 0u};
-            if (gm < m && gk < k)
-                xreg[i] = *reinterpret_cast<const u32x4_t *>(x + (int64_t)gm * k + gk);
-        }
-    };
-
-    auto store_tile = [&](int buf) {
-        uint8_t *ws = lds + buf * C::kStageBytes;
-        uint8_t *xs = ws + C::kWBytes;
-#pragma unroll
-        for (int i = 0; i < C::kWPerThread; ++i) {
-            const int c = tid + i * kGemmThreads;
-            const int row = c / (kBK / 16);
-            const int kc = c % (kBK / 16);
-            *reinterpret_cast<u32x4_t *>(ws + row * kWRow + kc * 16) = wreg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < C::kXPerThread; ++i) {
-            const int c = tid + i * kGemmThreads;
-            const int row = c / (kBK / 8);
-            const int kc = c % (kBK / 8);
-            *reinterpret_cast<u32x4_t *>(xs + row * kXRow + kc * 16) = xreg[i];
-        }
-    };
-
-    float4v acc[C::kSubN][C::kSubM];
-#pragma unroll
-    for (int i = 0; i < C::kSubN; ++i)
-#pragma unroll
-        for (int j = 0; j < C::kSubM; ++j)
-            acc[i][j] = (float4v){0.f, 0.f, 0.f, 0.f};
-
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    const int lrow = lane % 16;
-    const int lgrp = lane / 16;
-    for (int kt = 0; kt < ktiles; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < ktiles)
-            load_tile(kt + 1);
-        const uint8_t *ws = lds + buf * C::kStageBytes;
-        const uint8_t *xs = ws + C::kWBytes;
-
-        half8_t b0[C::kSubM], b1[C::kSubM];
-#pragma unroll
-        for (int j = 0; j < C::kSubM; ++j) {
-            const uint8_t *p = xs + (wave_m * C::kWaveM + j * 16 + lrow) * kXRow + lgrp * 32;
-            b0[j] = *reinterpret_cast<const half8_t *>(p);
-            b1[j] = *reinterpret_cast<const half8_t *>(p + 16);
-        }
-#pragma unroll
-        for (int i = 0; i < C::kSubN; ++i) {
-            const u32x4_t codes = *reinterpret_cast<const u32x4_t *>(
-                ws + (wave_n * C::kWaveN + i * 16 + lrow) * kWRow + lgrp * 16);
-            const half8_t a0 = i8x8_to_half8(codes.x, codes.y);
-            const half8_t a1 = i8x8_to_half8(codes.z, codes.w);
-#pragma unroll
-            for (int j = 0; j < C::kSubM; ++j) {
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0[j], acc[i][j], 0, 0, 0);
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1[j], acc[i][j], 0, 0, 0);
-            }
-        }
-        if (kt + 1 < ktiles)
-            store_tile(buf ^ 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue: scale, round to fp16, store ----
-    const bool vec_ok = (n % 4) == 0;
-#pragma unroll
-    for (int i = 0; i < C::kSubN; ++i) {
-        const int gn = n0 + wave_n * C::kWaveN + i * 16 + lgrp * 4;
-        float s[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            s[r] = (gn + r < n) ? f16_bits_to_f32(scales[gn + r]) : 0.0f;
-#pragma unroll
-        for (int j = 0; j < C::kSubM; ++j) {
-            const int gm = m0 + wave_m * C::kWaveM + j * 16 + lrow;
-            if (gm >= m)
-                continue;
-            uint16_t out[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                out[r] = f32_to_f16_bits(acc[i][j][r] * s[r]);
-            uint16_t *dst = y + (int64_t)gm * n + gn;
-            if (vec_ok && gn + 3 < n) {
-                u32x2_t pk = {(uint32_t)out[0] | ((uint32_t)out[1] << 16),
-                              (uint32_t)out[2] | ((uint32_t)out[3] << 16)};
-                *reinterpret_cast<u32x2_t *>(dst) = pk;
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (gn + r < n)
-                        dst[r] = out[r];
-            }
-        }
-    }
-}
-
-template <int BN, int BM>
-hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
-                      int64_t m, int64_t n, int64_t k, hipStream_t stream)
-{
-    const int64_t tiles_m = (m + BM - 1) / BM;
-    const int64_t tiles_n = (n + BN - 1) / BN;
-    const int64_t blocks = tiles_m * tiles_n;
-    if (blocks > 0x7fffffff)
-        return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((mfma_gemm_kernel<BN, BM>), dim3((unsigned)blocks), dim3(kGemmThreads), 0,
-                       stream, x, q, scales, y, (int)m, (int)n, (int)k, (int)tiles_m, (int)tiles_n);
-    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -281,28 +81,29 @@ hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales
 // outputs are never stored); k chunks beyond k are zero-filled with
 // ordinary LDS stores.
 // ---------------------------------------------------------------------------
-constexpr int kDmaBN = 256;                // output channels per workgroup
-constexpr int kDmaWBytes = kDmaBN * kBK;   // 16 KiB int8 weight tile per stage
 
-// NW waves per workgroup side by side along n; each wave owns kDmaBN / NW
+// NW waves per workgroup side by side along n; each wave owns BN / NW
 // output channels x all BM activation rows.
-template <int NW, int BM>
+template <int NW, int BN, int BM>
 struct DmaCfg {
+    static constexpr int kBN = BN;                            // output channels per workgroup
+    static constexpr int kWBytes = BN * kBK;                  // int8 weight tile per stage
     static constexpr int kThreads = NW * kWave;
     static constexpr int kXBytes = BM * kBK * 2;             // fp16 activation tile per stage
-    static constexpr int kStage = kDmaWBytes + kXBytes;
-    static constexpr int kWInstr = kDmaWBytes / 1024 / NW;   // copies per wave per stage
+    static constexpr int kStage = kWBytes + kXBytes;
+    static constexpr int kWInstr = kWBytes / 1024 / NW;      // copies per wave per stage
     static constexpr int kXInstr = kXBytes / 1024 / NW;
     static constexpr int kInstr = kWInstr + kXInstr;
-    static constexpr int kWaveN = kDmaBN / NW;               // output channels per wave
+    static constexpr int kWaveN = BN / NW;                   // output channels per wave
     static constexpr int kSI = kWaveN / 32;                   // 32 x 32 MFMA tiles along n
     static constexpr int kSJ = BM / 32;                       // 32 x 32 MFMA tiles along m
-    // epilogue: the fp16 output tile, [BM][kDmaBN] with rows padded by 16
+    // epilogue: the fp16 output tile, [BM][BN] with rows padded by 16
     // bytes; rows [0, BM/2) go to stage 0's array, [BM/2, BM) to stage 1's
-    static constexpr int kYRow = kDmaBN * 2 + 16;
+    static constexpr int kYRow = BN * 2 + 16;
     static constexpr int kYHalf = (BM / 2) * kYRow;
     static constexpr int kStageAlloc = kStage > kYHalf ? kStage : kYHalf;
-    static_assert(kWInstr * 64 * 16 * NW == kDmaWBytes && kXInstr * 64 * 16 * NW == kXBytes, "copy split");
+    static_assert(kWInstr * 64 * 16 * NW == kWBytes && kXInstr * 64 * 16 * NW == kXBytes, "copy split");
+    static_assert(kXInstr % 2 == 0, "activation copies alternate between the two 8-row swizzle phases");
     static_assert(kSI >= 1 && kWaveN % 32 == 0 && BM % 64 == 0, "tile config");
 };
 
@@ -343,18 +144,18 @@ __device__ __forceinline__ int xslot(int row)
 template <int I>
 using stage_t = std::integral_constant<int, I>;
 
-template <int NW, int BM>
+template <int NW, int BN, int BM>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm_dma_kernel(
     const uint16_t *__restrict__ x, const int8_t *__restrict__ q,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y,
     int m, int n, int k, int tiles_m, int tiles_n)
 {
-    using C = DmaCfg<NW, BM>;
+    using C = DmaCfg<NW, BN, BM>;
     constexpr int kSJ = C::kSJ;
     __shared__ __attribute__((aligned(1024))) uint8_t ring0[C::kStageAlloc];
     __shared__ __attribute__((aligned(1024))) uint8_t ring1[C::kStageAlloc];
-    __shared__ __attribute__((aligned(16))) float scale_lds[kDmaBN];
+    __shared__ __attribute__((aligned(16))) float scale_lds[BN];
     auto ring = [&](auto s) -> uint8_t * {
         if constexpr (decltype(s)::value == 0)
             return ring0;
@@ -369,7 +170,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
     const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
     const int tn = tile / tiles_m;
     const int tm = tile % tiles_m;
-    const int n0 = tn * kDmaBN;
+    const int n0 = tn * BN;
     const int m0 = tm * BM;
     const int ktiles = (k + kBK - 1) / kBK;
     // the last tile issues fewer copies when k is ragged; waits then drain
@@ -401,7 +202,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
         }
 #pragma unroll
         for (int i = 0; i < C::kXInstr; ++i) {
-            uint8_t *dst = st + kDmaWBytes + (wave * C::kXInstr + i) * 1024;
+            uint8_t *dst = st + C::kWBytes + (wave * C::kXInstr + i) * 1024;
             const int row = (wave * C::kXInstr + i) * 8 + lane / 8;
             const int gm = min(m0 + row, m - 1);
             const int gk = k0 + ((i & 1) ? xchunk_odd : xchunk_even) * 8;
@@ -430,7 +231,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
     int x_off[4];
 #pragma unroll
     for (int sidx = 0; sidx < 4; ++sidx)
-        x_off[sidx] = kDmaWBytes + xrow * 2 * kBK + 16 * ((4 * lgrp + sidx) ^ xslot(xrow));
+        x_off[sidx] = C::kWBytes + xrow * 2 * kBK + 16 * ((4 * lgrp + sidx) ^ xslot(xrow));
 
     float16v acc[C::kSI][kSJ];
 #pragma unroll
@@ -472,7 +273,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
     // this tile's per-channel scales, staged once in LDS for the epilogue;
     // the first barrier of the main loop publishes the LDS writes
 #pragma unroll
-    for (int c = tid; c < kDmaBN; c += C::kThreads)
+    for (int c = tid; c < BN; c += C::kThreads)
         scale_lds[c] = n0 + c < n ? f16_bits_to_f32(scales[n0 + c]) : 0.0f;
 
     // Step t (stage t % 2) waits for its own copies of tile t, the barrier
@@ -513,7 +314,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
     // each group of 4 registers is 4 consecutive output channels of one
     // activation row.  They are scaled, rounded and written as 8 bytes into
     // the tile's [activation row][channel] image in LDS (row stride
-    // 2 * kDmaBN + 16 bytes: the 32 rows one instruction touches fall on
+    // 2 * BN + 16 bytes: the 32 rows one instruction touches fall on
     // distinct bank pairs); then the workgroup copies the image out in
     // 16-byte pieces, so every wave writes whole 512-byte row segments of Y
     // instead of scattered 8-byte pieces of 32 rows.
@@ -538,8 +339,8 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
         }
     }
     ring_barrier();
-    constexpr int kRowChunks = kDmaBN / 8; // 16-byte pieces per output row
-    const bool vec_ok = (n % 8) == 0 && n0 + kDmaBN <= n;
+    constexpr int kRowChunks = BN / 8; // 16-byte pieces per output row
+    const bool vec_ok = (n % 8) == 0 && n0 + BN <= n;
     const int rows = min(BM, m - m0);
     for (int c = tid; c < rows * kRowChunks; c += C::kThreads) {
         const int row = c / kRowChunks;
@@ -561,18 +362,45 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
     }
 }
 
-template <int NW, int BM>
+template <int NW, int BN, int BM>
 hipError_t launch_dma(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
                       int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
     const int64_t tiles_m = (m + BM - 1) / BM;
-    const int64_t tiles_n = (n + kDmaBN - 1) / kDmaBN;
+    const int64_t tiles_n = (n + BN - 1) / BN;
     const int64_t blocks = tiles_m * tiles_n;
     if (blocks > 0x7fffffff)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((mfma_gemm_dma_kernel<NW, BM>), dim3((unsigned)blocks), dim3(NW * kWave),
+    hipLaunchKernelGGL((mfma_gemm_dma_kernel<NW, BN, BM>), dim3((unsigned)blocks), dim3(NW * kWave),
                        0, stream, x, q, scales, y, (int)m, (int)n, (int)k, (int)tiles_m, (int)tiles_n);
     return hipGetLastError();
+}
+
+// Workgroups of this tile shape one CU holds at once (registers and LDS),
+// queried once per device.
+template <int BN, int BM>
+int64_t slots_per_cu()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 1;
+    if (cached[dev] == 0) {
+        int blocks = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, mfma_gemm_dma_kernel<4, BN, BM>, 4 * kWave, 0) !=
+                hipSuccess || blocks < 1)
+            blocks = 1;
+        cached[dev] = blocks;
+    }
+    return cached[dev];
+}
+
+template <int BN, int BM>
+bool fills(int64_t m, int64_t n)
+{
+    const int64_t tiles = ((n + BN - 1) / BN) * ((m + BM - 1) / BM);
+    const int64_t slots = slots_per_cu<BN, BM>() * (int64_t)device_cu_count();
+    return 4 * tiles >= 3 * slots;
 }
 
 } // namespace
@@ -580,11 +408,15 @@ hipError_t launch_dma(const uint16_t *x, const int8_t *q, const uint16_t *scales
 hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
                             int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
-    if (m <= 32)
-        return launch_cfg<128, 32>(x, q, scales, y, m, n, k, stream);
-    if (m <= 64)
-        return launch_cfg<128, 64>(x, q, scales, y, m, n, k, stream);
-    return launch_dma<QW_DMA_NW, QW_DMA_BM>(x, q, scales, y, m, n, k, stream);
+    // largest tile first (more reuse per byte staged); 256 x 64 before
+    // 128 x 128 (same area, half the activation bytes per tile)
+    if (fills<256, 128>(m, n))
+        return launch_dma<4, 256, 128>(x, q, scales, y, m, n, k, stream);
+    if (fills<256, 64>(m, n))
+        return launch_dma<4, 256, 64>(x, q, scales, y, m, n, k, stream);
+    if (fills<128, 128>(m, n))
+        return launch_dma<4, 128, 128>(x, q, scales, y, m, n, k, stream);
+    return launch_dma<4, 128, 64>(x, q, scales, y, m, n, k, stream);
 }
 
 } // namespace qw

@@ -40,10 +40,14 @@ int device_cu_count()
 // MFMA GEMM, whose weight tiles are reused across activation rows.
 int auto_path(int64_t m, int64_t n, int64_t k)
 {
-    (void)n;
     if (m <= 2 && gemv_supported(m, k))
         return QW_PATH_GEMV;
-    if (m <= 32)
+    // The skinny kernel streams the weights once per 16 activation rows; it
+    // beats the tiled MFMA kernel up to 16 rows, and up to 64 rows when the
+    // weight is narrow enough (n <= 16384) that MFMA tiles leave most CUs
+    // idle (crossover sweep over m at (k, n) = (4096, 27392), (4096, 4608),
+    // (1024, 4096)).
+    if (m <= 16 || (m <= 64 && n <= 16384))
         return QW_PATH_SKINNY;
     return QW_PATH_MFMA;
 }

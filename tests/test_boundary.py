@@ -127,6 +127,13 @@ def test_auto_path_choice():
     assert qw.auto_path(8, 4608, 4096) == "skinny"
     assert qw.auto_path(512, 27392, 4096) == "mfma"
     assert qw.auto_path(4096, 4096, 1024) == "mfma"
+    # crossover: skinny to 16 rows, to 64 rows for narrow weights
+    assert qw.auto_path(16, 27392, 4096) == "skinny"
+    assert qw.auto_path(24, 27392, 4096) == "mfma"
+    assert qw.auto_path(64, 4608, 4096) == "skinny"
+    assert qw.auto_path(65, 4608, 4096) == "mfma"
+    # k too long for the GEMV's LDS staging: skinny even at m = 1
+    assert qw.auto_path(1, 64, 65536) == "skinny"
     with pytest.raises(ValueError):
         qw.auto_path(1, 4, 24)
 
