@@ -168,13 +168,17 @@ def time_full_steps(runner, steps, warmup):
 
 
 def time_gemm_only(runner, launches, warmup):
-    """Cold GEMM launches rotating over the operand sets; event pairs per launch."""
+    """Cold GEMM launches rotating over the operand sets; event pairs per launch.
+    A GPU-side sleep is queued first so that every launch is enqueued before
+    the GPU reaches it: the event pairs then see device time only, not gaps
+    left by host-side launch latency."""
     torch = runner.torch
     for it in range(warmup):
         runner.gemm(it % runner.sets)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(launches)]
     torch.cuda.synchronize()
+    torch.cuda._sleep(40_000_000)
     for it in range(launches):
         ev[it][0].record()
         runner.gemm((warmup + it) % runner.sets)
@@ -207,7 +211,7 @@ def cpu_baseline(wl, target_s=10.0, max_s=30.0):
                       % (steps, wl.name, el, per_step)}
 
 
-def sweep_paths(ms=(1, 2, 4, 8, 16, 32, 64, 128, 256, 512),
+def sweep_paths(ms=(1, 2, 3, 4, 8, 16, 24, 32, 48, 64, 96, 128, 256, 512),
                 shapes=((4096, 27392), (4096, 4608), (1024, 4096))):
     """Cold timing of each GEMM kernel across m (random codes; timing only)."""
     import torch
@@ -298,6 +302,7 @@ def main():
         sweep_paths()
         return
 
+    import int8_weight_quantized_amd as qw
     wl = synthetic.BY_NAME[args.workload]
     per_set = quant_bytes(wl.n, wl.k) + gemm_bytes(wl.m, wl.n, wl.k)
     sets = rotation_count(per_set)
@@ -334,6 +339,7 @@ def main():
             fl = gemm_flops(other.m, other.n, other.k)
             kname = gemm_kernel_name(other.m, other.n, other.k)
             ent = {"workload": other.name, "kernel": kname, "cold_sets": r.sets,
+                   "mfma_tile": list(qw.mfma_tile(other.m, other.n, other.k)) if kname == "mfma" else None,
                    "avg_us": avg_ms * 1e3, "median_us": med_ms * 1e3,
                    "TBps": gbytes / (avg_ms * 1e-3) / 1e12,
                    "hbm_frac": gbytes / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,

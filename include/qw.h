@@ -166,6 +166,19 @@ QW_API qw_status qw_w8a16_gemm_path(const uint16_t *x, const int8_t *q,
  */
 QW_API int qw_w8a16_gemm_auto_path(int64_t m, int64_t n, int64_t k);
 
+/*
+ * qw_w8a16_gemm_mfma_tile -- the output tile QW_PATH_MFMA uses for this
+ * shape on the current HIP device, encoded BN * 1000 + BM (BN output
+ * channels x BM activation rows per workgroup: 256128, 256064, 128128 or
+ * 128064), for benchmarks, logs and tests.  The choice depends on the
+ * device's CU count and the kernels' occupancy (queried once per device):
+ * the largest tile whose grid fills three quarters of the workgroups the
+ * chip holds at once, else 128 x 64.  Returns -1 for shapes the GEMM
+ * rejects (m, n <= 0, k <= 0, k % 16 != 0, a size beyond INT32_MAX) or
+ * when no HIP device is current.
+ */
+QW_API int qw_w8a16_gemm_mfma_tile(int64_t m, int64_t n, int64_t k);
+
 /* A static, human-readable name for a status code (never NULL). */
 QW_API const char *qw_status_string(qw_status status);
 

@@ -66,6 +66,8 @@ def _load():
     lib.qw_status_string.restype = ctypes.c_char_p
     lib.qw_w8a16_gemm_auto_path.argtypes = [i64, i64, i64]
     lib.qw_w8a16_gemm_auto_path.restype = ctypes.c_int
+    lib.qw_w8a16_gemm_mfma_tile.argtypes = [i64, i64, i64]
+    lib.qw_w8a16_gemm_mfma_tile.restype = ctypes.c_int
     lib.qw_version.argtypes = []
     lib.qw_version.restype = ctypes.c_int
     _lib_handle = lib
@@ -94,6 +96,15 @@ def auto_path(m: int, n: int, k: int) -> str:
     if p < 0:
         raise ValueError("unsupported GEMM shape m=%d n=%d k=%d" % (m, n, k))
     return PATH_NAMES[p]
+
+
+def mfma_tile(m: int, n: int, k: int):
+    """(BN, BM) output tile the MFMA kernel uses for this shape on the current
+    device (needs a GPU)."""
+    t = int(library().qw_w8a16_gemm_mfma_tile(m, n, k))
+    if t < 0:
+        raise ValueError("no MFMA tile for m=%d n=%d k=%d (bad shape or no device)" % (m, n, k))
+    return t // 1000, t % 1000
 
 
 # ---------------------------------------------------------------------------

@@ -405,18 +405,32 @@ bool fills(int64_t m, int64_t n)
 
 } // namespace
 
-hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
-                            int64_t m, int64_t n, int64_t k, hipStream_t stream)
+int mfma_tile_choice(int64_t m, int64_t n)
 {
     // largest tile first (more reuse per byte staged); 256 x 64 before
     // 128 x 128 (same area, half the activation bytes per tile)
     if (fills<256, 128>(m, n))
-        return launch_dma<4, 256, 128>(x, q, scales, y, m, n, k, stream);
+        return 256128;
     if (fills<256, 64>(m, n))
-        return launch_dma<4, 256, 64>(x, q, scales, y, m, n, k, stream);
+        return 256064;
     if (fills<128, 128>(m, n))
+        return 128128;
+    return 128064;
+}
+
+hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
+                            int64_t m, int64_t n, int64_t k, hipStream_t stream)
+{
+    switch (mfma_tile_choice(m, n)) {
+    case 256128:
+        return launch_dma<4, 256, 128>(x, q, scales, y, m, n, k, stream);
+    case 256064:
+        return launch_dma<4, 256, 64>(x, q, scales, y, m, n, k, stream);
+    case 128128:
         return launch_dma<4, 128, 128>(x, q, scales, y, m, n, k, stream);
-    return launch_dma<4, 128, 64>(x, q, scales, y, m, n, k, stream);
+    default:
+        return launch_dma<4, 128, 64>(x, q, scales, y, m, n, k, stream);
+    }
 }
 
 } // namespace qw

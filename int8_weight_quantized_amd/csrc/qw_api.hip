@@ -182,6 +182,16 @@ QW_API int qw_w8a16_gemm_auto_path(int64_t m, int64_t n, int64_t k)
     return qw::auto_path(m, n, k);
 }
 
+QW_API int qw_w8a16_gemm_mfma_tile(int64_t m, int64_t n, int64_t k)
+{
+    if (m <= 0 || n <= 0 || k <= 0 || k % 16 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim)
+        return -1;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return -1;
+    return qw::mfma_tile_choice(m, n);
+}
+
 QW_API const char *qw_status_string(qw_status status)
 {
     switch (status) {

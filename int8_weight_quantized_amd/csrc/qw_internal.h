@@ -35,6 +35,10 @@ hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *
                             uint16_t *y, int64_t m, int64_t n, int64_t k,
                             hipStream_t stream);
 
+// Output tile of the MFMA GEMM for this shape on the current device,
+// encoded BN * 1000 + BM.
+int mfma_tile_choice(int64_t m, int64_t n);
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
 

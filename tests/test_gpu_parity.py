@@ -76,6 +76,29 @@ def test_gemm_workload(name):
         assert np.all(np.isfinite(y.astype(np.float32))), "non-finite output outside the sample"
 
 
+# Shapes that between them land on every MFMA tile shape (the choice depends
+# on the CU count and the kernels' occupancy, so coverage is checked, not
+# which shape gets which tile).
+TILE_SHAPES = [(512, 27392, 256), (2048, 4608, 128), (256, 27392, 128), (384, 13824, 128),
+               (96, 27392, 256), (1024, 9216, 128), (4096, 4096, 64), (320, 6144, 144)]
+
+
+def test_mfma_every_tile_shape():
+    import int8_weight_quantized_amd as qw
+    seen = set()
+    for m, n, k in TILE_SHAPES:
+        tile = qw.mfma_tile(m, n, k)
+        seen.add(tile)
+        x, q, s = _small_case(m, n, k, seed=m + n)
+        say("gemm mfma tile=%s m=%d n=%d k=%d" % (tile, m, n, k))
+        y = gpu_gemm(x, q, s, path=MFMA)
+        mi, ni = _sample_indices(m, n, np.random.default_rng(m * 7 + n))
+        ref = oracle.gemm_sampled(x, q, s, mi, ni)
+        assert_gemm_close(y[mi, ni], ref, "mfma tile %s %dx%dx%d (sampled)" % (tile, m, n, k))
+        assert np.all(np.isfinite(y.astype(np.float32))), "non-finite output outside the sample"
+    assert seen == {(256, 128), (256, 64), (128, 128), (128, 64)}, "tiles exercised: %s" % sorted(seen)
+
+
 # Shapes spanning several tiles with ragged tails in m, n and k.
 SMALL_SHAPES = [
     (1, 1000, 272), (1, 129, 1040), (2, 300, 2064), (3, 257, 528), (4, 64, 16),
