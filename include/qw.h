@@ -101,6 +101,23 @@ QW_API qw_status qw_quantize_weights(const float *w, int64_t n, int64_t k,
                                      uint16_t *scales, void *stream);
 
 /*
+ * qw_quantize_weights_f16 -- qw_quantize_weights for fp16 weights (the dtype
+ * the ChatGLM2/BM1684X page's model ships in, section 1), and the per-token
+ * quantizer of fp16 activations for the W8A8 product below.
+ *
+ * Every weight is first widened exactly to binary32; everything else is
+ * qw_quantize_weights's contract word for word, so the codes and scales
+ * equal those of qw_quantize_weights on the widened matrix.
+ *
+ *   w   fp16 bits [n][k], read only
+ *   (other arguments and errors as qw_quantize_weights; the overlap checks
+ *   use 2 bytes per input weight)
+ */
+QW_API qw_status qw_quantize_weights_f16(const uint16_t *w, int64_t n, int64_t k,
+                                         double clip_percentile, int8_t *q,
+                                         uint16_t *scales, void *stream);
+
+/*
  * qw_w8a16_gemm -- Y = X * dequant(Q)^T with per-channel fp16 scales.
  *
  * Source: ChatGLM2/BM1684X page, section 4 (后端性能提升原理): load, cast

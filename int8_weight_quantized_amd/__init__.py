@@ -58,6 +58,8 @@ def _load():
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.qw_quantize_weights.argtypes = [vp, i64, i64, ctypes.c_double, vp, vp, vp]
     lib.qw_quantize_weights.restype = ctypes.c_int
+    lib.qw_quantize_weights_f16.argtypes = [vp, i64, i64, ctypes.c_double, vp, vp, vp]
+    lib.qw_quantize_weights_f16.restype = ctypes.c_int
     lib.qw_w8a16_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     lib.qw_w8a16_gemm.restype = ctypes.c_int
     lib.qw_w8a16_gemm_path.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
@@ -116,6 +118,11 @@ def quantize_weights_raw(w_ptr: int, n: int, k: int, clip_percentile: float,
     return int(library().qw_quantize_weights(w_ptr, n, k, float(clip_percentile), q_ptr, s_ptr, stream))
 
 
+def quantize_weights_f16_raw(w_ptr: int, n: int, k: int, clip_percentile: float,
+                             q_ptr: int, s_ptr: int, stream: int = 0) -> int:
+    return int(library().qw_quantize_weights_f16(w_ptr, n, k, float(clip_percentile), q_ptr, s_ptr, stream))
+
+
 def w8a16_gemm_raw(x_ptr: int, q_ptr: int, s_ptr: int, y_ptr: int, m: int, n: int, k: int,
                    stream: int = 0, path: int = 0) -> int:
     return int(library().qw_w8a16_gemm_path(x_ptr, q_ptr, s_ptr, y_ptr, m, n, k, int(path), stream))
@@ -150,14 +157,16 @@ def _check(t, name, dtype, ndim):
 
 
 def quantize_weights(w, clip_percentile: float = 100.0, out=None):
-    """Per-output-row symmetric int8 quantization of an fp32 Linear weight.
+    """Per-output-row symmetric int8 quantization of a Linear weight.
 
-    w: cuda float32 [N, K] (K % 16 == 0, K <= 65536).  clip_percentile in
-    (0, 100]; 100 uses the row absmax.  Returns (q int8 [N, K], scales
-    float16 [N]); ``out=(q, scales)`` writes into preallocated tensors.
+    w: cuda float32 or float16 [N, K] (K % 16 == 0, K <= 65536; fp16 is
+    widened exactly to fp32 first).  clip_percentile in (0, 100]; 100 uses
+    the row absmax.  Returns (q int8 [N, K], scales float16 [N]);
+    ``out=(q, scales)`` writes into preallocated tensors.
     """
     torch = _torch()
-    _check(w, "w", torch.float32, 2)
+    f16 = isinstance(w, torch.Tensor) and w.dtype == torch.float16
+    _check(w, "w", torch.float16 if f16 else torch.float32, 2)
     n, k = w.shape
     if out is None:
         q = torch.empty((n, k), dtype=torch.int8, device=w.device)
@@ -168,10 +177,10 @@ def quantize_weights(w, clip_percentile: float = 100.0, out=None):
         _check(s, "scales", torch.float16, 1)
         if tuple(q.shape) != (n, k) or tuple(s.shape) != (n,):
             raise ValueError("output shapes must be [N, K] and [N]")
-    st = quantize_weights_raw(w.data_ptr(), n, k, clip_percentile, q.data_ptr(), s.data_ptr(),
-                              _stream_of(w))
+    raw = quantize_weights_f16_raw if f16 else quantize_weights_raw
+    st = raw(w.data_ptr(), n, k, clip_percentile, q.data_ptr(), s.data_ptr(), _stream_of(w))
     if st != QW_SUCCESS:
-        raise QwError(st, "qw_quantize_weights")
+        raise QwError(st, "qw_quantize_weights_f16" if f16 else "qw_quantize_weights")
     return q, s
 
 

@@ -6,7 +6,9 @@
 // "量化：裁剪+对称"), one F16 scale per output channel of a Linear weight
 // ("探索ChatGLM2在算能BM1684X上INT8量化部署", sections 2 and 3).
 //
-// One workgroup (one wave for rows up to 1024 values) owns one row.  The
+// Input weights are fp32, or fp16 widened exactly to binary32 on load (the
+// same arithmetic then follows).  One workgroup (one wave for rows up to
+// 1024 values) owns one row.  The
 // row is read from HBM exactly once with 16-byte loads and stays in
 // registers (VPT float4 per thread) while the bound is found, so the kernel
 // moves 4 bytes in and 1 byte out per weight plus 2 bytes of scale per row
@@ -226,15 +228,29 @@ __device__ uint32_t block_select_rank(const float (&v)[VPT * 4], const bool (&va
     return prefix;
 }
 
-template <int THREADS, int VPT, bool PERCENTILE>
+// Four consecutive weights of a row as binary32: 16 bytes of fp32, or 8
+// bytes of fp16 widened exactly.
+template <bool F16>
+__device__ __forceinline__ float4_t load4(const void *row, int idx)
+{
+    if constexpr (F16) {
+        const u32x2_t b = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(row) + idx);
+        return (float4_t){f16_bits_to_f32((uint16_t)(b.x & 0xffffu)), f16_bits_to_f32((uint16_t)(b.x >> 16)),
+                          f16_bits_to_f32((uint16_t)(b.y & 0xffffu)), f16_bits_to_f32((uint16_t)(b.y >> 16))};
+    } else {
+        return __builtin_nontemporal_load(reinterpret_cast<const float4_t *>(row) + idx);
+    }
+}
+
+template <int THREADS, int VPT, bool PERCENTILE, bool F16>
 __global__ __launch_bounds__(THREADS) void quantize_rows_kernel(
-    const float *__restrict__ w, int k, int64_t rank_i, double frac_f,
+    const void *__restrict__ w, int k, int64_t rank_i, double frac_f,
     int8_t *__restrict__ q, uint16_t *__restrict__ scales)
 {
     __shared__ QuantShared<THREADS> sh;
     const int64_t row = blockIdx.x;
     const int nvec = k >> 2;
-    const float4_t *src = reinterpret_cast<const float4_t *>(w + row * (int64_t)k);
+    const void *src = static_cast<const uint8_t *>(w) + row * (int64_t)k * (F16 ? 2 : 4);
 
     float v[VPT * 4];
     bool valid[VPT];
@@ -244,7 +260,7 @@ __global__ __launch_bounds__(THREADS) void quantize_rows_kernel(
         valid[j] = idx < nvec;
         float4_t f = {0.f, 0.f, 0.f, 0.f};
         if (valid[j])
-            f = __builtin_nontemporal_load(src + idx);
+            f = load4<F16>(src, idx);
         v[j * 4 + 0] = f.x;
         v[j * 4 + 1] = f.y;
         v[j * 4 + 2] = f.z;
@@ -339,24 +355,33 @@ __global__ __launch_bounds__(THREADS) void quantize_rows_kernel(
     }
 }
 
-template <int THREADS, int VPT>
-hipError_t launch_cfg(const float *w, int64_t n, int64_t k, int mode, int64_t rank_i, double frac_f,
-                      int8_t *q, uint16_t *scales, hipStream_t stream)
+template <int THREADS, int VPT, bool F16>
+hipError_t launch_typed(const void *w, int64_t n, int64_t k, int mode, int64_t rank_i, double frac_f,
+                        int8_t *q, uint16_t *scales, hipStream_t stream)
 {
     const dim3 grid((unsigned)n), block(THREADS);
     if (mode == 0)
-        hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, false>), grid, block, 0, stream,
+        hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, false, F16>), grid, block, 0, stream,
                            w, (int)k, rank_i, frac_f, q, scales);
     else
-        hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, true>), grid, block, 0, stream,
+        hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, true, F16>), grid, block, 0, stream,
                            w, (int)k, rank_i, frac_f, q, scales);
     return hipGetLastError();
 }
 
+template <int THREADS, int VPT>
+hipError_t launch_cfg(const void *w, bool f16, int64_t n, int64_t k, int mode, int64_t rank_i,
+                      double frac_f, int8_t *q, uint16_t *scales, hipStream_t stream)
+{
+    return f16 ? launch_typed<THREADS, VPT, true>(w, n, k, mode, rank_i, frac_f, q, scales, stream)
+               : launch_typed<THREADS, VPT, false>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
+}
+
 } // namespace
 
-hipError_t launch_quantize(const float *w, int64_t n, int64_t k, int mode, int64_t rank_i,
-                           double frac_f, int8_t *q, uint16_t *scales, hipStream_t stream)
+hipError_t launch_quantize(const void *w, bool w_is_f16, int64_t n, int64_t k, int mode,
+                           int64_t rank_i, double frac_f, int8_t *q, uint16_t *scales,
+                           hipStream_t stream)
 {
     // float4 slots per row; a workgroup of THREADS holds THREADS * VPT of them.
     // Rows up to 1024 values get one wave each: every reduction is then a
@@ -364,24 +389,24 @@ hipError_t launch_quantize(const float *w, int64_t n, int64_t k, int mode, int64
     // percentile; no gain at 2048).
     const int64_t nvec = k / 4;
     if (nvec <= kWave * 1)
-        return launch_cfg<64, 1>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
+        return launch_cfg<64, 1>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
     if (nvec <= kWave * 2)
-        return launch_cfg<64, 2>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
+        return launch_cfg<64, 2>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
     if (nvec <= kWave * 4)
-        return launch_cfg<64, 4>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
+        return launch_cfg<64, 4>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
     if (nvec <= 256 * 1)
-        return launch_cfg<256, 1>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
+        return launch_cfg<256, 1>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
     if (nvec <= 256 * 2)
-        return launch_cfg<256, 2>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
+        return launch_cfg<256, 2>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
     if (nvec <= 256 * 4)
-        return launch_cfg<256, 4>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
+        return launch_cfg<256, 4>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
     if (nvec <= 256 * 8)
-        return launch_cfg<256, 8>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
+        return launch_cfg<256, 8>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
     if (nvec <= 256 * 16)
-        return launch_cfg<256, 16>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
+        return launch_cfg<256, 16>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
     if (nvec <= 1024 * 8)
-        return launch_cfg<1024, 8>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
-    return launch_cfg<1024, 16>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
+        return launch_cfg<1024, 8>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
+    return launch_cfg<1024, 16>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
 }
 
 } // namespace qw

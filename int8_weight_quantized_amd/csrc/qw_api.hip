@@ -99,12 +99,10 @@ qw_status check_gemm_args(const uint16_t *x, const int8_t *q, const uint16_t *sc
     return QW_SUCCESS;
 }
 
-} // namespace
-
-extern "C" {
-
-QW_API qw_status qw_quantize_weights(const float *w, int64_t n, int64_t k, double clip_percentile,
-                                     int8_t *q, uint16_t *scales, void *stream)
+// Shared body of the fp32 and fp16 quantizer entry points (wbytes = bytes
+// per input weight).
+qw_status quantize_common(const void *w, int wbytes, int64_t n, int64_t k, double clip_percentile,
+                          int8_t *q, uint16_t *scales, void *stream)
 {
     if (n < 0 || k <= 0)
         return QW_ERROR_INVALID_VALUE;
@@ -119,7 +117,8 @@ QW_API qw_status qw_quantize_weights(const float *w, int64_t n, int64_t k, doubl
     if (misaligned(w) || misaligned(q) || misaligned(scales))
         return QW_ERROR_MISALIGNED;
     const uint64_t elems = (uint64_t)n * (uint64_t)k;
-    if (overlaps(q, elems, w, elems * 4u) || overlaps(scales, (uint64_t)n * 2u, w, elems * 4u) ||
+    if (overlaps(q, elems, w, elems * (uint64_t)wbytes) ||
+        overlaps(scales, (uint64_t)n * 2u, w, elems * (uint64_t)wbytes) ||
         overlaps(scales, (uint64_t)n * 2u, q, elems))
         return QW_ERROR_INVALID_VALUE;
 
@@ -138,8 +137,24 @@ QW_API qw_status qw_quantize_weights(const float *w, int64_t n, int64_t k, doubl
             frac_f = pos - i_floor;
         }
     }
-    return launch_status(qw::launch_quantize(w, n, k, mode, rank_i, frac_f, q, scales,
+    return launch_status(qw::launch_quantize(w, wbytes == 2, n, k, mode, rank_i, frac_f, q, scales,
                                              static_cast<hipStream_t>(stream)));
+}
+
+} // namespace
+
+extern "C" {
+
+QW_API qw_status qw_quantize_weights(const float *w, int64_t n, int64_t k, double clip_percentile,
+                                     int8_t *q, uint16_t *scales, void *stream)
+{
+    return quantize_common(w, 4, n, k, clip_percentile, q, scales, stream);
+}
+
+QW_API qw_status qw_quantize_weights_f16(const uint16_t *w, int64_t n, int64_t k, double clip_percentile,
+                                         int8_t *q, uint16_t *scales, void *stream)
+{
+    return quantize_common(w, 2, n, k, clip_percentile, q, scales, stream);
 }
 
 QW_API qw_status qw_w8a16_gemm_path(const uint16_t *x, const int8_t *q, const uint16_t *scales,

@@ -35,15 +35,17 @@ def host(t) -> np.ndarray:
 
 
 def gpu_quantize(w: np.ndarray, pct: float):
-    """Quantize on the GPU through the C ABI; returns (q int8, scale bits uint16)."""
+    """Quantize fp32 or fp16 weights on the GPU through the C ABI; returns
+    (q int8, scale bits uint16)."""
     import int8_weight_quantized_amd as qw
     torch = torch_mod()
     n, k = w.shape
     wd = dev(w)
     qd = torch.full((n, k), 99, dtype=torch.int8, device="cuda:0")
     sd = torch.full((n,), 0x5555, dtype=torch.int16, device="cuda:0")
-    st = qw.quantize_weights_raw(wd.data_ptr(), n, k, pct, qd.data_ptr(), sd.data_ptr(),
-                                 int(torch.cuda.current_stream().cuda_stream))
+    raw = qw.quantize_weights_f16_raw if w.dtype == np.float16 else qw.quantize_weights_raw
+    st = raw(wd.data_ptr(), n, k, pct, qd.data_ptr(), sd.data_ptr(),
+             int(torch.cuda.current_stream().cuda_stream))
     assert st == 0, qw.status_string(st)
     return host(qd), host(sd).view(np.uint16)
 

@@ -27,8 +27,8 @@ def _exported_symbols():
 
 def test_header_declares_the_entry_points():
     decl = _declared_functions()
-    for name in ("qw_quantize_weights", "qw_w8a16_gemm", "qw_w8a16_gemm_path",
-                 "qw_w8a16_gemm_auto_path", "qw_status_string", "qw_version"):
+    for name in ("qw_quantize_weights", "qw_quantize_weights_f16", "qw_w8a16_gemm", "qw_w8a16_gemm_path",
+                 "qw_w8a16_gemm_auto_path", "qw_w8a16_gemm_mfma_tile", "qw_status_string", "qw_version"):
         assert name in decl
 
 
@@ -85,6 +85,19 @@ D = 4 << 20
 ])
 def test_quantize_rejects(args, status):
     assert qw.quantize_weights_raw(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, -1, 16, 100.0, B, C), qw.QW_ERROR_INVALID_VALUE),          # n < 0
+    ((A, 4, 16, 0.0, B, C), qw.QW_ERROR_INVALID_VALUE),             # pct == 0
+    ((0, 4, 16, 100.0, B, C), qw.QW_ERROR_INVALID_VALUE),           # null w
+    ((A, 4, 24, 100.0, B, C), qw.QW_ERROR_UNSUPPORTED),             # k % 16
+    ((A + 8, 4, 16, 100.0, B, C), qw.QW_ERROR_MISALIGNED),
+    ((A, 4, 16, 100.0, A + 96, C), qw.QW_ERROR_INVALID_VALUE),      # q inside w (4 x 16 fp16 = 128 bytes)
+    ((A, 4, 16, 100.0, B, A + 112), qw.QW_ERROR_INVALID_VALUE),     # scales inside w's last row
+])
+def test_quantize_f16_rejects(args, status):
+    assert qw.quantize_weights_f16_raw(*args) == status
 
 
 def test_quantize_empty_is_noop():

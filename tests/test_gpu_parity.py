@@ -294,6 +294,25 @@ def test_quantize_percentile_near_top_with_duplicates(r):
     _check_quant(w, pct, "near-top r=%d" % r)
 
 
+@pytest.mark.parametrize("n,k,pct", [(64, 16, 100.0), (37, 1040, 100.0), (96, 4096, 99.99),
+                                      (300, 1024, 99.9), (17, 4112, 90.0), (8, 65536, 100.0)])
+def test_quantize_f16_input(n, k, pct):
+    """fp16 weights: the codes and scales must equal the oracle's on the
+    exactly widened fp32 matrix.  The matrix mixes normal, subnormal, zero
+    and large fp16 values."""
+    rng = np.random.default_rng(n * 131 + k)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float16)
+    w.flat[rng.integers(0, w.size, max(1, w.size // 500))] = np.float16(6.0e-6)   # subnormal
+    w.flat[rng.integers(0, w.size, max(1, w.size // 500))] = np.float16(0.0)
+    w.flat[rng.integers(0, w.size, max(1, w.size // 1000))] = np.float16(-3.5)
+    w[0, :] = np.float16(0.0)                                                        # all-zero row
+    say("quantize f16 n=%d k=%d pct=%r" % (n, k, pct))
+    q_ref, s_ref, _ = oracle.quantize(w.astype(np.float32), pct)
+    q, s = gpu_quantize(w, pct)
+    assert np.array_equal(s, s_ref), "scales differ at rows %s" % np.nonzero(s != s_ref)[0][:5]
+    assert np.array_equal(q, q_ref), "codes differ at %s" % np.argwhere(q != q_ref)[:5]
+
+
 def test_quantize_deterministic():
     wl, x, w, q, s = workload_data("transformer_big_ffn_outliers_m4096_k1024_n4096")
     say("quantize determinism")
