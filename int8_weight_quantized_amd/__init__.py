@@ -54,6 +54,16 @@ def _load():
         raise ImportError(
             "libqw.so is not built (expected at %s); run `python -m int8_weight_quantized_amd.build`"
             % LIBRARY_PATH)
+    # One HIP runtime per process: torch ships its own libamdhip64.so.7 and
+    # loads it under a different file name, so if libqw.so were loaded
+    # first the process would map two runtimes and torch's would find no
+    # GPU.  Importing torch first makes the loader resolve libqw.so's
+    # dependency (by soname) to the runtime torch already loaded, which is
+    # also what makes torch's stream handles valid here.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIBRARY_PATH)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.qw_quantize_weights.argtypes = [vp, i64, i64, ctypes.c_double, vp, vp, vp]

@@ -5,6 +5,7 @@ before touching the GPU (no compute call is made here)."""
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -46,6 +47,20 @@ def test_library_is_independent_of_the_oracle():
     assert not any(s.startswith("oracle_") for s in exported)
     deps = subprocess.run(["ldd", qw.LIBRARY_PATH], capture_output=True, text=True).stdout
     assert "oracle" not in deps
+
+
+def test_one_hip_runtime_whichever_loads_first():
+    """Loading libqw.so before torch must not map a second HIP runtime (torch
+    would then see no GPU and its stream handles would be foreign to libqw)."""
+    pytest.importorskip("torch")
+    code = (
+        "import int8_weight_quantized_amd as qw; qw.library(); import torch\n"
+        "paths = set(l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l)\n"
+        "print(len(paths)); print(sorted(paths))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.splitlines()[0] == "1", out.stdout
 
 
 def test_status_strings_and_version():

@@ -80,7 +80,8 @@ def test_gemm_workload(name):
 # on the CU count and the kernels' occupancy, so coverage is checked, not
 # which shape gets which tile).
 TILE_SHAPES = [(512, 27392, 256), (2048, 4608, 128), (256, 27392, 128), (384, 13824, 128),
-               (96, 27392, 256), (1024, 9216, 128), (4096, 4096, 64), (320, 6144, 144)]
+               (96, 27392, 256), (1024, 9216, 128), (4096, 4096, 64), (320, 6144, 144),
+               (384, 32768, 128), (129, 40960, 64)]
 
 
 def test_mfma_every_tile_shape():
