@@ -1,4 +1,5 @@
-"""CPU oracle for int8 weight-only quantization and the W8A16 matmul.
+"""CPU oracle for int8 weight-only quantization, the W8A16 matmul and the
+W8A8 (int8 x int8) matmul.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
 the ``cpu_baseline`` leg of ``bench.py`` may import this package.  The
@@ -71,6 +72,8 @@ def _declare(lib):
     lib.oracle_quantize.restype = ctypes.c_int
     lib.oracle_gemm.argtypes = [u16p, i8p, u16p, i64, i64, i64, f64p]
     lib.oracle_gemm_sampled.argtypes = [u16p, i8p, u16p, i64, i64p, i64p, i64, f64p]
+    lib.oracle_w8a8_gemm.argtypes = [i8p, u16p, i8p, u16p, i64, i64, i64, f64p]
+    lib.oracle_w8a8_gemm_sampled.argtypes = [i8p, u16p, i8p, u16p, i64, i64p, i64p, i64, f64p]
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
 
@@ -175,6 +178,42 @@ class Oracle:
                                     _ptr(ni, ctypes.c_int64), mi.size, _ptr(out, ctypes.c_double))
         return out
 
+    def w8a8_gemm(self, qx, sx_bits, q, s_bits) -> np.ndarray:
+        """Binary64 reference ref[m, n] = (sum_k qx[m,k] q[n,k]) * Sx[m] * S[n]."""
+        qx = np.ascontiguousarray(qx, dtype=np.int8)
+        sx = np.ascontiguousarray(sx_bits, dtype=np.uint16)
+        q = np.ascontiguousarray(q, dtype=np.int8)
+        s = np.ascontiguousarray(s_bits, dtype=np.uint16)
+        m, k = qx.shape
+        n = q.shape[0]
+        if q.shape != (n, k) or s.shape != (n,) or sx.shape != (m,):
+            raise ValueError("shape mismatch")
+        ref = np.empty((m, n), dtype=np.float64)
+        self._l.oracle_w8a8_gemm(_ptr(qx, ctypes.c_int8), _ptr(sx, ctypes.c_uint16),
+                                 _ptr(q, ctypes.c_int8), _ptr(s, ctypes.c_uint16), m, n, k,
+                                 _ptr(ref, ctypes.c_double))
+        return ref
+
+    def w8a8_gemm_sampled(self, qx, sx_bits, q, s_bits, mi, ni) -> np.ndarray:
+        """W8A8 ref[mi[c], ni[c]] for each c, computed one output at a time."""
+        qx = np.ascontiguousarray(qx, dtype=np.int8)
+        sx = np.ascontiguousarray(sx_bits, dtype=np.uint16)
+        q = np.ascontiguousarray(q, dtype=np.int8)
+        s = np.ascontiguousarray(s_bits, dtype=np.uint16)
+        mi = np.ascontiguousarray(mi, dtype=np.int64)
+        ni = np.ascontiguousarray(ni, dtype=np.int64)
+        k = qx.shape[1]
+        if q.shape[1] != k or mi.shape != ni.shape or sx.shape != (qx.shape[0],) or s.shape != (q.shape[0],):
+            raise ValueError("shape mismatch")
+        if mi.size and (mi.min() < 0 or mi.max() >= qx.shape[0] or ni.min() < 0 or ni.max() >= q.shape[0]):
+            raise IndexError("sample index out of range")
+        out = np.empty(mi.shape, dtype=np.float64)
+        self._l.oracle_w8a8_gemm_sampled(_ptr(qx, ctypes.c_int8), _ptr(sx, ctypes.c_uint16),
+                                         _ptr(q, ctypes.c_int8), _ptr(s, ctypes.c_uint16), k,
+                                         _ptr(mi, ctypes.c_int64), _ptr(ni, ctypes.c_int64), mi.size,
+                                         _ptr(out, ctypes.c_double))
+        return out
+
     def num_threads(self) -> int:
         return int(self._l.oracle_num_threads())
 
@@ -199,6 +238,14 @@ def gemm(x_f16, q, s_bits):
 
 def gemm_sampled(x_f16, q, s_bits, mi, ni):
     return default().gemm_sampled(x_f16, q, s_bits, mi, ni)
+
+
+def w8a8_gemm(qx, sx_bits, q, s_bits):
+    return default().w8a8_gemm(qx, sx_bits, q, s_bits)
+
+
+def w8a8_gemm_sampled(qx, sx_bits, q, s_bits, mi, ni):
+    return default().w8a8_gemm_sampled(qx, sx_bits, q, s_bits, mi, ni)
 
 
 def f64_to_f16_bits(x):

@@ -426,6 +426,69 @@ def pin_cosine_vs_unquantized(o):
     assert cos > 0.99, cos
 
 
+# --------------------------------------------------------------------------
+# W8A8 matmul reference
+# --------------------------------------------------------------------------
+
+def pin_w8a8_unit_scales_is_integer_matmul(o, seed=12):
+    """With every scale 1.0 the W8A8 reference is the integer matrix product,
+    which numpy computes exactly in int64."""
+    rng = np.random.default_rng(seed)
+    one = np.float16(1.0).view(np.uint16)
+    for (m, n, k) in ((1, 3, 16), (5, 7, 33), (4, 9, 1040)):
+        qx = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+        q = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+        ref = o.w8a8_gemm(qx, np.full(m, one, np.uint16), q, np.full(n, one, np.uint16))
+        want = qx.astype(np.int64) @ q.astype(np.int64).T
+        assert np.array_equal(ref, want.astype(np.float64))
+
+
+def pin_w8a8_equals_w8a16_on_exact_activations(o, seed=13):
+    """Power-of-two activation scales make x = qx * Sx exact in binary16, and
+    then every term and partial sum of both references is exact, so the W8A8
+    reference must equal the (separately pinned) W8A16 reference of the
+    dequantized activations exactly, element by element."""
+    rng = np.random.default_rng(seed)
+    for (m, n, k) in ((3, 5, 48), (6, 11, 256)):
+        qx = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+        ex = rng.integers(0, 11, size=m)
+        sx = (2.0 ** (-ex)).astype(np.float16)
+        x = (qx.astype(np.float64) * sx.astype(np.float64)[:, None]).astype(np.float16)
+        assert np.array_equal(x.astype(np.float64), qx.astype(np.float64) * sx.astype(np.float64)[:, None])
+        q = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+        s = rng.uniform(1e-4, 1e-2, size=n).astype(np.float16).view(np.uint16)
+        ref = o.w8a8_gemm(qx, sx.view(np.uint16), q, s)
+        assert np.array_equal(ref, o.gemm(x, q, s))
+        mi = rng.integers(0, m, size=13)
+        ni = rng.integers(0, n, size=13)
+        assert np.array_equal(o.w8a8_gemm_sampled(qx, sx.view(np.uint16), q, s, mi, ni), ref[mi, ni])
+
+
+def pin_w8a8_scaling_and_symmetry(o, seed=14):
+    """Row m scales with Sx[m] alone, column n with S[n] alone, and swapping
+    the operands transposes the result."""
+    rng = np.random.default_rng(seed)
+    m, n, k = 4, 6, 80
+    qx = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+    q = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+    sx = rng.uniform(1e-3, 1e-1, size=m).astype(np.float16)
+    s = rng.uniform(1e-4, 1e-2, size=n).astype(np.float16)
+    ref = o.w8a8_gemm(qx, sx.view(np.uint16), q, s.view(np.uint16))
+    sx2 = sx.copy()
+    sx2[1] = sx[1] * np.float16(2)
+    ref2 = o.w8a8_gemm(qx, sx2.view(np.uint16), q, s.view(np.uint16))
+    assert np.array_equal(ref2[1], 2.0 * ref[1])
+    assert np.array_equal(np.delete(ref2, 1, 0), np.delete(ref, 1, 0))
+    s2 = s.copy()
+    s2[4] = s[4] * np.float16(4)
+    ref3 = o.w8a8_gemm(qx, sx.view(np.uint16), q, s2.view(np.uint16))
+    assert np.array_equal(ref3[:, 4], 4.0 * ref[:, 4])
+    assert np.array_equal(np.delete(ref3, 4, 1), np.delete(ref, 4, 1))
+    assert np.array_equal(o.w8a8_gemm(q, s.view(np.uint16), qx, sx.view(np.uint16)), ref.T)
+    zero = o.w8a8_gemm(np.zeros_like(qx), sx.view(np.uint16), q, s.view(np.uint16))
+    assert np.all(zero == 0.0) and not np.any(np.signbit(zero))
+
+
 FAST_PINS = (
     pin_f32_to_f16_sample,
     pin_f16_to_f32_exhaustive,
@@ -442,4 +505,7 @@ FAST_PINS = (
     pin_gemm_bruteforce,
     pin_gemm_zero_and_scaling,
     pin_cosine_vs_unquantized,
+    pin_w8a8_unit_scales_is_integer_matmul,
+    pin_w8a8_equals_w8a16_on_exact_activations,
+    pin_w8a8_scaling_and_symmetry,
 )

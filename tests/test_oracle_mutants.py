@@ -44,6 +44,17 @@ MUTANTS = {
                         "double xv = (double)oracle_f16_to_f32(xrow[k - 1 - j]);"),
     "gemm_scale_of_wrong_row": ("(double)oracle_f16_to_f32(scales[j]), k);",
                                 "(double)oracle_f16_to_f32(scales[i % n]), k);"),
+    # W8A8: dropped activation scale, wrong sign, reversed k, narrow
+    # accumulator, activation scale taken from the weight's row index
+    "w8a8_drops_x_scale": ("return (double)acc * (sx * sw);", "return (double)acc * sw;"),
+    "w8a8_wrong_sign": ("acc += (int64_t)xrow[j] * (int64_t)qrow[j];",
+                        "acc -= (int64_t)xrow[j] * (int64_t)qrow[j];"),
+    "w8a8_reversed_k": ("acc += (int64_t)xrow[j] * (int64_t)qrow[j];",
+                        "acc += (int64_t)xrow[k - 1 - j] * (int64_t)qrow[j];"),
+    "w8a8_int16_accumulator": ("    int64_t acc = 0;\n    for (int64_t j = 0; j < k; ++j)\n        acc += (int64_t)xrow[j]",
+                               "    int16_t acc = 0;\n    for (int64_t j = 0; j < k; ++j)\n        acc += (int64_t)xrow[j]"),
+    "w8a8_x_scale_of_wrong_row": ("w8a8_one(qx + i * k, q + j * k, (double)oracle_f16_to_f32(sx[i]), sw, k);",
+                                  "w8a8_one(qx + i * k, q + j * k, (double)oracle_f16_to_f32(sx[j % m]), sw, k);"),
 }
 
 
