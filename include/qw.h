@@ -196,6 +196,58 @@ QW_API int qw_w8a16_gemm_auto_path(int64_t m, int64_t n, int64_t k);
  */
 QW_API int qw_w8a16_gemm_mfma_tile(int64_t m, int64_t n, int64_t k);
 
+/*
+ * qw_w8a8_gemm -- Y = (QX * Q^T) scaled by Sx[i] * S[c]: both operands int8
+ * with one fp16 scale per row (W8A8).
+ *
+ * Source: LightSeq slide deck ("LightSeq：高性能NLP序列推理实践"), slide
+ * 量化：裁剪+对称: the product of two symmetrically quantized values is the
+ * product of their codes times both scales, with no zero-point cross terms,
+ * so the matmul runs on int8 codes and the scales are applied once at the
+ * end; LightSeq's article ("最高加速9倍！字節跳動開源8比特混合精度
+ * Transformer引擎（1）", section on quantized inference speed) runs
+ * Transformer GEMMs this way as int8 GEMMs.  The activation codes and
+ * scales come from quantizing each activation row (token) with the
+ * weights' quantizer, qw_quantize_weights_f16 with clip_percentile 100.
+ *
+ *   acc[i][c] = sum_j QX[i][j] * Q[c][j]       exact, int32
+ *   Y[i][c]   = binary16_RNE( binary32(float(acc) * (S[c] * Sx[i])) )
+ *
+ * float(acc) rounds to binary32 only when |acc| >= 2^24; S[c] * Sx[i] is
+ * exact in binary32.  Accuracy contract: |Y - exact| <= 2^-10 |exact| +
+ * 2^-24 element-wise (one binary16 rounding plus at most two binary32
+ * roundings); bit-exact when |acc| < 2^24 and the scales are powers of two.
+ *
+ *   qx      int8 [m][k] activation codes
+ *   sx      fp16 bits [m], one scale per activation row
+ *   q       int8 [n][k] weight codes (as written by qw_quantize_weights)
+ *   scales  fp16 bits [n]
+ *   y       fp16 bits [m][n] (written)
+ *   m, n, k as qw_w8a16_gemm (k % 16 == 0; m == 0 or n == 0 is a no-op)
+ *   stream  hipStream_t
+ *
+ * One kernel for every m: the LDS-tiled MFMA GEMM on
+ * v_mfma_i32_32x32x32_i8, tile shape picked as for qw_w8a16_gemm's MFMA
+ * path.  All pointers 16-byte aligned.
+ *
+ * Errors: QW_ERROR_INVALID_VALUE (null pointer with m, n > 0, negative
+ * size, k <= 0, y overlapping qx, sx, q or scales), QW_ERROR_UNSUPPORTED
+ * (k % 16 != 0, a size beyond INT32_MAX), QW_ERROR_MISALIGNED,
+ * QW_ERROR_LAUNCH.
+ */
+QW_API qw_status qw_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t *q,
+                              const uint16_t *scales, uint16_t *y, int64_t m, int64_t n,
+                              int64_t k, void *stream);
+
+/*
+ * qw_w8a8_gemm_mfma_tile -- the output tile qw_w8a8_gemm uses for this
+ * shape on the current HIP device (same encoding and rules as
+ * qw_w8a16_gemm_mfma_tile, with the W8A8 kernels' occupancy: 256128,
+ * 256064 or 128064; 128 x 128 is not used).  Returns -1
+ * for shapes qw_w8a8_gemm rejects or when no HIP device is current.
+ */
+QW_API int qw_w8a8_gemm_mfma_tile(int64_t m, int64_t n, int64_t k);
+
 /* A static, human-readable name for a status code (never NULL). */
 QW_API const char *qw_status_string(qw_status status);
 

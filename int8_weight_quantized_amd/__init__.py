@@ -70,6 +70,10 @@ def _load():
     lib.qw_quantize_weights.restype = ctypes.c_int
     lib.qw_quantize_weights_f16.argtypes = [vp, i64, i64, ctypes.c_double, vp, vp, vp]
     lib.qw_quantize_weights_f16.restype = ctypes.c_int
+    lib.qw_w8a8_gemm.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.qw_w8a8_gemm.restype = ctypes.c_int
+    lib.qw_w8a8_gemm_mfma_tile.argtypes = [i64, i64, i64]
+    lib.qw_w8a8_gemm_mfma_tile.restype = ctypes.c_int
     lib.qw_w8a16_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     lib.qw_w8a16_gemm.restype = ctypes.c_int
     lib.qw_w8a16_gemm_path.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
@@ -119,6 +123,15 @@ def mfma_tile(m: int, n: int, k: int):
     return t // 1000, t % 1000
 
 
+def w8a8_tile(m: int, n: int, k: int):
+    """(BN, BM) output tile the W8A8 kernel uses for this shape on the
+    current device (needs a GPU)."""
+    t = int(library().qw_w8a8_gemm_mfma_tile(m, n, k))
+    if t < 0:
+        raise ValueError("no W8A8 tile for m=%d n=%d k=%d (bad shape or no device)" % (m, n, k))
+    return t // 1000, t % 1000
+
+
 # ---------------------------------------------------------------------------
 # raw C-ABI calls (device pointers as ints); used by tests and the benchmark
 # ---------------------------------------------------------------------------
@@ -136,6 +149,11 @@ def quantize_weights_f16_raw(w_ptr: int, n: int, k: int, clip_percentile: float,
 def w8a16_gemm_raw(x_ptr: int, q_ptr: int, s_ptr: int, y_ptr: int, m: int, n: int, k: int,
                    stream: int = 0, path: int = 0) -> int:
     return int(library().qw_w8a16_gemm_path(x_ptr, q_ptr, s_ptr, y_ptr, m, n, k, int(path), stream))
+
+
+def w8a8_gemm_raw(qx_ptr: int, sx_ptr: int, q_ptr: int, s_ptr: int, y_ptr: int, m: int, n: int,
+                  k: int, stream: int = 0) -> int:
+    return int(library().qw_w8a8_gemm(qx_ptr, sx_ptr, q_ptr, s_ptr, y_ptr, m, n, k, stream))
 
 
 # ---------------------------------------------------------------------------
@@ -222,6 +240,41 @@ def w8a16_gemm(x, q, scales, out=None, path: str = "auto"):
     return y
 
 
-__all__ = ["quantize_weights", "w8a16_gemm", "QwError", "status_string", "version", "library",
-           "auto_path",
-           "quantize_weights_raw", "w8a16_gemm_raw", "PATHS", "LIBRARY_PATH"]
+def quantize_activations(x, out=None):
+    """Per-token (per-row) symmetric int8 quantization of fp16 activations
+    [M, K] for W8A8: the weights' quantizer with the row absmax.  Returns
+    (qx int8 [M, K], sx float16 [M])."""
+    return quantize_weights(x, 100.0, out=out)
+
+
+def w8a8_gemm(qx, sx, q, scales, out=None):
+    """Y = (qx * q^T) * sx[:, None] * scales[None, :]: qx int8 [M, K], sx fp16
+    [M], q int8 [N, K], scales fp16 [N] -> fp16 [M, N]."""
+    torch = _torch()
+    _check(qx, "qx", torch.int8, 2)
+    _check(sx, "sx", torch.float16, 1)
+    _check(q, "q", torch.int8, 2)
+    _check(scales, "scales", torch.float16, 1)
+    m, k = qx.shape
+    n = q.shape[0]
+    if q.shape[1] != k or scales.shape[0] != n or sx.shape[0] != m:
+        raise ValueError("shape mismatch: qx %s, sx %s, q %s, scales %s" % (
+            tuple(qx.shape), tuple(sx.shape), tuple(q.shape), tuple(scales.shape)))
+    if out is None:
+        y = torch.empty((m, n), dtype=torch.float16, device=qx.device)
+    else:
+        y = out
+        _check(y, "out", torch.float16, 2)
+        if tuple(y.shape) != (m, n):
+            raise ValueError("out must be [M, N]")
+    st = w8a8_gemm_raw(qx.data_ptr(), sx.data_ptr(), q.data_ptr(), scales.data_ptr(), y.data_ptr(),
+                       m, n, k, _stream_of(qx))
+    if st != QW_SUCCESS:
+        raise QwError(st, "qw_w8a8_gemm")
+    return y
+
+
+__all__ = ["quantize_weights", "quantize_activations", "w8a16_gemm", "w8a8_gemm", "QwError",
+           "status_string", "version", "library", "auto_path", "mfma_tile", "w8a8_tile",
+           "quantize_weights_raw", "quantize_weights_f16_raw", "w8a16_gemm_raw", "w8a8_gemm_raw",
+           "PATHS", "LIBRARY_PATH"]

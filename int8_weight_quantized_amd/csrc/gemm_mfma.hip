@@ -34,6 +34,8 @@ namespace {
 
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef float float16v __attribute__((ext_vector_type(16)));
+typedef int int4v __attribute__((ext_vector_type(4)));
+typedef int int16v __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 64; // k per step
 
@@ -83,13 +85,14 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks)
 // ---------------------------------------------------------------------------
 
 // NW waves per workgroup side by side along n; each wave owns BN / NW
-// output channels x all BM activation rows.
-template <int NW, int BN, int BM>
+// output channels x all BM activation rows.  A8: the activations are int8
+// codes (W8A8) instead of fp16.
+template <int NW, int BN, int BM, bool A8>
 struct DmaCfg {
     static constexpr int kBN = BN;                            // output channels per workgroup
     static constexpr int kWBytes = BN * kBK;                  // int8 weight tile per stage
     static constexpr int kThreads = NW * kWave;
-    static constexpr int kXBytes = BM * kBK * 2;             // fp16 activation tile per stage
+    static constexpr int kXBytes = BM * kBK * (A8 ? 1 : 2);  // activation tile per stage
     static constexpr int kStage = kWBytes + kXBytes;
     static constexpr int kWInstr = kWBytes / 1024 / NW;      // copies per wave per stage
     static constexpr int kXInstr = kXBytes / 1024 / NW;
@@ -103,7 +106,7 @@ struct DmaCfg {
     static constexpr int kYHalf = (BM / 2) * kYRow;
     static constexpr int kStageAlloc = kStage > kYHalf ? kStage : kYHalf;
     static_assert(kWInstr * 64 * 16 * NW == kWBytes && kXInstr * 64 * 16 * NW == kXBytes, "copy split");
-    static_assert(kXInstr % 2 == 0, "activation copies alternate between the two 8-row swizzle phases");
+    static_assert(A8 || kXInstr % 2 == 0, "fp16 activation copies alternate between the two 8-row swizzle phases");
     static_assert(kSI >= 1 && kWaveN % 32 == 0 && BM % 64 == 0, "tile config");
 };
 
@@ -144,18 +147,25 @@ __device__ __forceinline__ int xslot(int row)
 template <int I>
 using stage_t = std::integral_constant<int, I>;
 
-template <int NW, int BN, int BM>
+// A8 (W8A8): x holds int8 activation codes with one fp16 scale per row in
+// sx; the MFMA is v_mfma_i32_32x32x32_i8 with exact int32 accumulators and
+// the epilogue multiplies by S[n] * Sx[m].  Otherwise x is fp16 and sx is
+// unused.
+template <int NW, int BN, int BM, bool A8>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm_dma_kernel(
-    const uint16_t *__restrict__ x, const int8_t *__restrict__ q,
+    const void *__restrict__ xv, const uint16_t *__restrict__ sx, const int8_t *__restrict__ q,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y,
     int m, int n, int k, int tiles_m, int tiles_n)
 {
-    using C = DmaCfg<NW, BN, BM>;
+    using C = DmaCfg<NW, BN, BM, A8>;
     constexpr int kSJ = C::kSJ;
+    const uint16_t *__restrict__ x = static_cast<const uint16_t *>(xv);
+    const int8_t *__restrict__ qx = static_cast<const int8_t *>(xv);
     __shared__ __attribute__((aligned(1024))) uint8_t ring0[C::kStageAlloc];
     __shared__ __attribute__((aligned(1024))) uint8_t ring1[C::kStageAlloc];
     __shared__ __attribute__((aligned(16))) float scale_lds[BN];
+    __shared__ __attribute__((aligned(16))) float xscale_lds[A8 ? BM : 1];
     auto ring = [&](auto s) -> uint8_t * {
         if constexpr (decltype(s)::value == 0)
             return ring0;
@@ -203,13 +213,24 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
 #pragma unroll
         for (int i = 0; i < C::kXInstr; ++i) {
             uint8_t *dst = st + C::kWBytes + (wave * C::kXInstr + i) * 1024;
-            const int row = (wave * C::kXInstr + i) * 8 + lane / 8;
-            const int gm = min(m0 + row, m - 1);
-            const int gk = k0 + ((i & 1) ? xchunk_odd : xchunk_even) * 8;
-            if (decltype(full)::value || gk < k)
-                __builtin_amdgcn_global_load_lds(x + (int64_t)gm * k + gk, (lds_ptr_t)dst, 16, 0, 0);
-            else
-                *reinterpret_cast<u32x4_t *>(dst + lane * 16) = (u32x4_t){0u, 0u, 0u, 0u};
+            if constexpr (A8) {
+                // int8 activation rows are laid out like weight rows
+                const int row = (wave * C::kXInstr + i) * 16 + lane / 4;
+                const int gm = min(m0 + row, m - 1);
+                const int gk = k0 + wchunk * 16;
+                if (decltype(full)::value || gk < k)
+                    __builtin_amdgcn_global_load_lds(qx + (int64_t)gm * k + gk, (lds_ptr_t)dst, 16, 0, 0);
+                else
+                    *reinterpret_cast<u32x4_t *>(dst + lane * 16) = (u32x4_t){0u, 0u, 0u, 0u};
+            } else {
+                const int row = (wave * C::kXInstr + i) * 8 + lane / 8;
+                const int gm = min(m0 + row, m - 1);
+                const int gk = k0 + ((i & 1) ? xchunk_odd : xchunk_even) * 8;
+                if (decltype(full)::value || gk < k)
+                    __builtin_amdgcn_global_load_lds(x + (int64_t)gm * k + gk, (lds_ptr_t)dst, 16, 0, 0);
+                else
+                    *reinterpret_cast<u32x4_t *>(dst + lane * 16) = (u32x4_t){0u, 0u, 0u, 0u};
+            }
         }
     };
     using full_t = std::integral_constant<bool, true>;
@@ -233,14 +254,54 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
     for (int sidx = 0; sidx < 4; ++sidx)
         x_off[sidx] = C::kWBytes + xrow * 2 * kBK + 16 * ((4 * lgrp + sidx) ^ xslot(xrow));
 
-    float16v acc[C::kSI][kSJ];
+    // A8: v_mfma_i32_32x32x32_i8 takes 16 consecutive k codes per lane, and
+    // a 64-wide k step is two MFMAs s = 0, 1; in MFMA s, lane group g covers
+    // the 16 codes of chunk 2 g + s of its row, for the weight (A) and the
+    // activation (B) operand alike, so every k is paired with itself.
+    const int xa_off0 = C::kWBytes + xrow * kBK + 16 * ((2 * lgrp) ^ wslot(xrow));
+    const int xa_off1 = C::kWBytes + xrow * kBK + 16 * ((2 * lgrp + 1) ^ wslot(xrow));
+
+    using acc_t = std::conditional_t<A8, int16v, float16v>;
+    acc_t acc[C::kSI][kSJ];
 #pragma unroll
     for (int i = 0; i < C::kSI; ++i)
 #pragma unroll
         for (int j = 0; j < kSJ; ++j)
-            acc[i][j] = (float16v){};
+            acc[i][j] = (acc_t){};
+
+    auto compute_a8 = [&](const uint8_t *st) {
+        u32x4_t clo[C::kSI], chi[C::kSI];
+#pragma unroll
+        for (int i = 0; i < C::kSI; ++i) {
+            clo[i] = *reinterpret_cast<const u32x4_t *>(st + w_off0 + i * 32 * kBK);
+            chi[i] = *reinterpret_cast<const u32x4_t *>(st + w_off1 + i * 32 * kBK);
+        }
+        u32x4_t blo[kSJ], bhi[kSJ];
+#pragma unroll
+        for (int j = 0; j < kSJ; ++j) {
+            blo[j] = *reinterpret_cast<const u32x4_t *>(st + xa_off0 + j * 32 * kBK);
+            bhi[j] = *reinterpret_cast<const u32x4_t *>(st + xa_off1 + j * 32 * kBK);
+        }
+#pragma unroll
+        for (int i = 0; i < C::kSI; ++i)
+#pragma unroll
+            for (int j = 0; j < kSJ; ++j)
+                if constexpr (A8)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                        __builtin_bit_cast(int4v, clo[i]), __builtin_bit_cast(int4v, blo[j]), acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < C::kSI; ++i)
+#pragma unroll
+            for (int j = 0; j < kSJ; ++j)
+                if constexpr (A8)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                        __builtin_bit_cast(int4v, chi[i]), __builtin_bit_cast(int4v, bhi[j]), acc[i][j], 0, 0, 0);
+    };
 
     auto compute = [&](const uint8_t *st) {
+      if constexpr (A8) {
+        compute_a8(st);
+      } else {
         u32x4_t clo[C::kSI], chi[C::kSI];
 #pragma unroll
         for (int i = 0; i < C::kSI; ++i) {
@@ -261,9 +322,11 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
                 const half8_t a = (sidx & 1) ? i8x8_to_half8(c.z, c.w) : i8x8_to_half8(c.x, c.y);
 #pragma unroll
                 for (int j = 0; j < kSJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[j][sidx], acc[i][j], 0, 0, 0);
+                    if constexpr (!A8)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[j][sidx], acc[i][j], 0, 0, 0);
             }
         }
+      }
     };
 
     // prologue: tile 0 in flight
@@ -275,6 +338,11 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
 #pragma unroll
     for (int c = tid; c < BN; c += C::kThreads)
         scale_lds[c] = n0 + c < n ? f16_bits_to_f32(scales[n0 + c]) : 0.0f;
+    if constexpr (A8) {
+#pragma unroll
+        for (int r = tid; r < BM; r += C::kThreads)
+            xscale_lds[r] = m0 + r < m ? f16_bits_to_f32(sx[m0 + r]) : 0.0f;
+    }
 
     // Step t (stage t % 2) waits for its own copies of tile t, the barrier
     // publishes everyone's copies and certifies that tile t-1's stage is no
@@ -330,10 +398,18 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
                 // rows [0, BM/2) of the image live in stage 0's array
                 uint8_t *img = j < kSJ / 2 ? ring0 + (j * 32 + lrow) * C::kYRow
                                            : ring1 + (j * 32 - BM / 2 + lrow) * C::kYRow;
-                const uint32_t o0 = f32_to_f16_bits(acc[i][j][4 * qd + 0] * sc[0]);
-                const uint32_t o1 = f32_to_f16_bits(acc[i][j][4 * qd + 1] * sc[1]);
-                const uint32_t o2 = f32_to_f16_bits(acc[i][j][4 * qd + 2] * sc[2]);
-                const uint32_t o3 = f32_to_f16_bits(acc[i][j][4 * qd + 3] * sc[3]);
+                // W8A16: acc * S[n].  W8A8: float(acc) * (S[n] * Sx[m]); the
+                // product of two fp16 scales is exact in fp32.
+                auto val = [&](int e) -> float {
+                    if constexpr (A8)
+                        return (float)acc[i][j][4 * qd + e] * (sc[e] * xscale_lds[j * 32 + lrow]);
+                    else
+                        return acc[i][j][4 * qd + e] * sc[e];
+                };
+                const uint32_t o0 = f32_to_f16_bits(val(0));
+                const uint32_t o1 = f32_to_f16_bits(val(1));
+                const uint32_t o2 = f32_to_f16_bits(val(2));
+                const uint32_t o3 = f32_to_f16_bits(val(3));
                 *reinterpret_cast<u32x2_t *>(img + nl * 2) = (u32x2_t){o0 | (o1 << 16), o2 | (o3 << 16)};
             }
         }
@@ -362,23 +438,23 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
     }
 }
 
-template <int NW, int BN, int BM>
-hipError_t launch_dma(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
-                      int64_t m, int64_t n, int64_t k, hipStream_t stream)
+template <int NW, int BN, int BM, bool A8>
+hipError_t launch_dma(const void *x, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
+                      uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
     const int64_t tiles_m = (m + BM - 1) / BM;
     const int64_t tiles_n = (n + BN - 1) / BN;
     const int64_t blocks = tiles_m * tiles_n;
     if (blocks > 0x7fffffff)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((mfma_gemm_dma_kernel<NW, BN, BM>), dim3((unsigned)blocks), dim3(NW * kWave),
-                       0, stream, x, q, scales, y, (int)m, (int)n, (int)k, (int)tiles_m, (int)tiles_n);
+    hipLaunchKernelGGL((mfma_gemm_dma_kernel<NW, BN, BM, A8>), dim3((unsigned)blocks), dim3(NW * kWave),
+                       0, stream, x, sx, q, scales, y, (int)m, (int)n, (int)k, (int)tiles_m, (int)tiles_n);
     return hipGetLastError();
 }
 
 // Workgroups of this tile shape one CU holds at once (registers and LDS),
 // queried once per device.
-template <int BN, int BM>
+template <int BN, int BM, bool A8>
 int64_t slots_per_cu()
 {
     static int cached[64] = {0};
@@ -387,50 +463,80 @@ int64_t slots_per_cu()
         return 1;
     if (cached[dev] == 0) {
         int blocks = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, mfma_gemm_dma_kernel<4, BN, BM>, 4 * kWave, 0) !=
-                hipSuccess || blocks < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, mfma_gemm_dma_kernel<4, BN, BM, A8>,
+                                                        4 * kWave, 0) != hipSuccess || blocks < 1)
             blocks = 1;
         cached[dev] = blocks;
     }
     return cached[dev];
 }
 
-template <int BN, int BM>
+template <int BN, int BM, bool A8>
 bool fills(int64_t m, int64_t n)
 {
     const int64_t tiles = ((n + BN - 1) / BN) * ((m + BM - 1) / BM);
-    const int64_t slots = slots_per_cu<BN, BM>() * (int64_t)device_cu_count();
+    const int64_t slots = slots_per_cu<BN, BM, A8>() * (int64_t)device_cu_count();
     return 4 * tiles >= 3 * slots;
+}
+
+template <bool A8>
+int tile_choice(int64_t m, int64_t n)
+{
+    // largest tile first (more reuse per byte staged); 256 x 64 before
+    // 128 x 128 (same area, half the activation bytes per tile)
+    if (fills<256, 128, A8>(m, n))
+        return 256128;
+    if (fills<256, 64, A8>(m, n))
+        return 256064;
+    // W8A8: the 128 x 128 tile holds four workgroups per CU (int8 activation
+    // tiles are half the LDS), so it fills the chip only where 256 x 64
+    // already does and is never the choice
+    if (!A8 && fills<128, 128, A8>(m, n))
+        return 128128;
+    return 128064;
+}
+
+template <bool A8>
+hipError_t launch_tiles(const void *x, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
+                        uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
+{
+    switch (tile_choice<A8>(m, n)) {
+    case 256128:
+        return launch_dma<4, 256, 128, A8>(x, sx, q, scales, y, m, n, k, stream);
+    case 256064:
+        return launch_dma<4, 256, 64, A8>(x, sx, q, scales, y, m, n, k, stream);
+    case 128128:
+        if constexpr (!A8)
+            return launch_dma<4, 128, 128, A8>(x, sx, q, scales, y, m, n, k, stream);
+        [[fallthrough]];
+    default:
+        return launch_dma<4, 128, 64, A8>(x, sx, q, scales, y, m, n, k, stream);
+    }
 }
 
 } // namespace
 
 int mfma_tile_choice(int64_t m, int64_t n)
 {
-    // largest tile first (more reuse per byte staged); 256 x 64 before
-    // 128 x 128 (same area, half the activation bytes per tile)
-    if (fills<256, 128>(m, n))
-        return 256128;
-    if (fills<256, 64>(m, n))
-        return 256064;
-    if (fills<128, 128>(m, n))
-        return 128128;
-    return 128064;
+    return tile_choice<false>(m, n);
+}
+
+int w8a8_tile_choice(int64_t m, int64_t n)
+{
+    return tile_choice<true>(m, n);
 }
 
 hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
                             int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
-    switch (mfma_tile_choice(m, n)) {
-    case 256128:
-        return launch_dma<4, 256, 128>(x, q, scales, y, m, n, k, stream);
-    case 256064:
-        return launch_dma<4, 256, 64>(x, q, scales, y, m, n, k, stream);
-    case 128128:
-        return launch_dma<4, 128, 128>(x, q, scales, y, m, n, k, stream);
-    default:
-        return launch_dma<4, 128, 64>(x, q, scales, y, m, n, k, stream);
-    }
+    return launch_tiles<false>(x, nullptr, q, scales, y, m, n, k, stream);
+}
+
+hipError_t launch_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t *q,
+                            const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                            hipStream_t stream)
+{
+    return launch_tiles<true>(qx, sx, q, scales, y, m, n, k, stream);
 }
 
 } // namespace qw

@@ -207,6 +207,37 @@ QW_API int qw_w8a16_gemm_mfma_tile(int64_t m, int64_t n, int64_t k)
     return qw::mfma_tile_choice(m, n);
 }
 
+QW_API qw_status qw_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t *q,
+                              const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                              void *stream)
+{
+    if (m < 0 || n < 0 || k <= 0)
+        return QW_ERROR_INVALID_VALUE;
+    if (m == 0 || n == 0)
+        return QW_SUCCESS;
+    if (!qx || !sx || !q || !scales || !y)
+        return QW_ERROR_INVALID_VALUE;
+    if (k % 16 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim)
+        return QW_ERROR_UNSUPPORTED;
+    if (misaligned(qx) || misaligned(sx) || misaligned(q) || misaligned(scales) || misaligned(y))
+        return QW_ERROR_MISALIGNED;
+    const uint64_t ybytes = (uint64_t)m * (uint64_t)n * 2u;
+    if (overlaps(y, ybytes, qx, (uint64_t)m * (uint64_t)k) || overlaps(y, ybytes, sx, (uint64_t)m * 2u) ||
+        overlaps(y, ybytes, q, (uint64_t)n * (uint64_t)k) || overlaps(y, ybytes, scales, (uint64_t)n * 2u))
+        return QW_ERROR_INVALID_VALUE;
+    return launch_status(qw::launch_w8a8_gemm(qx, sx, q, scales, y, m, n, k, static_cast<hipStream_t>(stream)));
+}
+
+QW_API int qw_w8a8_gemm_mfma_tile(int64_t m, int64_t n, int64_t k)
+{
+    if (m <= 0 || n <= 0 || k <= 0 || k % 16 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim)
+        return -1;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return -1;
+    return qw::w8a8_tile_choice(m, n);
+}
+
 QW_API const char *qw_status_string(qw_status status)
 {
     switch (status) {

@@ -40,6 +40,13 @@ hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *
 // encoded BN * 1000 + BM.
 int mfma_tile_choice(int64_t m, int64_t n);
 
+// W8A8 GEMM on the matrix cores (int8 activation codes qx [m, k] with one
+// fp16 scale per row in sx), any m, n, k with k % 16 == 0, and its tile.
+hipError_t launch_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t *q,
+                            const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                            hipStream_t stream);
+int w8a8_tile_choice(int64_t m, int64_t n);
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
 

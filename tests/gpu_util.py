@@ -66,6 +66,35 @@ def gpu_gemm(x: np.ndarray, q: np.ndarray, s_bits: np.ndarray, path: int = 0):
     return host(yd).view(np.float16)
 
 
+def gpu_w8a8(qx: np.ndarray, sx_bits: np.ndarray, q: np.ndarray, s_bits: np.ndarray):
+    """W8A8 GEMM on the GPU through the C ABI; returns Y as float16."""
+    import int8_weight_quantized_amd as qw
+    torch = torch_mod()
+    m, k = qx.shape
+    n = q.shape[0]
+    qxd = dev(np.ascontiguousarray(qx, dtype=np.int8))
+    sxd = dev(np.ascontiguousarray(sx_bits, dtype=np.uint16).view(np.int16))
+    qd = dev(np.ascontiguousarray(q, dtype=np.int8))
+    sd = dev(np.ascontiguousarray(s_bits, dtype=np.uint16).view(np.int16))
+    yd = torch.full((m, n), 0x7e00, dtype=torch.int16, device="cuda:0")  # NaN canary
+    st = qw.w8a8_gemm_raw(qxd.data_ptr(), sxd.data_ptr(), qd.data_ptr(), sd.data_ptr(), yd.data_ptr(),
+                          m, n, k, int(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, qw.status_string(st)
+    return host(yd).view(np.float16)
+
+
+def assert_w8a8_close(y: np.ndarray, ref: np.ndarray, what: str = ""):
+    """Element-wise |Y - ref| <= 2^-10 |ref| + 2^-24: one binary16 rounding
+    (at most 2^-11 relative) of a value carrying at most two binary32
+    roundings, with the binary16 subnormal quantum covered by 2^-24."""
+    y64 = y.astype(np.float64)
+    assert np.all(np.isfinite(y64)), "%s: non-finite output" % what
+    bound = np.abs(ref) * 2.0 ** -10 + 2.0 ** -24
+    bad = np.argwhere(np.abs(y64 - ref) > bound)
+    assert bad.size == 0, "%s: %d elements out of bound, first %s (gpu %r, ref %r)" % (
+        what, len(bad), bad[0], y64[tuple(bad[0])], ref[tuple(bad[0])])
+
+
 def assert_gemm_close(y: np.ndarray, ref: np.ndarray, what: str = ""):
     """max |Y - ref| <= 2e-3 * max|ref| + 1e-3, with ref the binary64 oracle."""
     y64 = y.astype(np.float64)

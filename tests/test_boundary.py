@@ -29,7 +29,8 @@ def _exported_symbols():
 def test_header_declares_the_entry_points():
     decl = _declared_functions()
     for name in ("qw_quantize_weights", "qw_quantize_weights_f16", "qw_w8a16_gemm", "qw_w8a16_gemm_path",
-                 "qw_w8a16_gemm_auto_path", "qw_w8a16_gemm_mfma_tile", "qw_status_string", "qw_version"):
+                 "qw_w8a16_gemm_auto_path", "qw_w8a16_gemm_mfma_tile", "qw_w8a8_gemm",
+                 "qw_w8a8_gemm_mfma_tile", "qw_status_string", "qw_version"):
         assert name in decl
 
 
@@ -141,6 +142,39 @@ def test_quantize_empty_is_noop():
 ])
 def test_gemm_rejects(args, status):
     assert qw.w8a16_gemm_raw(*args) == status
+
+
+E = 5 << 20
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, B, C, D, E, -1, 4, 16), qw.QW_ERROR_INVALID_VALUE),
+    ((A, B, C, D, E, 1, -4, 16), qw.QW_ERROR_INVALID_VALUE),
+    ((A, B, C, D, E, 1, 4, 0), qw.QW_ERROR_INVALID_VALUE),
+    ((0, B, C, D, E, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),
+    ((A, 0, C, D, E, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),
+    ((A, B, 0, D, E, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),
+    ((A, B, C, 0, E, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),
+    ((A, B, C, D, 0, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),
+    ((A, B, C, D, E, 1, 4, 24), qw.QW_ERROR_UNSUPPORTED),
+    ((A, B, C, D, E, 1 << 31, 4, 16), qw.QW_ERROR_UNSUPPORTED),
+    ((A + 1, B, C, D, E, 1, 4, 16), qw.QW_ERROR_MISALIGNED),
+    ((A, B + 2, C, D, E, 1, 4, 16), qw.QW_ERROR_MISALIGNED),
+    ((A, B, C + 8, D, E, 1, 4, 16), qw.QW_ERROR_MISALIGNED),
+    ((A, B, C, D + 4, E, 1, 4, 16), qw.QW_ERROR_MISALIGNED),
+    ((A, B, C, D, E + 2, 1, 4, 16), qw.QW_ERROR_MISALIGNED),
+    ((A, B, C, D, A, 2, 4, 16), qw.QW_ERROR_INVALID_VALUE),         # y overlaps qx
+    ((A, B, C, D, B - 16, 2, 8, 16), qw.QW_ERROR_INVALID_VALUE),    # y overlaps sx
+    ((A, B, C, D, C + 32, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),    # y overlaps q
+    ((A, B, C, D, D, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),         # y overlaps scales
+])
+def test_w8a8_rejects(args, status):
+    assert qw.w8a8_gemm_raw(*args) == status
+
+
+def test_w8a8_empty_is_noop():
+    assert qw.w8a8_gemm_raw(0, 0, 0, 0, 0, 0, 4, 16) == qw.QW_SUCCESS
+    assert qw.w8a8_gemm_raw(0, 0, 0, 0, 0, 3, 0, 16) == qw.QW_SUCCESS
 
 
 def test_gemm_path_checks():
