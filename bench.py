@@ -14,8 +14,9 @@ Printed: ONE JSON line with the whole-step throughput (algorithmic bytes of
 both kernels / step time, in TB/s), a roofline entry for the kernel that
 takes most of the step (its algorithmic bytes / its average duration,
 measured with HIP events on the launch stream), per-kernel figures, cold
-GEMM-only figures for every workload (decode TB/s, prefill TFLOP/s), and the
-CPU oracle timed on the host cores.
+GEMM-only figures for every workload (decode TB/s, prefill TFLOP/s), cold
+figures of the W8A8 (int8 x int8) GEMM with per-token activation
+quantization, and the CPU oracle timed on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -37,6 +38,7 @@ if ROOT not in sys.path:
 METRIC = "W8A16 GEMM effective TB/s (decode M=1) and TFLOP/s (prefill M=512), 1×MI355X"
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, AMD published
 MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 MFMA, AMD published
+MFMA_I8_PEAK_TOPS = 5000.0       # MI355X dense int8 MFMA, AMD published
 MALL_BYTES = 256 << 20           # Infinity Cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CSRC = os.path.join(ROOT, "int8_weight_quantized_amd", "csrc")
@@ -60,6 +62,18 @@ def gemm_bytes(m, n, k):
 
 def gemm_flops(m, n, k):
     return 2 * m * n * k
+
+
+def w8a8_bytes(m, n, k):
+    """Algorithmic bytes of the W8A8 GEMM: int8 weight and activation codes,
+    fp16 scales of both, fp16 Y written."""
+    return n * k + 2 * n + m * k + 2 * m + 2 * m * n
+
+
+def act_quant_bytes(m, k):
+    """Algorithmic bytes of per-token activation quantization: read X fp16,
+    write codes and fp16 scales."""
+    return 2 * m * k + m * k + 2 * m
 
 
 def kernel_source_sha(kernel):
@@ -140,6 +154,81 @@ class StepRunner:
                                     self.y[i].data_ptr(), wl.m, wl.n, wl.k, self.stream, 0)
         if st:
             raise RuntimeError(self.qw.status_string(st))
+
+
+class W8A8Runner:
+    """Rotating operand sets for the W8A8 path: fp16 activations quantized
+    per token (the library's quantizer), int8 weight codes quantized once."""
+
+    def __init__(self, wl, sets):
+        import torch
+
+        import int8_weight_quantized_amd as qw
+        import synthetic
+        self.qw, self.torch, self.wl, self.sets = qw, torch, wl, sets
+        x, w = synthetic.make_inputs(wl)
+        dev = "cuda:0"
+        xd = torch.from_numpy(x).to(dev)
+        self.x = [xd] + [xd.clone() for _ in range(sets - 1)]
+        wd = torch.from_numpy(w).to(dev)
+        q0, s0 = qw.quantize_weights(wd, wl.clip_percentile)
+        del wd
+        self.q = [q0] + [q0.clone() for _ in range(sets - 1)]
+        self.s = [s0] + [s0.clone() for _ in range(sets - 1)]
+        self.qx = [torch.empty((wl.m, wl.k), dtype=torch.int8, device=dev) for _ in range(sets)]
+        self.sx = [torch.empty((wl.m,), dtype=torch.float16, device=dev) for _ in range(sets)]
+        self.y = [torch.empty((wl.m, wl.n), dtype=torch.float16, device=dev) for _ in range(sets)]
+        self.stream = int(torch.cuda.current_stream().cuda_stream)
+        for i in range(sets):
+            self.quantize(i)
+
+    def quantize(self, i):
+        wl = self.wl
+        st = self.qw.quantize_weights_f16_raw(self.x[i].data_ptr(), wl.m, wl.k, 100.0, self.qx[i].data_ptr(),
+                                              self.sx[i].data_ptr(), self.stream)
+        if st:
+            raise RuntimeError(self.qw.status_string(st))
+
+    def gemm(self, i):
+        wl = self.wl
+        st = self.qw.w8a8_gemm_raw(self.qx[i].data_ptr(), self.sx[i].data_ptr(), self.q[i].data_ptr(),
+                                   self.s[i].data_ptr(), self.y[i].data_ptr(), wl.m, wl.n, wl.k, self.stream)
+        if st:
+            raise RuntimeError(self.qw.status_string(st))
+
+
+def time_w8a8(wl, launches=40, warmup=10):
+    """Cold W8A8 figures for one workload: the GEMM alone (as
+    time_gemm_only) and per-token activation quantization followed by the
+    GEMM, each launch pair timed with events."""
+    import torch
+    r = W8A8Runner(wl, rotation_count(w8a8_bytes(wl.m, wl.n, wl.k) + act_quant_bytes(wl.m, wl.k)))
+    avg_ms, med_ms = time_gemm_only(r, launches, warmup)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(launches)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(40_000_000)
+    for it in range(launches):
+        i = it % r.sets
+        ev[it][0].record()
+        r.quantize(i)
+        ev[it][1].record()
+        r.gemm(i)
+        ev[it][2].record()
+    torch.cuda.synchronize()
+    aq_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / launches
+    pair_ms = sum(e[0].elapsed_time(e[2]) for e in ev) / launches
+    ops = gemm_flops(wl.m, wl.n, wl.k)
+    tile = r.qw.w8a8_tile(wl.m, wl.n, wl.k)
+    sets = r.sets
+    del r
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "kernel": "w8a8_mfma", "mfma_tile": list(tile), "cold_sets": sets,
+            "avg_us": avg_ms * 1e3, "median_us": med_ms * 1e3,
+            "TOPs": ops / (avg_ms * 1e-3) / 1e12,
+            "mfma_i8_frac": ops / (avg_ms * 1e-3) / 1e12 / MFMA_I8_PEAK_TOPS,
+            "TBps": w8a8_bytes(wl.m, wl.n, wl.k) / (avg_ms * 1e-3) / 1e12,
+            "act_quantize_us": aq_ms * 1e3,
+            "act_quantize_plus_gemm_us": pair_ms * 1e3}
 
 
 def time_full_steps(runner, steps, warmup):
@@ -270,6 +359,9 @@ def main():
     ap.add_argument("--sweep-paths", action="store_true",
                     help="only time every GEMM kernel over a range of m (decode -> prefill "
                          "crossover), one JSON line per (shape, m, kernel)")
+    ap.add_argument("--only-w8a8", action="store_true",
+                    help="only the W8A8 figures of --workload (per-token activation quantization + "
+                         "W8A8 GEMM, --steps launches after --warmup), one JSON line (for profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB (fp16 negate, 5 launches) so "
                          "that HBM counters can be scaled against a kernel of known traffic")
@@ -304,6 +396,9 @@ def main():
 
     import int8_weight_quantized_amd as qw
     wl = synthetic.BY_NAME[args.workload]
+    if args.only_w8a8:
+        print(json.dumps(time_w8a8(wl, launches=args.steps, warmup=args.warmup)), flush=True)
+        return
     per_set = quant_bytes(wl.n, wl.k) + gemm_bytes(wl.m, wl.n, wl.k)
     sets = rotation_count(per_set)
     runner = StepRunner(wl, sets, with_weights=True)
@@ -349,6 +444,12 @@ def main():
             del r
             torch.cuda.empty_cache()
 
+    w8a8 = []
+    if not args.no_secondary and not args.only_step:
+        for name in ("small_batch_m8_k4096_n4608", "chatglm2_prefill_m512_k4096_n27392",
+                     "transformer_big_ffn_outliers_m4096_k1024_n4096"):
+            w8a8.append(time_w8a8(synthetic.BY_NAME[name]))
+
     result = {
         "metric": METRIC,
         "value": value,
@@ -368,6 +469,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "gemm_cold": secondary,
+        "w8a8_cold": w8a8,
     }
     if not args.no_cpu_baseline and not args.only_step:
         result["cpu_baseline"] = cpu_baseline(wl)

@@ -56,6 +56,9 @@ typedef enum qw_status {
 
 /* Largest row length the quantizer accepts (a row is held in registers). */
 #define QW_QUANTIZE_MAX_K 65536
+/* Longest reduction qw_w8a8_gemm accepts: the int32 accumulator holds
+ * k * 127 * 127 without overflow for k <= 2^17. */
+#define QW_W8A8_MAX_K 131072
 
 /*
  * qw_quantize_weights -- per-output-channel symmetric int8 quantization.
@@ -223,7 +226,8 @@ QW_API int qw_w8a16_gemm_mfma_tile(int64_t m, int64_t n, int64_t k);
  *   q       int8 [n][k] weight codes (as written by qw_quantize_weights)
  *   scales  fp16 bits [n]
  *   y       fp16 bits [m][n] (written)
- *   m, n, k as qw_w8a16_gemm (k % 16 == 0; m == 0 or n == 0 is a no-op)
+ *   m, n    as qw_w8a16_gemm (m == 0 or n == 0 is a no-op)
+ *   k       16 <= k <= QW_W8A8_MAX_K, k % 16 == 0
  *   stream  hipStream_t
  *
  * One kernel for every m: the LDS-tiled MFMA GEMM on
@@ -232,8 +236,8 @@ QW_API int qw_w8a16_gemm_mfma_tile(int64_t m, int64_t n, int64_t k);
  *
  * Errors: QW_ERROR_INVALID_VALUE (null pointer with m, n > 0, negative
  * size, k <= 0, y overlapping qx, sx, q or scales), QW_ERROR_UNSUPPORTED
- * (k % 16 != 0, a size beyond INT32_MAX), QW_ERROR_MISALIGNED,
- * QW_ERROR_LAUNCH.
+ * (k % 16 != 0, k > QW_W8A8_MAX_K, m or n beyond INT32_MAX),
+ * QW_ERROR_MISALIGNED, QW_ERROR_LAUNCH.
  */
 QW_API qw_status qw_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t *q,
                               const uint16_t *scales, uint16_t *y, int64_t m, int64_t n,

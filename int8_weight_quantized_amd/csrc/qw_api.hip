@@ -217,7 +217,7 @@ QW_API qw_status qw_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t
         return QW_SUCCESS;
     if (!qx || !sx || !q || !scales || !y)
         return QW_ERROR_INVALID_VALUE;
-    if (k % 16 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim)
+    if (k % 16 != 0 || m > kMaxDim || n > kMaxDim || k > QW_W8A8_MAX_K)
         return QW_ERROR_UNSUPPORTED;
     if (misaligned(qx) || misaligned(sx) || misaligned(q) || misaligned(scales) || misaligned(y))
         return QW_ERROR_MISALIGNED;
@@ -230,7 +230,7 @@ QW_API qw_status qw_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t
 
 QW_API int qw_w8a8_gemm_mfma_tile(int64_t m, int64_t n, int64_t k)
 {
-    if (m <= 0 || n <= 0 || k <= 0 || k % 16 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim)
+    if (m <= 0 || n <= 0 || k <= 0 || k % 16 != 0 || m > kMaxDim || n > kMaxDim || k > QW_W8A8_MAX_K)
         return -1;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)

@@ -158,6 +158,7 @@ E = 5 << 20
     ((A, B, C, D, 0, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),
     ((A, B, C, D, E, 1, 4, 24), qw.QW_ERROR_UNSUPPORTED),
     ((A, B, C, D, E, 1 << 31, 4, 16), qw.QW_ERROR_UNSUPPORTED),
+    ((A, B, C, D, E, 1, 4, 131072 + 16), qw.QW_ERROR_UNSUPPORTED),  # int32 accumulator limit
     ((A + 1, B, C, D, E, 1, 4, 16), qw.QW_ERROR_MISALIGNED),
     ((A, B + 2, C, D, E, 1, 4, 16), qw.QW_ERROR_MISALIGNED),
     ((A, B, C + 8, D, E, 1, 4, 16), qw.QW_ERROR_MISALIGNED),

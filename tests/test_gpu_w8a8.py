@@ -113,6 +113,28 @@ def test_w8a8_exact_arithmetic_bitexact(m, n, k):
     assert np.array_equal(y.view(np.uint16), want)
 
 
+def test_w8a8_longest_k_saturated():
+    """k at the documented maximum with saturated codes: |acc| = k * 127^2 =
+    2^17 * 16129 sits just below 2^31, so the int32 accumulator must not
+    wrap; 16129 * 2^17 is exact in binary32, so Y is bit-exact."""
+    import int8_weight_quantized_amd as qw
+    k = 131072
+    rng = np.random.default_rng(17)
+    qx = np.empty((3, k), dtype=np.int8)
+    qx[0], qx[1] = 127, -127
+    qx[2] = rng.integers(-127, 128, size=k)
+    q = np.empty((4, k), dtype=np.int8)
+    q[0], q[1] = 127, -127
+    q[2:] = rng.integers(-127, 128, size=(2, k))
+    sx = np.full(3, np.float16(2.0 ** -8)).view(np.uint16)
+    s = np.full(4, np.float16(2.0 ** -9)).view(np.uint16)
+    say("w8a8 longest k m=3 n=4 k=%d" % k)
+    y = gpu_w8a8(qx, sx, q, s)
+    want = oracle.f64_to_f16_bits(oracle.w8a8_gemm(qx, sx, q, s))
+    assert np.array_equal(y.view(np.uint16), want)
+    assert qw.w8a8_gemm_raw(1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20, 1, 4, k + 16) == qw.QW_ERROR_UNSUPPORTED
+
+
 def test_w8a8_zero_codes_and_zero_scales():
     m, n, k = 70, 300, 272
     qx, sx, q, s = _codes(m, n, k, seed=5)
