@@ -72,6 +72,8 @@ def _declare(lib):
     lib.oracle_quantize.restype = ctypes.c_int
     lib.oracle_gemm.argtypes = [u16p, i8p, u16p, i64, i64, i64, f64p]
     lib.oracle_gemm_sampled.argtypes = [u16p, i8p, u16p, i64, i64p, i64p, i64, f64p]
+    lib.oracle_quantize_fixed.argtypes = [f32p, i64, i64, f32p, i8p, u16p]
+    lib.oracle_quantize_fixed.restype = ctypes.c_int
     lib.oracle_w8a8_gemm.argtypes = [i8p, u16p, i8p, u16p, i64, i64, i64, f64p]
     lib.oracle_w8a8_gemm_sampled.argtypes = [i8p, u16p, i8p, u16p, i64, i64p, i64p, i64, f64p]
     lib.oracle_num_threads.restype = ctypes.c_int
@@ -145,6 +147,22 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_quantize rejected its arguments (rc=%d)" % rc)
         return q, s, t
+
+    def quantize_fixed(self, w, bounds):
+        """Per-row quantization with given bounds (fixed-range clip):
+        returns (q int8 [n,k], scale bits uint16 [n])."""
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        b = np.ascontiguousarray(bounds, dtype=np.float32)
+        n, k = w.shape
+        if b.shape != (n,):
+            raise ValueError("bounds must be [n]")
+        q = np.empty((n, k), dtype=np.int8)
+        s = np.empty((n,), dtype=np.uint16)
+        rc = self._l.oracle_quantize_fixed(_ptr(w, ctypes.c_float), n, k, _ptr(b, ctypes.c_float),
+                                           _ptr(q, ctypes.c_int8), _ptr(s, ctypes.c_uint16))
+        if rc != 0:
+            raise ValueError("oracle_quantize_fixed rejected its arguments (rc=%d)" % rc)
+        return q, s
 
     def gemm(self, x_f16, q, s_bits) -> np.ndarray:
         """Binary64 reference ref[m, n] = sum_k x[m,k] * q[n,k] * S[n]."""
@@ -230,6 +248,10 @@ def default() -> Oracle:
 
 def quantize(w, pct: float = 100.0):
     return default().quantize(w, pct)
+
+
+def quantize_fixed(w, bounds):
+    return default().quantize_fixed(w, bounds)
 
 
 def gemm(x_f16, q, s_bits):

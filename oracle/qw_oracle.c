@@ -228,7 +228,34 @@ double oracle_row_percentile(const float *row, int64_t k, double pct, float *scr
 /* Quantizer                                                                */
 /* ------------------------------------------------------------------------ */
 
-/* Quantize W[n][k] (row-major binary32) per output row.
+/* Scale and codes of one row for the bound t (a2 and a3): S is the binary16
+ * rounding of the binary32 quotient t / 127, and each code is the
+ * round-half-even of the binary32 quotient w / S clamped to [-127, 127]
+ * (LightSeq slide deck, slide "量化：裁剪+对称", symmetric formula with
+ * n = 8 bits).  Returns S's bit pattern. */
+static uint16_t quantize_row_with_bound(const float *row, int64_t k, float t, int8_t *qrow)
+{
+    float s32 = t / 127.0f;
+    uint16_t s16 = oracle_f32_to_f16(s32);
+    float s = oracle_f16_to_f32(s16);
+    for (int64_t j = 0; j < k; ++j) {
+        if (s == 0.0f) {
+            qrow[j] = 0;
+            continue;
+        }
+        float ratio = row[j] / s;       /* binary32 IEEE division */
+        float rounded = rintf(ratio);  /* default mode: nearest, ties to even */
+        if (rounded > 127.0f)
+            rounded = 127.0f;
+        if (rounded < -127.0f)
+            rounded = -127.0f;
+        qrow[j] = (int8_t)rounded;
+    }
+    return s16;
+}
+
+/* Quantize W[n][k] (row-major binary32) per output row, with the bound
+ * taken from the row's data (its absmax, or the pct-th percentile of |w|).
  *   q       [n][k] int8 codes (out)
  *   scales  [n] binary16 bit patterns (out)
  *   thresh  [n] binary32 clip bound t (out, may be NULL)
@@ -256,30 +283,35 @@ int oracle_quantize(const float *w, int64_t n, int64_t k, double pct,
             const float *row = w + r * k;
             double t64 = oracle_row_percentile(row, k, pct, scratch);
             float t = (float)t64;
-            float s32 = t / 127.0f;
-            uint16_t s16 = oracle_f32_to_f16(s32);
-            float s = oracle_f16_to_f32(s16);
-            scales[r] = s16;
+            scales[r] = quantize_row_with_bound(row, k, t, q + r * k);
             if (thresh)
                 thresh[r] = t;
-            int8_t *qrow = q + r * k;
-            for (int64_t j = 0; j < k; ++j) {
-                if (s == 0.0f) {
-                    qrow[j] = 0;
-                    continue;
-                }
-                float ratio = row[j] / s;       /* binary32 IEEE division */
-                float rounded = rintf(ratio);  /* default mode: nearest, ties to even */
-                if (rounded > 127.0f)
-                    rounded = 127.0f;
-                if (rounded < -127.0f)
-                    rounded = -127.0f;
-                qrow[j] = (int8_t)rounded;
-            }
         }
         free(scratch);
     }
     return bad ? -1 : 0;
+}
+
+/* Fixed-range clip: the bound of row r is given (bounds[r], finite and
+ * >= 0, e.g. a range fixed during training) instead of being measured on
+ * the row; the scale and codes then follow exactly as above.  Source:
+ * LightSeq slide deck, slide "量化流程" (fixed range clip next to the
+ * percentage clip).  Returns 0, or -1 for invalid arguments. */
+int oracle_quantize_fixed(const float *w, int64_t n, int64_t k, const float *bounds,
+                          int8_t *q, uint16_t *scales)
+{
+    if (n < 0 || k <= 0)
+        return -1;
+    for (int64_t i = 0; i < n * k; ++i)
+        if (!isfinite(w[i]))
+            return -1;
+    for (int64_t r = 0; r < n; ++r)
+        if (!isfinite(bounds[r]) || bounds[r] < 0.0f)
+            return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r)
+        scales[r] = quantize_row_with_bound(w + r * k, k, bounds[r], q + r * k);
+    return 0;
 }
 
 /* ------------------------------------------------------------------------ */

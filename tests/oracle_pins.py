@@ -427,6 +427,48 @@ def pin_cosine_vs_unquantized(o):
 
 
 # --------------------------------------------------------------------------
+# fixed-range clip
+# --------------------------------------------------------------------------
+
+def pin_fixed_range_bruteforce(o, seed=15):
+    """Given bounds (below, at and above the row's absmax, and zero): the
+    scale is the binary16 nearest to the binary32 nearest to t/127 and every
+    code is the clamped round-half-even of the binary32 quotient, checked
+    with exact rationals; elements beyond the bound saturate with their
+    sign."""
+    rng = np.random.default_rng(seed)
+    for trial in range(40):
+        n = int(rng.integers(1, 5))
+        k = int(rng.integers(1, 20))
+        w = (rng.standard_normal((n, k)) * 10.0 ** rng.integers(-3, 2)).astype(np.float32)
+        amax = np.abs(w).max(axis=1)
+        factor = rng.choice([0.0, 0.3, 0.8, 1.0, 1.7], size=n)
+        bounds = (amax * factor).astype(np.float32)
+        q, sb = o.quantize_fixed(w, bounds)
+        check_scale_rows(bounds, sb)
+        check_quant_elements(w, q, sb)
+        s = f16_from_bits(sb).astype(np.float64)
+        for r in range(n):
+            if s[r] == 0:
+                assert np.all(q[r] == 0)
+                continue
+            big = np.abs(w[r].astype(np.float64)) >= 127.5 * s[r]
+            assert np.all(np.abs(q[r][big]) == 127)
+            assert np.all(np.sign(q[r][big]) == np.sign(w[r][big]))
+
+
+def pin_fixed_range_of_measured_bound(o, seed=16):
+    """With each row's own measured bound (absmax or percentile) passed as
+    the fixed range, the result equals the data-driven quantizer's."""
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((9, 300)) * 0.02).astype(np.float32)
+    for pct in (100.0, 99.0, 75.0):
+        q, s, t = o.quantize(w, pct)
+        qf, sf = o.quantize_fixed(w, t)
+        assert np.array_equal(q, qf) and np.array_equal(s, sf)
+
+
+# --------------------------------------------------------------------------
 # W8A8 matmul reference
 # --------------------------------------------------------------------------
 
@@ -505,6 +547,8 @@ FAST_PINS = (
     pin_gemm_bruteforce,
     pin_gemm_zero_and_scaling,
     pin_cosine_vs_unquantized,
+    pin_fixed_range_bruteforce,
+    pin_fixed_range_of_measured_bound,
     pin_w8a8_unit_scales_is_integer_matmul,
     pin_w8a8_equals_w8a16_on_exact_activations,
     pin_w8a8_scaling_and_symmetry,

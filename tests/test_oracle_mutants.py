@@ -23,8 +23,11 @@ MUTANTS = {
     # quantize with the unrounded binary32 scale
     "fp32_scale_for_codes": ("float ratio = row[j] / s; ", "float ratio = row[j] / s32; "),
     # clamp range +-128 on the negative side
-    "clamp_minus_128": ("if (rounded < -127.0f)\n                    rounded = -127.0f;",
-                        "if (rounded < -128.0f)\n                    rounded = -128.0f;"),
+    "clamp_minus_128": ("if (rounded < -127.0f)\n            rounded = -127.0f;",
+                        "if (rounded < -128.0f)\n            rounded = -128.0f;"),
+    # fixed-range clip: bound taken as the row absmax instead of the given one
+    "fixed_range_ignores_bound": ("scales[r] = quantize_row_with_bound(w + r * k, k, bounds[r], q + r * k);",
+                                  "scales[r] = quantize_row_with_bound(w + r * k, k, (float)oracle_row_percentile(w + r * k, 1, 100.0, (float[1]){0}), q + r * k);"),
     # wrong bound divisor
     "divide_by_128": ("float s32 = t / 127.0f;", "float s32 = t / 128.0f;"),
     # percentile: wrong rank (ceil) and dropped interpolation term

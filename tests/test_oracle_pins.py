@@ -29,3 +29,10 @@ def test_quantize_rejects_bad_arguments(orc):
     bad[1, 2] = np.inf
     with pytest.raises(ValueError):
         orc.quantize(bad, 100.0)
+
+
+def test_quantize_fixed_rejects_bad_bounds(orc):
+    w = np.ones((2, 4), dtype=np.float32)
+    for b in ([1.0, -1.0], [1.0, np.inf], [np.nan, 1.0]):
+        with pytest.raises(ValueError):
+            orc.quantize_fixed(w, np.float32(b))
