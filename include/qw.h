@@ -121,6 +121,33 @@ QW_API qw_status qw_quantize_weights_f16(const uint16_t *w, int64_t n, int64_t k
                                          uint16_t *scales, void *stream);
 
 /*
+ * qw_quantize_weights_fixed_range -- the quantizer with each row's clip
+ * bound given instead of measured (fixed-range clip).
+ *
+ * Source: LightSeq slide deck ("LightSeq：高性能NLP序列推理实践"), slide
+ * 量化流程: a fixed range clip beside the percentage clip, both followed by
+ * the symmetric quantization of slide 量化：裁剪+对称.  The bound of row r
+ * is bounds[r] (for example a range fixed during quantization-aware
+ * training); scale and codes then follow qw_quantize_weights exactly:
+ *
+ *   S[r] = binary16_RNE( binary32(bounds[r] / 127) )
+ *   q[r][c] = clamp( round_half_even( binary32(w[r][c] / S[r]) ), -127, 127 )
+ *   (q = 0 when S[r] == 0)
+ *
+ *   w       fp32 [n][k], read only
+ *   bounds  fp32 [n], read only; each finite and >= 0 (other values give
+ *           unspecified codes and scales; they are not checked on the host)
+ *   q, scales, n, k, stream as qw_quantize_weights
+ *
+ * Errors: as qw_quantize_weights (no percentile argument), plus
+ * QW_ERROR_INVALID_VALUE for a null bounds pointer or q or scales
+ * overlapping bounds, and QW_ERROR_MISALIGNED for a misaligned bounds.
+ */
+QW_API qw_status qw_quantize_weights_fixed_range(const float *w, int64_t n, int64_t k,
+                                                 const float *bounds, int8_t *q,
+                                                 uint16_t *scales, void *stream);
+
+/*
  * qw_w8a16_gemm -- Y = X * dequant(Q)^T with per-channel fp16 scales.
  *
  * Source: ChatGLM2/BM1684X page, section 4 (后端性能提升原理): load, cast

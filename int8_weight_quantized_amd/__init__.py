@@ -70,6 +70,8 @@ def _load():
     lib.qw_quantize_weights.restype = ctypes.c_int
     lib.qw_quantize_weights_f16.argtypes = [vp, i64, i64, ctypes.c_double, vp, vp, vp]
     lib.qw_quantize_weights_f16.restype = ctypes.c_int
+    lib.qw_quantize_weights_fixed_range.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+    lib.qw_quantize_weights_fixed_range.restype = ctypes.c_int
     lib.qw_w8a8_gemm.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.qw_w8a8_gemm.restype = ctypes.c_int
     lib.qw_w8a8_gemm_mfma_tile.argtypes = [i64, i64, i64]
@@ -144,6 +146,11 @@ def quantize_weights_raw(w_ptr: int, n: int, k: int, clip_percentile: float,
 def quantize_weights_f16_raw(w_ptr: int, n: int, k: int, clip_percentile: float,
                              q_ptr: int, s_ptr: int, stream: int = 0) -> int:
     return int(library().qw_quantize_weights_f16(w_ptr, n, k, float(clip_percentile), q_ptr, s_ptr, stream))
+
+
+def quantize_weights_fixed_range_raw(w_ptr: int, n: int, k: int, bounds_ptr: int, q_ptr: int, s_ptr: int,
+                                     stream: int = 0) -> int:
+    return int(library().qw_quantize_weights_fixed_range(w_ptr, n, k, bounds_ptr, q_ptr, s_ptr, stream))
 
 
 def w8a16_gemm_raw(x_ptr: int, q_ptr: int, s_ptr: int, y_ptr: int, m: int, n: int, k: int,
@@ -240,6 +247,28 @@ def w8a16_gemm(x, q, scales, out=None, path: str = "auto"):
     return y
 
 
+def quantize_weights_fixed_range(w, bounds, out=None):
+    """Per-row symmetric int8 quantization with given clip bounds: w cuda
+    float32 [N, K], bounds cuda float32 [N] (finite, >= 0).  Returns
+    (q int8 [N, K], scales float16 [N])."""
+    torch = _torch()
+    _check(w, "w", torch.float32, 2)
+    _check(bounds, "bounds", torch.float32, 1)
+    n, k = w.shape
+    if bounds.shape[0] != n:
+        raise ValueError("bounds must be [N]")
+    if out is None:
+        q = torch.empty((n, k), dtype=torch.int8, device=w.device)
+        s = torch.empty((n,), dtype=torch.float16, device=w.device)
+    else:
+        q, s = out
+    st = quantize_weights_fixed_range_raw(w.data_ptr(), n, k, bounds.data_ptr(), q.data_ptr(), s.data_ptr(),
+                                          _stream_of(w))
+    if st != QW_SUCCESS:
+        raise QwError(st, "qw_quantize_weights_fixed_range")
+    return q, s
+
+
 def quantize_activations(x, out=None):
     """Per-token (per-row) symmetric int8 quantization of fp16 activations
     [M, K] for W8A8: the weights' quantizer with the row absmax.  Returns
@@ -274,7 +303,7 @@ def w8a8_gemm(qx, sx, q, scales, out=None):
     return y
 
 
-__all__ = ["quantize_weights", "quantize_activations", "w8a16_gemm", "w8a8_gemm", "QwError",
+__all__ = ["quantize_weights", "quantize_weights_fixed_range", "quantize_activations", "w8a16_gemm", "w8a8_gemm", "QwError",
            "status_string", "version", "library", "auto_path", "mfma_tile", "w8a8_tile",
-           "quantize_weights_raw", "quantize_weights_f16_raw", "w8a16_gemm_raw", "w8a8_gemm_raw",
+           "quantize_weights_raw", "quantize_weights_f16_raw", "quantize_weights_fixed_range_raw", "w8a16_gemm_raw", "w8a8_gemm_raw",
            "PATHS", "LIBRARY_PATH"]

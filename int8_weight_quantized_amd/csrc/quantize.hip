@@ -242,11 +242,14 @@ __device__ __forceinline__ float4_t load4(const void *row, int idx)
     }
 }
 
-template <int THREADS, int VPT, bool PERCENTILE, bool F16>
+// MODE: 0 absmax bound, 1 percentile bound, 2 fixed range (the bound of
+// row r is bounds[r], given by the caller; no reduction).
+template <int THREADS, int VPT, int MODE, bool F16>
 __global__ __launch_bounds__(THREADS) void quantize_rows_kernel(
     const void *__restrict__ w, int k, int64_t rank_i, double frac_f,
-    int8_t *__restrict__ q, uint16_t *__restrict__ scales)
+    const float *__restrict__ bounds, int8_t *__restrict__ q, uint16_t *__restrict__ scales)
 {
+    constexpr bool PERCENTILE = MODE == 1;
     __shared__ QuantShared<THREADS> sh;
     const int64_t row = blockIdx.x;
     const int nvec = k >> 2;
@@ -267,7 +270,9 @@ __global__ __launch_bounds__(THREADS) void quantize_rows_kernel(
         v[j * 4 + 3] = f.w;
     }
     float t;
-    if (!PERCENTILE) {
+    if constexpr (MODE == 2) {
+        t = bounds[row];
+    } else if constexpr (!PERCENTILE) {
         uint32_t m = 0;
 #pragma unroll
         for (int e = 0; e < VPT * 4; ++e) {
@@ -357,31 +362,36 @@ __global__ __launch_bounds__(THREADS) void quantize_rows_kernel(
 
 template <int THREADS, int VPT, bool F16>
 hipError_t launch_typed(const void *w, int64_t n, int64_t k, int mode, int64_t rank_i, double frac_f,
-                        int8_t *q, uint16_t *scales, hipStream_t stream)
+                        const float *bounds, int8_t *q, uint16_t *scales, hipStream_t stream)
 {
     const dim3 grid((unsigned)n), block(THREADS);
     if (mode == 0)
-        hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, false, F16>), grid, block, 0, stream,
-                           w, (int)k, rank_i, frac_f, q, scales);
+        hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, 0, F16>), grid, block, 0, stream,
+                           w, (int)k, rank_i, frac_f, bounds, q, scales);
+    else if (mode == 1)
+        hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, 1, F16>), grid, block, 0, stream,
+                           w, (int)k, rank_i, frac_f, bounds, q, scales);
+    else if constexpr (!F16)
+        hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, 2, false>), grid, block, 0, stream,
+                           w, (int)k, rank_i, frac_f, bounds, q, scales);
     else
-        hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, true, F16>), grid, block, 0, stream,
-                           w, (int)k, rank_i, frac_f, q, scales);
+        return hipErrorInvalidValue; // fixed range is offered for fp32 weights only
     return hipGetLastError();
 }
 
 template <int THREADS, int VPT>
 hipError_t launch_cfg(const void *w, bool f16, int64_t n, int64_t k, int mode, int64_t rank_i,
-                      double frac_f, int8_t *q, uint16_t *scales, hipStream_t stream)
+                      double frac_f, const float *bounds, int8_t *q, uint16_t *scales, hipStream_t stream)
 {
-    return f16 ? launch_typed<THREADS, VPT, true>(w, n, k, mode, rank_i, frac_f, q, scales, stream)
-               : launch_typed<THREADS, VPT, false>(w, n, k, mode, rank_i, frac_f, q, scales, stream);
+    return f16 ? launch_typed<THREADS, VPT, true>(w, n, k, mode, rank_i, frac_f, bounds, q, scales, stream)
+               : launch_typed<THREADS, VPT, false>(w, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
 }
 
 } // namespace
 
 hipError_t launch_quantize(const void *w, bool w_is_f16, int64_t n, int64_t k, int mode,
-                           int64_t rank_i, double frac_f, int8_t *q, uint16_t *scales,
-                           hipStream_t stream)
+                           int64_t rank_i, double frac_f, const float *bounds, int8_t *q,
+                           uint16_t *scales, hipStream_t stream)
 {
     // float4 slots per row; a workgroup of THREADS holds THREADS * VPT of them.
     // Rows up to 1024 values get one wave each: every reduction is then a
@@ -389,24 +399,24 @@ hipError_t launch_quantize(const void *w, bool w_is_f16, int64_t n, int64_t k, i
     // percentile; no gain at 2048).
     const int64_t nvec = k / 4;
     if (nvec <= kWave * 1)
-        return launch_cfg<64, 1>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
+        return launch_cfg<64, 1>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
     if (nvec <= kWave * 2)
-        return launch_cfg<64, 2>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
+        return launch_cfg<64, 2>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
     if (nvec <= kWave * 4)
-        return launch_cfg<64, 4>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
+        return launch_cfg<64, 4>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
     if (nvec <= 256 * 1)
-        return launch_cfg<256, 1>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
+        return launch_cfg<256, 1>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
     if (nvec <= 256 * 2)
-        return launch_cfg<256, 2>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
+        return launch_cfg<256, 2>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
     if (nvec <= 256 * 4)
-        return launch_cfg<256, 4>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
+        return launch_cfg<256, 4>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
     if (nvec <= 256 * 8)
-        return launch_cfg<256, 8>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
+        return launch_cfg<256, 8>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
     if (nvec <= 256 * 16)
-        return launch_cfg<256, 16>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
+        return launch_cfg<256, 16>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
     if (nvec <= 1024 * 8)
-        return launch_cfg<1024, 8>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
-    return launch_cfg<1024, 16>(w, w_is_f16, n, k, mode, rank_i, frac_f, q, scales, stream);
+        return launch_cfg<1024, 8>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
+    return launch_cfg<1024, 16>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
 }
 
 } // namespace qw

@@ -137,8 +137,8 @@ qw_status quantize_common(const void *w, int wbytes, int64_t n, int64_t k, doubl
             frac_f = pos - i_floor;
         }
     }
-    return launch_status(qw::launch_quantize(w, wbytes == 2, n, k, mode, rank_i, frac_f, q, scales,
-                                             static_cast<hipStream_t>(stream)));
+    return launch_status(qw::launch_quantize(w, wbytes == 2, n, k, mode, rank_i, frac_f, nullptr, q,
+                                             scales, static_cast<hipStream_t>(stream)));
 }
 
 } // namespace
@@ -155,6 +155,29 @@ QW_API qw_status qw_quantize_weights_f16(const uint16_t *w, int64_t n, int64_t k
                                          int8_t *q, uint16_t *scales, void *stream)
 {
     return quantize_common(w, 2, n, k, clip_percentile, q, scales, stream);
+}
+
+QW_API qw_status qw_quantize_weights_fixed_range(const float *w, int64_t n, int64_t k,
+                                                 const float *bounds, int8_t *q, uint16_t *scales,
+                                                 void *stream)
+{
+    if (n < 0 || k <= 0)
+        return QW_ERROR_INVALID_VALUE;
+    if (n == 0)
+        return QW_SUCCESS;
+    if (!w || !bounds || !q || !scales)
+        return QW_ERROR_INVALID_VALUE;
+    if (k % 16 != 0 || k > QW_QUANTIZE_MAX_K || n > kMaxDim)
+        return QW_ERROR_UNSUPPORTED;
+    if (misaligned(w) || misaligned(bounds) || misaligned(q) || misaligned(scales))
+        return QW_ERROR_MISALIGNED;
+    const uint64_t elems = (uint64_t)n * (uint64_t)k;
+    if (overlaps(q, elems, w, elems * 4u) || overlaps(scales, (uint64_t)n * 2u, w, elems * 4u) ||
+        overlaps(scales, (uint64_t)n * 2u, q, elems) || overlaps(q, elems, bounds, (uint64_t)n * 4u) ||
+        overlaps(scales, (uint64_t)n * 2u, bounds, (uint64_t)n * 4u))
+        return QW_ERROR_INVALID_VALUE;
+    return launch_status(qw::launch_quantize(w, false, n, k, 2, 0, 0.0, bounds, q, scales,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 QW_API qw_status qw_w8a16_gemm_path(const uint16_t *x, const int8_t *q, const uint16_t *scales,

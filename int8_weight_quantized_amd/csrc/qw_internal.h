@@ -12,10 +12,11 @@ namespace qw {
 // Per-row quantizer of fp32 (w_is_f16 false) or fp16 weights.  mode 0:
 // absmax bound; mode 1: percentile bound with the rank i (0-based,
 // ascending) and interpolation fraction f computed on the host in binary64
-// (i < k - 1 in mode 1).
+// (i < k - 1 in mode 1); mode 2 (fp32 weights only): the bound of row r is
+// bounds[r] (device pointer, unused in the other modes).
 hipError_t launch_quantize(const void *w, bool w_is_f16, int64_t n, int64_t k, int mode,
-                           int64_t rank_i, double frac_f, int8_t *q, uint16_t *scales,
-                           hipStream_t stream);
+                           int64_t rank_i, double frac_f, const float *bounds, int8_t *q,
+                           uint16_t *scales, hipStream_t stream);
 
 // Decode GEMV (VALU dot products).  Requires m <= 8 and
 // m * ceil(k / 1024) <= 32 (the activations fit the LDS budget).

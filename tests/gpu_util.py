@@ -50,6 +50,22 @@ def gpu_quantize(w: np.ndarray, pct: float):
     return host(qd), host(sd).view(np.uint16)
 
 
+def gpu_quantize_fixed(w: np.ndarray, bounds: np.ndarray):
+    """Fixed-range quantization on the GPU through the C ABI; returns
+    (q int8, scale bits uint16)."""
+    import int8_weight_quantized_amd as qw
+    torch = torch_mod()
+    n, k = w.shape
+    wd = dev(np.ascontiguousarray(w, dtype=np.float32))
+    bd = dev(np.ascontiguousarray(bounds, dtype=np.float32))
+    qd = torch.full((n, k), 99, dtype=torch.int8, device="cuda:0")
+    sd = torch.full((n,), 0x5555, dtype=torch.int16, device="cuda:0")
+    st = qw.quantize_weights_fixed_range_raw(wd.data_ptr(), n, k, bd.data_ptr(), qd.data_ptr(), sd.data_ptr(),
+                                             int(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, qw.status_string(st)
+    return host(qd), host(sd).view(np.uint16)
+
+
 def gpu_gemm(x: np.ndarray, q: np.ndarray, s_bits: np.ndarray, path: int = 0):
     """W8A16 GEMM on the GPU through the C ABI; returns Y as float16."""
     import int8_weight_quantized_amd as qw

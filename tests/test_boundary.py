@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     decl = _declared_functions()
     for name in ("qw_quantize_weights", "qw_quantize_weights_f16", "qw_w8a16_gemm", "qw_w8a16_gemm_path",
                  "qw_w8a16_gemm_auto_path", "qw_w8a16_gemm_mfma_tile", "qw_w8a8_gemm",
-                 "qw_w8a8_gemm_mfma_tile", "qw_status_string", "qw_version"):
+                 "qw_w8a8_gemm_mfma_tile", "qw_quantize_weights_fixed_range", "qw_status_string",
+                 "qw_version"):
         assert name in decl
 
 
@@ -114,6 +115,21 @@ def test_quantize_rejects(args, status):
 ])
 def test_quantize_f16_rejects(args, status):
     assert qw.quantize_weights_f16_raw(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, -1, 16, D, B, C), qw.QW_ERROR_INVALID_VALUE),              # n < 0
+    ((A, 4, 0, D, B, C), qw.QW_ERROR_INVALID_VALUE),                # k == 0
+    ((A, 4, 16, 0, B, C), qw.QW_ERROR_INVALID_VALUE),               # null bounds
+    ((0, 4, 16, D, B, C), qw.QW_ERROR_INVALID_VALUE),               # null w
+    ((A, 4, 24, D, B, C), qw.QW_ERROR_UNSUPPORTED),                 # k % 16
+    ((A, 4, 16, D + 4, B, C), qw.QW_ERROR_MISALIGNED),              # bounds
+    ((A, 4, 16, D, B, D), qw.QW_ERROR_INVALID_VALUE),               # scales overlap bounds
+    ((A, 4, 16, D, D, C), qw.QW_ERROR_INVALID_VALUE),               # q overlaps bounds
+    ((A, 4, 16, D, A + 128, C), qw.QW_ERROR_INVALID_VALUE),         # q inside w (4 x 16 fp32)
+])
+def test_quantize_fixed_range_rejects(args, status):
+    assert qw.quantize_weights_fixed_range_raw(*args) == status
 
 
 def test_quantize_empty_is_noop():

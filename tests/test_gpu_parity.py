@@ -314,6 +314,34 @@ def test_quantize_f16_input(n, k, pct):
     assert np.array_equal(q, q_ref), "codes differ at %s" % np.argwhere(q != q_ref)[:5]
 
 
+@pytest.mark.parametrize("n,k", [(64, 16), (37, 1040), (300, 1024), (96, 4096), (17, 4112), (5, 65536)])
+def test_quantize_fixed_range(n, k):
+    """Given per-row bounds (zero, below, at and above the absmax): codes
+    and scales bit-identical to the oracle's fixed-range quantizer."""
+    from gpu_util import gpu_quantize_fixed
+    rng = np.random.default_rng(n + k)
+    w = synthetic.random_w(n, k, n * 7 + k)
+    amax = np.abs(w).max(axis=1)
+    bounds = (amax * rng.choice([0.0, 0.25, 0.9, 1.0, 3.0], size=n)).astype(np.float32)
+    bounds[0] = 0.0
+    say("quantize fixed range n=%d k=%d" % (n, k))
+    q_ref, s_ref = oracle.quantize_fixed(w, bounds)
+    q, s = gpu_quantize_fixed(w, bounds)
+    assert np.array_equal(s, s_ref), "scales differ at rows %s" % np.nonzero(s != s_ref)[0][:5]
+    assert np.array_equal(q, q_ref), "codes differ at %s" % np.argwhere(q != q_ref)[:5]
+
+
+def test_quantize_fixed_range_of_workload_bounds():
+    """The outlier workload's own 99.99th-percentile bounds passed as fixed
+    ranges give exactly the percentile quantizer's codes."""
+    from gpu_util import gpu_quantize_fixed
+    wl, x, w, q_ref, s_ref = workload_data("transformer_big_ffn_outliers_m4096_k1024_n4096")
+    _, _, t = oracle.quantize(w, wl.clip_percentile)
+    say("quantize fixed range of workload bounds n=%d k=%d" % (wl.n, wl.k))
+    q, s = gpu_quantize_fixed(w, t)
+    assert np.array_equal(s, s_ref) and np.array_equal(q, q_ref)
+
+
 def test_quantize_deterministic():
     wl, x, w, q, s = workload_data("transformer_big_ffn_outliers_m4096_k1024_n4096")
     say("quantize determinism")
