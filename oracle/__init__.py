@@ -72,6 +72,10 @@ def _declare(lib):
     lib.oracle_quantize.restype = ctypes.c_int
     lib.oracle_gemm.argtypes = [u16p, i8p, u16p, i64, i64, i64, f64p]
     lib.oracle_gemm_sampled.argtypes = [u16p, i8p, u16p, i64, i64p, i64p, i64, f64p]
+    lib.oracle_quantize_asym.argtypes = [f32p, i64, i64, i8p, u16p, i8p]
+    lib.oracle_quantize_asym.restype = ctypes.c_int
+    lib.oracle_gemm_asym.argtypes = [u16p, i8p, u16p, i8p, i64, i64, i64, f64p]
+    lib.oracle_gemm_asym_sampled.argtypes = [u16p, i8p, u16p, i8p, i64, i64p, i64p, i64, f64p]
     lib.oracle_quantize_fixed.argtypes = [f32p, i64, i64, f32p, i8p, u16p]
     lib.oracle_quantize_fixed.restype = ctypes.c_int
     lib.oracle_w8a8_gemm.argtypes = [i8p, u16p, i8p, u16p, i64, i64, i64, f64p]
@@ -164,6 +168,54 @@ class Oracle:
             raise ValueError("oracle_quantize_fixed rejected its arguments (rc=%d)" % rc)
         return q, s
 
+    def quantize_asym(self, w):
+        """Asymmetric per-row quantization: returns (q int8 [n,k], scale bits
+        uint16 [n], zero points int8 [n])."""
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        n, k = w.shape
+        q = np.empty((n, k), dtype=np.int8)
+        s = np.empty((n,), dtype=np.uint16)
+        z = np.empty((n,), dtype=np.int8)
+        rc = self._l.oracle_quantize_asym(_ptr(w, ctypes.c_float), n, k, _ptr(q, ctypes.c_int8),
+                                          _ptr(s, ctypes.c_uint16), _ptr(z, ctypes.c_int8))
+        if rc != 0:
+            raise ValueError("oracle_quantize_asym rejected its arguments (rc=%d)" % rc)
+        return q, s, z
+
+    def gemm_asym(self, x_f16, q, s_bits, zeros) -> np.ndarray:
+        """Binary64 reference ref[m, n] = sum_k x[m,k] * (q[n,k] - z[n]) * S[n]."""
+        x = np.ascontiguousarray(np.asarray(x_f16, dtype=np.float16)).view(np.uint16)
+        q = np.ascontiguousarray(q, dtype=np.int8)
+        s = np.ascontiguousarray(s_bits, dtype=np.uint16)
+        z = np.ascontiguousarray(zeros, dtype=np.int8)
+        m, k = x.shape
+        n = q.shape[0]
+        if q.shape != (n, k) or s.shape != (n,) or z.shape != (n,):
+            raise ValueError("shape mismatch")
+        ref = np.empty((m, n), dtype=np.float64)
+        self._l.oracle_gemm_asym(_ptr(x, ctypes.c_uint16), _ptr(q, ctypes.c_int8), _ptr(s, ctypes.c_uint16),
+                                 _ptr(z, ctypes.c_int8), m, n, k, _ptr(ref, ctypes.c_double))
+        return ref
+
+    def gemm_asym_sampled(self, x_f16, q, s_bits, zeros, mi, ni) -> np.ndarray:
+        x = np.ascontiguousarray(np.asarray(x_f16, dtype=np.float16)).view(np.uint16)
+        q = np.ascontiguousarray(q, dtype=np.int8)
+        s = np.ascontiguousarray(s_bits, dtype=np.uint16)
+        z = np.ascontiguousarray(zeros, dtype=np.int8)
+        mi = np.ascontiguousarray(mi, dtype=np.int64)
+        ni = np.ascontiguousarray(ni, dtype=np.int64)
+        k = x.shape[1]
+        if q.shape[1] != k or mi.shape != ni.shape or z.shape != (q.shape[0],):
+            raise ValueError("shape mismatch")
+        if mi.size and (mi.min() < 0 or mi.max() >= x.shape[0] or ni.min() < 0 or ni.max() >= q.shape[0]):
+            raise IndexError("sample index out of range")
+        out = np.empty(mi.shape, dtype=np.float64)
+        self._l.oracle_gemm_asym_sampled(_ptr(x, ctypes.c_uint16), _ptr(q, ctypes.c_int8),
+                                         _ptr(s, ctypes.c_uint16), _ptr(z, ctypes.c_int8), k,
+                                         _ptr(mi, ctypes.c_int64), _ptr(ni, ctypes.c_int64), mi.size,
+                                         _ptr(out, ctypes.c_double))
+        return out
+
     def gemm(self, x_f16, q, s_bits) -> np.ndarray:
         """Binary64 reference ref[m, n] = sum_k x[m,k] * q[n,k] * S[n]."""
         x = np.ascontiguousarray(np.asarray(x_f16, dtype=np.float16)).view(np.uint16)
@@ -252,6 +304,18 @@ def quantize(w, pct: float = 100.0):
 
 def quantize_fixed(w, bounds):
     return default().quantize_fixed(w, bounds)
+
+
+def quantize_asym(w):
+    return default().quantize_asym(w)
+
+
+def gemm_asym(x_f16, q, s_bits, zeros):
+    return default().gemm_asym(x_f16, q, s_bits, zeros)
+
+
+def gemm_asym_sampled(x_f16, q, s_bits, zeros, mi, ni):
+    return default().gemm_asym_sampled(x_f16, q, s_bits, zeros, mi, ni)
 
 
 def gemm(x_f16, q, s_bits):

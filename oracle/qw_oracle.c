@@ -314,18 +314,80 @@ int oracle_quantize_fixed(const float *w, int64_t n, int64_t k, const float *bou
     return 0;
 }
 
+/* Asymmetric (zero-point) quantization of W[n][k], 8 bits stored as int8.
+ * Source: LightSeq slide deck, slide "量化：裁剪+对称" (asymmetric case: the
+ * range [min, max] is spread over the 2^n - 1 steps with scale S and a zero
+ * point z, and a product of two such values expands into the code product
+ * plus zero-point cross terms).  Per row:
+ *   hi = max(0, max w), lo = min(0, min w)   (the range holds 0, so 0 is
+ *                                             exactly representable)
+ *   S  = binary16_RNE( binary32( binary32(hi - lo) / 255 ) )
+ *   z  = clamp( round_half_even( binary32(-lo / S) ) - 128, -128, 127 )
+ *   q  = clamp( round_half_even( binary32(w / S) ) + z, -128, 127 )
+ *   (S == 0: z = 0 and q = 0)
+ * so that w ~ S * (q - z), w = 0 maps to code z and lo to code -128.
+ * Returns 0, or -1 for invalid arguments (non-finite input included). */
+int oracle_quantize_asym(const float *w, int64_t n, int64_t k, int8_t *q, uint16_t *scales,
+                         int8_t *zeros)
+{
+    if (n < 0 || k <= 0)
+        return -1;
+    for (int64_t i = 0; i < n * k; ++i)
+        if (!isfinite(w[i]))
+            return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        const float *row = w + r * k;
+        int8_t *qrow = q + r * k;
+        float hi = 0.0f, lo = 0.0f;
+        for (int64_t j = 0; j < k; ++j) {
+            if (row[j] > hi)
+                hi = row[j];
+            if (row[j] < lo)
+                lo = row[j];
+        }
+        float range = hi - lo;
+        float s32 = range / 255.0f;
+        uint16_t s16 = oracle_f32_to_f16(s32);
+        float s = oracle_f16_to_f32(s16);
+        scales[r] = s16;
+        if (s == 0.0f) {
+            zeros[r] = 0;
+            for (int64_t j = 0; j < k; ++j)
+                qrow[j] = 0;
+            continue;
+        }
+        float zf = rintf(-lo / s) - 128.0f;
+        if (zf > 127.0f)
+            zf = 127.0f;
+        if (zf < -128.0f)
+            zf = -128.0f;
+        zeros[r] = (int8_t)zf;
+        for (int64_t j = 0; j < k; ++j) {
+            float c = rintf(row[j] / s) + zf;
+            if (c > 127.0f)
+                c = 127.0f;
+            if (c < -128.0f)
+                c = -128.0f;
+            qrow[j] = (int8_t)c;
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* W8A16 matmul reference                                                   */
 /* ------------------------------------------------------------------------ */
 
-/* One output: sum_k x[m][k] * (q[n][k] * S[n]) in binary64.  x holds
- * binary16 bit patterns.  Every product is exact in binary64 (11 x 8 x 11
- * significant bits); only the K-term sum rounds. */
-static double dot_one(const uint16_t *xrow, const int8_t *qrow, double s, int64_t k)
+/* One output: sum_k x[m][k] * ((q[n][k] - z[n]) * S[n]) in binary64 (z = 0
+ * for the symmetric quantizer).  x holds binary16 bit patterns.  Every
+ * product is exact in binary64 (11 x 9 x 11 significant bits); only the
+ * K-term sum rounds. */
+static double dot_one(const uint16_t *xrow, const int8_t *qrow, double z, double s, int64_t k)
 {
     double acc = 0.0;
     for (int64_t j = 0; j < k; ++j) {
-        double wdeq = (double)qrow[j] * s;
+        double wdeq = ((double)qrow[j] - z) * s;
         double xv = (double)oracle_f16_to_f32(xrow[j]);
         acc += xv * wdeq;
     }
@@ -340,7 +402,7 @@ void oracle_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
 #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t i = 0; i < m; ++i)
         for (int64_t j = 0; j < n; ++j)
-            ref[i * n + j] = dot_one(x + i * k, q + j * k,
+            ref[i * n + j] = dot_one(x + i * k, q + j * k, 0.0,
                                      (double)oracle_f16_to_f32(scales[j]), k);
 }
 
@@ -351,8 +413,32 @@ void oracle_gemm_sampled(const uint16_t *x, const int8_t *q, const uint16_t *sca
 {
 #pragma omp parallel for schedule(static)
     for (int64_t c = 0; c < count; ++c)
-        out[c] = dot_one(x + mi[c] * k, q + ni[c] * k,
+        out[c] = dot_one(x + mi[c] * k, q + ni[c] * k, 0.0,
                          (double)oracle_f16_to_f32(scales[ni[c]]), k);
+}
+
+/* Asymmetric weights: ref[m][n] = sum_k x[m][k] * ((q[n][k] - z[n]) * S[n]),
+ * the dequantization S * (q - z) of the asymmetric slide. */
+void oracle_gemm_asym(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                      const int8_t *zeros, int64_t m, int64_t n, int64_t k, double *ref)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            const double zj = (double)zeros[j];
+            ref[i * n + j] = dot_one(x + i * k, q + j * k, zj, (double)oracle_f16_to_f32(scales[j]), k);
+        }
+}
+
+void oracle_gemm_asym_sampled(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                              const int8_t *zeros, int64_t k, const int64_t *mi, const int64_t *ni,
+                              int64_t count, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < count; ++c) {
+        const double zc = (double)zeros[ni[c]];
+        out[c] = dot_one(x + mi[c] * k, q + ni[c] * k, zc, (double)oracle_f16_to_f32(scales[ni[c]]), k);
+    }
 }
 
 /* ------------------------------------------------------------------------ */

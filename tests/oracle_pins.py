@@ -469,6 +469,107 @@ def pin_fixed_range_of_measured_bound(o, seed=16):
 
 
 # --------------------------------------------------------------------------
+# asymmetric (zero-point) quantizer and matmul
+# --------------------------------------------------------------------------
+
+def _asym_rows(rng, n, k):
+    w = (rng.standard_normal((n, k)) * 10.0 ** rng.integers(-3, 2)).astype(np.float32)
+    kind = rng.integers(0, 4)
+    if kind == 1:
+        w = np.abs(w)                       # all >= 0: lo = 0, z = -128
+    elif kind == 2:
+        w = -np.abs(w)                      # all <= 0: hi = 0
+    elif kind == 3:
+        w = (w + np.float32(3.0) * np.abs(w).max()).astype(np.float32)  # offset range
+    return w
+
+
+def pin_asym_quantize_bruteforce(o, seed=17):
+    """Exact rationals: the range [min(0, min w), max(0, max w)] in binary32,
+    S the binary16 nearest to the binary32 nearest to range/255, z the
+    half-even rounding of the binary32 quotient -lo/S shifted by -128, each
+    code the half-even rounding of the binary32 quotient w/S plus z, all
+    clamped to int8."""
+    rng = np.random.default_rng(seed)
+    for trial in range(50):
+        n = int(rng.integers(1, 4))
+        k = int(rng.integers(1, 20))
+        w = _asym_rows(rng, n, k)
+        if trial % 7 == 0:
+            w[0] = 0.0
+        if trial % 5 == 1:
+            # range 255/256 gives S = 2^-8 exactly; the other weights sit on
+            # exact ties (j + 1/2) * S of the quotient
+            ties = np.float32([0.5, -0.49609375, 2.5 / 256, -3.5 / 256, 4.5 / 256, 0.5 / 256, -0.5 / 256,
+                               6.5 / 256])
+            w = np.tile(ties, (n, 1))
+            k = w.shape[1]
+        q, sb, z = o.quantize_asym(w)
+        for r in range(n):
+            hi = max(Fraction(0), max(_frac(v) for v in w[r]))
+            lo = min(Fraction(0), min(_frac(v) for v in w[r]))
+            rng32 = nearest_repr(hi - lo, np.float32)
+            s32 = nearest_repr(_frac(rng32) / 255, np.float32)
+            s16 = nearest_repr(_frac(s32), np.float16)
+            assert sb[r] == np.array([s16]).view(np.uint16)[0], (r, w[r], sb[r], s16)
+            S = _frac(s16)
+            if S == 0:
+                assert z[r] == 0 and np.all(q[r] == 0)
+                continue
+            zq = round(_frac(nearest_repr(-lo / S, np.float32)))
+            zz = max(-128, min(127, zq - 128))
+            assert int(z[r]) == zz, (r, int(z[r]), zz)
+            for c in range(k):
+                v = _frac(nearest_repr(_frac(w[r, c]) / S, np.float32))
+                want = max(-128, min(127, round(v) + zz))
+                assert int(q[r, c]) == want, (r, c, float(w[r, c]), int(q[r, c]), want)
+
+
+def pin_asym_quantize_invariants(o, seed=18):
+    """Zero maps to the zero point; the row minimum (when negative) maps to
+    -128; codes are monotone in w; every weight below the top code is
+    recovered to within S/2 (plus the binary32 quotient's rounding)."""
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((16, 333)) * 0.02).astype(np.float32)
+    w[3] = np.abs(w[3]) + np.float32(0.01)
+    w[5] = -np.abs(w[5])
+    w[:, 7] = 0.0
+    q, sb, z = o.quantize_asym(w)
+    s = f16_from_bits(sb).astype(np.float64)
+    for r in range(w.shape[0]):
+        assert q[r, 7] == z[r]
+        if w[r].min() < 0 and -128 < z[r] < 127:
+            assert q[r, np.argmin(w[r])] == -128
+        order = np.argsort(w[r], kind="stable")
+        assert np.all(np.diff(q[r][order].astype(np.int32)) >= 0)
+        inner = q[r] < 127
+        err = np.abs(w[r].astype(np.float64) - s[r] * (q[r].astype(np.float64) - z[r]))[inner]
+        assert np.all(err <= s[r] * (0.5 + 2.0 ** -15)), (r, err.max() / s[r])
+
+
+def pin_gemm_asym(o, seed=19):
+    """With zero points 0 the asymmetric reference is the (pinned) symmetric
+    one; with X in {-1,0,1} and power-of-two scales every term is exact and it
+    equals numpy's int64 product of X and (q - z), scaled."""
+    rng = np.random.default_rng(seed)
+    m, n, k = 4, 30, 200
+    x = rng.standard_normal((m, k)).astype(np.float16)
+    q = rng.integers(-128, 128, size=(n, k)).astype(np.int8)
+    s = rng.uniform(1e-4, 1e-2, size=n).astype(np.float16).view(np.uint16)
+    assert np.array_equal(o.gemm_asym(x, q, s, np.zeros(n, np.int8)), o.gemm(x, q, s))
+    xi = rng.integers(-1, 2, size=(m, k)).astype(np.float16)
+    z = rng.integers(-128, 128, size=n).astype(np.int8)
+    e = rng.integers(0, 11, size=n)
+    sp = (2.0 ** (-e)).astype(np.float16).view(np.uint16)
+    ref = o.gemm_asym(xi, q, sp, z)
+    want = xi.astype(np.int64) @ (q.astype(np.int64) - z.astype(np.int64)[:, None]).T
+    assert np.array_equal(ref, np.ldexp(want.astype(np.float64), -e[None, :]))
+    mi = rng.integers(0, m, size=17)
+    ni = rng.integers(0, n, size=17)
+    assert np.array_equal(o.gemm_asym_sampled(xi, q, sp, z, mi, ni), ref[mi, ni])
+
+
+# --------------------------------------------------------------------------
 # W8A8 matmul reference
 # --------------------------------------------------------------------------
 
@@ -549,6 +650,9 @@ FAST_PINS = (
     pin_cosine_vs_unquantized,
     pin_fixed_range_bruteforce,
     pin_fixed_range_of_measured_bound,
+    pin_asym_quantize_bruteforce,
+    pin_asym_quantize_invariants,
+    pin_gemm_asym,
     pin_w8a8_unit_scales_is_integer_matmul,
     pin_w8a8_equals_w8a16_on_exact_activations,
     pin_w8a8_scaling_and_symmetry,

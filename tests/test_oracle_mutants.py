@@ -41,12 +41,21 @@ MUTANTS = {
     "f16_decode_bias": ("v = ldexpf((float)(1024 + frac), expfield - 25);",
                         "v = ldexpf((float)(1024 + frac), expfield - 24);"),
     # matmul: dropped scale, wrong sign, transposed/wrong operand index
-    "gemm_drops_scale": ("double wdeq = (double)qrow[j] * s;", "double wdeq = (double)qrow[j];"),
+    "gemm_drops_scale": ("double wdeq = ((double)qrow[j] - z) * s;", "double wdeq = ((double)qrow[j] - z);"),
     "gemm_wrong_sign": ("acc += xv * wdeq;", "acc -= xv * wdeq;"),
     "gemm_reversed_k": ("double xv = (double)oracle_f16_to_f32(xrow[j]);",
                         "double xv = (double)oracle_f16_to_f32(xrow[k - 1 - j]);"),
-    "gemm_scale_of_wrong_row": ("(double)oracle_f16_to_f32(scales[j]), k);",
-                                "(double)oracle_f16_to_f32(scales[i % n]), k);"),
+    "gemm_scale_of_wrong_row": ("ref[i * n + j] = dot_one(x + i * k, q + j * k, 0.0,\n                                     (double)oracle_f16_to_f32(scales[j]), k);",
+                                "ref[i * n + j] = dot_one(x + i * k, q + j * k, 0.0,\n                                     (double)oracle_f16_to_f32(scales[i % n]), k);"),
+    # asymmetric quantizer and matmul
+    "asym_divide_by_256": ("float s32 = range / 255.0f;", "float s32 = range / 256.0f;"),
+    "asym_range_without_zero": ("float hi = 0.0f, lo = 0.0f;", "float hi = -INFINITY, lo = INFINITY;"),
+    "asym_zero_point_unshifted": ("float zf = rintf(-lo / s) - 128.0f;", "float zf = rintf(-lo / s);"),
+    "asym_zero_point_sign": ("float c = rintf(row[j] / s) + zf;", "float c = rintf(row[j] / s) - zf;"),
+    "asym_round_half_away": ("float c = rintf(row[j] / s) + zf;", "float c = roundf(row[j] / s) + zf;"),
+    "asym_clamp_at_127": ("if (c < -128.0f)\n                c = -128.0f;", "if (c < -127.0f)\n                c = -127.0f;"),
+    "gemm_asym_zero_point_sign": ("double wdeq = ((double)qrow[j] - z) * s;", "double wdeq = ((double)qrow[j] + z) * s;"),
+    "gemm_asym_zero_of_wrong_row": ("const double zj = (double)zeros[j];", "const double zj = (double)zeros[i % n];"),
     # W8A8: dropped activation scale, wrong sign, reversed k, narrow
     # accumulator, activation scale taken from the weight's row index
     "w8a8_drops_x_scale": ("return (double)acc * (sx * sw);", "return (double)acc * sw;"),
