@@ -148,6 +148,36 @@ QW_API qw_status qw_quantize_weights_fixed_range(const float *w, int64_t n, int6
                                                  uint16_t *scales, void *stream);
 
 /*
+ * qw_quantize_weights_asym -- asymmetric (zero-point) per-row int8
+ * quantization.
+ *
+ * Source: LightSeq slide deck ("LightSeq：高性能NLP序列推理实践"), slide
+ * 量化：裁剪+对称, asymmetric case: the value range is spread over the
+ * 2^n - 1 steps with a scale S and a zero point z, and W ~ S * (q - z).
+ * Per row r, with the range widened to hold 0 so that 0 is exact:
+ *
+ *   hi = max(0, max_c w[r][c]),  lo = min(0, min_c w[r][c])
+ *   S[r] = binary16_RNE( binary32( binary32(hi - lo) / 255 ) )
+ *   z[r] = clamp( round_half_even( binary32(-lo / S[r]) ) - 128, -128, 127 )
+ *   q[r][c] = clamp( round_half_even( binary32(w[r][c] / S[r]) ) + z[r], -128, 127 )
+ *   (S[r] == 0: z[r] = 0 and q[r][:] = 0)
+ *
+ * so w = 0 maps to code z[r] and the row minimum (when negative) to -128.
+ *
+ *   w       fp32 [n][k], read only
+ *   q       int8 [n][k] (written)
+ *   scales  fp16 bits [n] (written)
+ *   zeros   int8 [n] zero points (written)
+ *   n, k, stream as qw_quantize_weights
+ *
+ * Errors: as qw_quantize_weights (no percentile argument), plus
+ * QW_ERROR_INVALID_VALUE for a null zeros or zeros overlapping w, q or
+ * scales, and QW_ERROR_MISALIGNED for a misaligned zeros.
+ */
+QW_API qw_status qw_quantize_weights_asym(const float *w, int64_t n, int64_t k, int8_t *q,
+                                          uint16_t *scales, int8_t *zeros, void *stream);
+
+/*
  * qw_w8a16_gemm -- Y = X * dequant(Q)^T with per-channel fp16 scales.
  *
  * Source: ChatGLM2/BM1684X page, section 4 (后端性能提升原理): load, cast
@@ -205,6 +235,29 @@ QW_API qw_status qw_w8a16_gemm_path(const uint16_t *x, const int8_t *q,
                                     const uint16_t *scales, uint16_t *y,
                                     int64_t m, int64_t n, int64_t k, int path,
                                     void *stream);
+
+/*
+ * qw_w8a16_gemm_asym -- W8A16 with asymmetric weights (as written by
+ * qw_quantize_weights_asym):
+ *
+ *   Y[i][c] = binary16_RNE( S[c] * sum_j X[i][j] * (q[c][j] - z[c]) )
+ *
+ * the dequantization S * (q - z) of the asymmetric slide (LightSeq deck,
+ * 量化：裁剪+对称).  q - z is formed exactly in fp16 by the int8 cast (it
+ * lies in [-255, 255]); products are exact in fp32 and summed in fp32, as
+ * in qw_w8a16_gemm, with the same kernels, kernel choice and accuracy
+ * contract.  zeros: int8 [n], 16-byte aligned.  Errors: as qw_w8a16_gemm,
+ * plus QW_ERROR_INVALID_VALUE for a null zeros (m, n > 0) or y overlapping
+ * zeros, and QW_ERROR_MISALIGNED for a misaligned zeros.
+ * qw_w8a16_gemm_asym_path forces the kernel as qw_w8a16_gemm_path does.
+ */
+QW_API qw_status qw_w8a16_gemm_asym(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                                    const int8_t *zeros, uint16_t *y, int64_t m, int64_t n,
+                                    int64_t k, void *stream);
+QW_API qw_status qw_w8a16_gemm_asym_path(const uint16_t *x, const int8_t *q,
+                                         const uint16_t *scales, const int8_t *zeros,
+                                         uint16_t *y, int64_t m, int64_t n, int64_t k, int path,
+                                         void *stream);
 
 /*
  * qw_w8a16_gemm_auto_path -- the QW_PATH_* kernel qw_w8a16_gemm would run

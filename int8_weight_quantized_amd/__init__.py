@@ -72,6 +72,12 @@ def _load():
     lib.qw_quantize_weights_f16.restype = ctypes.c_int
     lib.qw_quantize_weights_fixed_range.argtypes = [vp, i64, i64, vp, vp, vp, vp]
     lib.qw_quantize_weights_fixed_range.restype = ctypes.c_int
+    lib.qw_quantize_weights_asym.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+    lib.qw_quantize_weights_asym.restype = ctypes.c_int
+    lib.qw_w8a16_gemm_asym.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.qw_w8a16_gemm_asym.restype = ctypes.c_int
+    lib.qw_w8a16_gemm_asym_path.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.qw_w8a16_gemm_asym_path.restype = ctypes.c_int
     lib.qw_w8a8_gemm.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.qw_w8a8_gemm.restype = ctypes.c_int
     lib.qw_w8a8_gemm_mfma_tile.argtypes = [i64, i64, i64]
@@ -151,6 +157,16 @@ def quantize_weights_f16_raw(w_ptr: int, n: int, k: int, clip_percentile: float,
 def quantize_weights_fixed_range_raw(w_ptr: int, n: int, k: int, bounds_ptr: int, q_ptr: int, s_ptr: int,
                                      stream: int = 0) -> int:
     return int(library().qw_quantize_weights_fixed_range(w_ptr, n, k, bounds_ptr, q_ptr, s_ptr, stream))
+
+
+def quantize_weights_asym_raw(w_ptr: int, n: int, k: int, q_ptr: int, s_ptr: int, z_ptr: int,
+                              stream: int = 0) -> int:
+    return int(library().qw_quantize_weights_asym(w_ptr, n, k, q_ptr, s_ptr, z_ptr, stream))
+
+
+def w8a16_gemm_asym_raw(x_ptr: int, q_ptr: int, s_ptr: int, z_ptr: int, y_ptr: int, m: int, n: int, k: int,
+                        stream: int = 0, path: int = 0) -> int:
+    return int(library().qw_w8a16_gemm_asym_path(x_ptr, q_ptr, s_ptr, z_ptr, y_ptr, m, n, k, int(path), stream))
 
 
 def w8a16_gemm_raw(x_ptr: int, q_ptr: int, s_ptr: int, y_ptr: int, m: int, n: int, k: int,
@@ -269,6 +285,44 @@ def quantize_weights_fixed_range(w, bounds, out=None):
     return q, s
 
 
+def quantize_weights_asym(w):
+    """Asymmetric per-row int8 quantization of a cuda float32 [N, K] weight:
+    returns (q int8 [N, K], scales float16 [N], zeros int8 [N]) with
+    W ~ scales[:, None] * (q - zeros[:, None])."""
+    torch = _torch()
+    _check(w, "w", torch.float32, 2)
+    n, k = w.shape
+    q = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    s = torch.empty((n,), dtype=torch.float16, device=w.device)
+    z = torch.empty((n,), dtype=torch.int8, device=w.device)
+    st = quantize_weights_asym_raw(w.data_ptr(), n, k, q.data_ptr(), s.data_ptr(), z.data_ptr(), _stream_of(w))
+    if st != QW_SUCCESS:
+        raise QwError(st, "qw_quantize_weights_asym")
+    return q, s, z
+
+
+def w8a16_gemm_asym(x, q, scales, zeros, out=None, path: str = "auto"):
+    """Y = X * (scales * (q - zeros))^T for asymmetric weights: x cuda fp16
+    [M, K], q int8 [N, K], scales fp16 [N], zeros int8 [N] -> fp16 [M, N]."""
+    torch = _torch()
+    _check(x, "x", torch.float16, 2)
+    _check(q, "q", torch.int8, 2)
+    _check(scales, "scales", torch.float16, 1)
+    _check(zeros, "zeros", torch.int8, 1)
+    m, k = x.shape
+    n = q.shape[0]
+    if q.shape[1] != k or scales.shape[0] != n or zeros.shape[0] != n:
+        raise ValueError("shape mismatch")
+    y = torch.empty((m, n), dtype=torch.float16, device=x.device) if out is None else out
+    if path not in PATHS:
+        raise ValueError("path must be one of %s" % sorted(PATHS))
+    st = w8a16_gemm_asym_raw(x.data_ptr(), q.data_ptr(), scales.data_ptr(), zeros.data_ptr(), y.data_ptr(),
+                             m, n, k, _stream_of(x), PATHS[path])
+    if st != QW_SUCCESS:
+        raise QwError(st, "qw_w8a16_gemm_asym")
+    return y
+
+
 def quantize_activations(x, out=None):
     """Per-token (per-row) symmetric int8 quantization of fp16 activations
     [M, K] for W8A8: the weights' quantizer with the row absmax.  Returns
@@ -303,7 +357,8 @@ def w8a8_gemm(qx, sx, q, scales, out=None):
     return y
 
 
-__all__ = ["quantize_weights", "quantize_weights_fixed_range", "quantize_activations", "w8a16_gemm", "w8a8_gemm", "QwError",
+__all__ = ["quantize_weights", "quantize_weights_fixed_range", "quantize_weights_asym", "w8a16_gemm_asym",
+           "quantize_activations", "w8a16_gemm", "w8a8_gemm", "QwError",
            "status_string", "version", "library", "auto_path", "mfma_tile", "w8a8_tile",
-           "quantize_weights_raw", "quantize_weights_f16_raw", "quantize_weights_fixed_range_raw", "w8a16_gemm_raw", "w8a8_gemm_raw",
+           "quantize_weights_raw", "quantize_weights_f16_raw", "quantize_weights_fixed_range_raw", "quantize_weights_asym_raw", "w8a16_gemm_asym_raw", "w8a16_gemm_raw", "w8a8_gemm_raw",
            "PATHS", "LIBRARY_PATH"]

@@ -155,7 +155,7 @@ template <int NW, int BN, int BM, bool A8>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm_dma_kernel(
     const void *__restrict__ xv, const uint16_t *__restrict__ sx, const int8_t *__restrict__ q,
-    const uint16_t *__restrict__ scales, uint16_t *__restrict__ y,
+    const uint16_t *__restrict__ scales, const int8_t *__restrict__ zeros, uint16_t *__restrict__ y,
     int m, int n, int k, int tiles_m, int tiles_n)
 {
     using C = DmaCfg<NW, BN, BM, A8>;
@@ -269,6 +269,15 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
         for (int j = 0; j < kSJ; ++j)
             acc[i][j] = (acc_t){};
 
+    // asymmetric weights (zeros non-null, fp16 activations only): the cast
+    // subtracts the zero point of each of this lane's weight rows
+    half2_t zbias[C::kSI];
+#pragma unroll
+    for (int i = 0; i < C::kSI; ++i) {
+        const int zr = n0 + wrow + 32 * i;
+        zbias[i] = zero_point_bias(zeros != nullptr && zr < n ? (int)zeros[zr] : 0);
+    }
+
     auto compute_a8 = [&](const uint8_t *st) {
         u32x4_t clo[C::kSI], chi[C::kSI];
 #pragma unroll
@@ -319,7 +328,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
 #pragma unroll
             for (int i = 0; i < C::kSI; ++i) {
                 const u32x4_t c = sidx < 2 ? clo[i] : chi[i];
-                const half8_t a = (sidx & 1) ? i8x8_to_half8(c.z, c.w) : i8x8_to_half8(c.x, c.y);
+                const half8_t a = (sidx & 1) ? i8x8_to_half8(c.z, c.w, zbias[i]) : i8x8_to_half8(c.x, c.y, zbias[i]);
 #pragma unroll
                 for (int j = 0; j < kSJ; ++j)
                     if constexpr (!A8)
@@ -440,7 +449,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
 
 template <int NW, int BN, int BM, bool A8>
 hipError_t launch_dma(const void *x, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
-                      uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
+                      const int8_t *zeros, uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
     const int64_t tiles_m = (m + BM - 1) / BM;
     const int64_t tiles_n = (n + BN - 1) / BN;
@@ -448,7 +457,8 @@ hipError_t launch_dma(const void *x, const uint16_t *sx, const int8_t *q, const 
     if (blocks > 0x7fffffff)
         return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((mfma_gemm_dma_kernel<NW, BN, BM, A8>), dim3((unsigned)blocks), dim3(NW * kWave),
-                       0, stream, x, sx, q, scales, y, (int)m, (int)n, (int)k, (int)tiles_m, (int)tiles_n);
+                       0, stream, x, sx, q, scales, zeros, y, (int)m, (int)n, (int)k, (int)tiles_m,
+                       (int)tiles_n);
     return hipGetLastError();
 }
 
@@ -498,19 +508,20 @@ int tile_choice(int64_t m, int64_t n)
 
 template <bool A8>
 hipError_t launch_tiles(const void *x, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
-                        uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
+                        const int8_t *zeros, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                        hipStream_t stream)
 {
     switch (tile_choice<A8>(m, n)) {
     case 256128:
-        return launch_dma<4, 256, 128, A8>(x, sx, q, scales, y, m, n, k, stream);
+        return launch_dma<4, 256, 128, A8>(x, sx, q, scales, zeros, y, m, n, k, stream);
     case 256064:
-        return launch_dma<4, 256, 64, A8>(x, sx, q, scales, y, m, n, k, stream);
+        return launch_dma<4, 256, 64, A8>(x, sx, q, scales, zeros, y, m, n, k, stream);
     case 128128:
         if constexpr (!A8)
-            return launch_dma<4, 128, 128, A8>(x, sx, q, scales, y, m, n, k, stream);
+            return launch_dma<4, 128, 128, A8>(x, sx, q, scales, zeros, y, m, n, k, stream);
         [[fallthrough]];
     default:
-        return launch_dma<4, 128, 64, A8>(x, sx, q, scales, y, m, n, k, stream);
+        return launch_dma<4, 128, 64, A8>(x, sx, q, scales, zeros, y, m, n, k, stream);
     }
 }
 
@@ -526,17 +537,18 @@ int w8a8_tile_choice(int64_t m, int64_t n)
     return tile_choice<true>(m, n);
 }
 
-hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
-                            int64_t m, int64_t n, int64_t k, hipStream_t stream)
+hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                            const int8_t *zeros, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                            hipStream_t stream)
 {
-    return launch_tiles<false>(x, nullptr, q, scales, y, m, n, k, stream);
+    return launch_tiles<false>(x, nullptr, q, scales, zeros, y, m, n, k, stream);
 }
 
 hipError_t launch_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t *q,
                             const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
                             hipStream_t stream)
 {
-    return launch_tiles<true>(qx, sx, q, scales, y, m, n, k, stream);
+    return launch_tiles<true>(qx, sx, q, scales, nullptr, y, m, n, k, stream);
 }
 
 } // namespace qw

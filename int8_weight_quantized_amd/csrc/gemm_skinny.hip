@@ -41,7 +41,7 @@ constexpr int kSkinnyTargetWaves = 2048; // enough in-flight loads to fill HBM
 template <int RT, int KSPLIT>
 __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
     const uint16_t *__restrict__ x, const int8_t *__restrict__ q,
-    const uint16_t *__restrict__ scales, uint16_t *__restrict__ y,
+    const uint16_t *__restrict__ scales, const int8_t *__restrict__ zeros, uint16_t *__restrict__ y,
     int m, int n, int k)
 {
     // Per wave, a staging slice for the weight codes of one iteration:
@@ -89,6 +89,13 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
             const int yn = n0 + 16 * t + 4 * g + i;
             sc[t][i] = yn < n ? scales[yn] : (uint16_t)0;
         }
+
+    // asymmetric weights: the cast subtracts the zero point of weight row
+    // n0 + 16 t + r (zeros == nullptr: symmetric)
+    half2_t zbias[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+        zbias[t] = zero_point_bias(zeros != nullptr && row_ok[t] ? (int)zeros[n0 + 16 * t + r] : 0);
 
     float4v acc[RT];
 #pragma unroll
@@ -150,8 +157,8 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
             const half8_t b1 = __builtin_bit_cast(half8_t, xb[u]);
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
-                const half8_t a0 = i8x8_to_half8(wv[u][t].x, wv[u][t].y);
-                const half8_t a1 = i8x8_to_half8(wv[u][t].z, wv[u][t].w);
+                const half8_t a0 = i8x8_to_half8(wv[u][t].x, wv[u][t].y, zbias[t]);
+                const half8_t a1 = i8x8_to_half8(wv[u][t].z, wv[u][t].w, zbias[t]);
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, acc[t], 0, 0, 0);
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, acc[t], 0, 0, 0);
             }
@@ -208,17 +215,17 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
 }
 
 template <int RT, int KSPLIT>
-hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
+hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros, uint16_t *y,
                       int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
     const dim3 grid((unsigned)((n + 16 * RT - 1) / (16 * RT)), (unsigned)((m + 15) / 16));
     hipLaunchKernelGGL((skinny_gemm_kernel<RT, KSPLIT>), grid, dim3(KSPLIT * kWave), 0, stream,
-                       x, q, scales, y, (int)m, (int)n, (int)k);
+                       x, q, scales, zeros, y, (int)m, (int)n, (int)k);
     return hipGetLastError();
 }
 
 template <int RT>
-hipError_t launch_rt(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
+hipError_t launch_rt(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros, uint16_t *y,
                      int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
     // split k until the grid holds about kSkinnyTargetWaves waves, keeping
@@ -230,27 +237,27 @@ hipError_t launch_rt(const uint16_t *x, const int8_t *q, const uint16_t *scales,
         ksplit *= 2;
     switch (ksplit) {
     case 1:
-        return launch_cfg<RT, 1>(x, q, scales, y, m, n, k, stream);
+        return launch_cfg<RT, 1>(x, q, scales, zeros, y, m, n, k, stream);
     case 2:
-        return launch_cfg<RT, 2>(x, q, scales, y, m, n, k, stream);
+        return launch_cfg<RT, 2>(x, q, scales, zeros, y, m, n, k, stream);
     case 4:
-        return launch_cfg<RT, 4>(x, q, scales, y, m, n, k, stream);
+        return launch_cfg<RT, 4>(x, q, scales, zeros, y, m, n, k, stream);
     case 8:
-        return launch_cfg<RT, 8>(x, q, scales, y, m, n, k, stream);
+        return launch_cfg<RT, 8>(x, q, scales, zeros, y, m, n, k, stream);
     default:
-        return launch_cfg<RT, 16>(x, q, scales, y, m, n, k, stream);
+        return launch_cfg<RT, 16>(x, q, scales, zeros, y, m, n, k, stream);
     }
 }
 
 } // namespace
 
 hipError_t launch_skinny_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
-                              uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
+                              const int8_t *zeros, uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
     // two 16-row weight tiles per wave: the activation operand is reused
     // twice; four tiles measured slower (fewer waves, longer dependent
     // MFMA chains)
-    return launch_rt<2>(x, q, scales, y, m, n, k, stream);
+    return launch_rt<2>(x, q, scales, zeros, y, m, n, k, stream);
 }
 
 } // namespace qw

@@ -45,7 +45,7 @@ struct GemvItem {
 template <int MT, int RU, int CH>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     const uint16_t *__restrict__ x, const int8_t *__restrict__ q,
-    const uint16_t *__restrict__ scales, uint16_t *__restrict__ y,
+    const uint16_t *__restrict__ scales, const int8_t *__restrict__ zeros, uint16_t *__restrict__ y,
     int m, int n, int k, int chunks, int total_waves)
 {
     extern __shared__ u32x4_t xs[];
@@ -102,6 +102,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
 
     constexpr int R = RU * MT;
     float acc[R];
+    half2_t zbias[RU];
 
     auto consume = [&](int it, const GemvItem<MT, RU, CH> &cur) {
         const int g = it / batches;
@@ -110,6 +111,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
 #pragma unroll
             for (int i = 0; i < R; ++i)
                 acc[i] = 0.0f;
+            // asymmetric weights: the zero points of this item's rows
+#pragma unroll
+            for (int r = 0; r < RU; ++r) {
+                const int j = g * RU + r;
+                const int64_t row = gw + (int64_t)j * total_waves;
+                zbias[r] = zero_point_bias(zeros != nullptr && j < my_rows ? (int)zeros[row] : 0);
+            }
         }
 #pragma unroll
         for (int cc = 0; cc < CH; ++cc) {
@@ -132,7 +140,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
 #pragma unroll
                 for (int r = 0; r < RU; ++r) {
                     half2_t hw[8];
-                    i8x16_to_half2x8(cur.w[r][cc], hw);
+                    i8x16_to_half2x8(cur.w[r][cc], hw, zbias[r]);
 #pragma unroll
                     for (int mm = 0; mm < MT; ++mm) {
                         float a = acc[r * MT + mm];
@@ -171,7 +179,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
 }
 
 template <int MT, int RU, int CH, int WPC>
-hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
+hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros,
+                      uint16_t *y,
                       int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
     const int chunks = (int)((k + kChunkK - 1) / kChunkK);
@@ -192,7 +201,7 @@ hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales
     }
     const int blocks = (int)((waves + kGemvWaves - 1) / kGemvWaves);
     hipLaunchKernelGGL((gemv_kernel<MT, RU, CH>), dim3(blocks), dim3(kGemvThreads), lds, stream,
-                       x, q, scales, y, (int)m, (int)n, (int)k, chunks, (int)waves);
+                       x, q, scales, zeros, y, (int)m, (int)n, (int)k, chunks, (int)waves);
     return hipGetLastError();
 }
 
@@ -209,18 +218,19 @@ bool gemv_supported(int64_t m, int64_t k)
     return mt * chunks <= kGemvMaxMChunks;
 }
 
-hipError_t launch_gemv(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
+hipError_t launch_gemv(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros,
+                       uint16_t *y,
                        int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
     // (MT, RU, CH, waves per CU) from measured sweeps; WPC stays within what
     // each configuration's register use lets a CU hold at once
     if (m <= 1)
-        return launch_cfg<1, 2, 4, 28>(x, q, scales, y, m, n, k, stream);
+        return launch_cfg<1, 2, 4, 28>(x, q, scales, zeros, y, m, n, k, stream);
     if (m <= 2)
-        return launch_cfg<2, 1, 4, 32>(x, q, scales, y, m, n, k, stream);
+        return launch_cfg<2, 1, 4, 32>(x, q, scales, zeros, y, m, n, k, stream);
     if (m <= 4)
-        return launch_cfg<4, 2, 2, 16>(x, q, scales, y, m, n, k, stream);
-    return launch_cfg<8, 2, 2, 16>(x, q, scales, y, m, n, k, stream);
+        return launch_cfg<4, 2, 2, 16>(x, q, scales, zeros, y, m, n, k, stream);
+    return launch_cfg<8, 2, 2, 16>(x, q, scales, zeros, y, m, n, k, stream);
 }
 
 } // namespace qw

@@ -243,11 +243,14 @@ __device__ __forceinline__ float4_t load4(const void *row, int idx)
 }
 
 // MODE: 0 absmax bound, 1 percentile bound, 2 fixed range (the bound of
-// row r is bounds[r], given by the caller; no reduction).
+// row r is bounds[r], given by the caller; no reduction), 3 asymmetric
+// (range [min(0, min w), max(0, max w)] over 255 steps, int8 zero point
+// per row written to zeros).
 template <int THREADS, int VPT, int MODE, bool F16>
 __global__ __launch_bounds__(THREADS) void quantize_rows_kernel(
     const void *__restrict__ w, int k, int64_t rank_i, double frac_f,
-    const float *__restrict__ bounds, int8_t *__restrict__ q, uint16_t *__restrict__ scales)
+    const float *__restrict__ bounds, int8_t *__restrict__ q, uint16_t *__restrict__ scales,
+    int8_t *__restrict__ zeros)
 {
     constexpr bool PERCENTILE = MODE == 1;
     __shared__ QuantShared<THREADS> sh;
@@ -270,8 +273,24 @@ __global__ __launch_bounds__(THREADS) void quantize_rows_kernel(
         v[j * 4 + 3] = f.w;
     }
     float t;
+    float neg_lo = 0.0f; // MODE 3: -min(0, min w)
     if constexpr (MODE == 2) {
         t = bounds[row];
+    } else if constexpr (MODE == 3) {
+        // max(0, max w) and max(0, max -w) as bit patterns of non-negative
+        // floats, whose unsigned order is their numeric order
+        uint32_t hb = 0, lb = 0;
+#pragma unroll
+        for (int e = 0; e < VPT * 4; ++e) {
+            const float val = v[e];
+            const uint32_t b = abs_bits(val);
+            if (val > 0.0f)
+                hb = b > hb ? b : hb;
+            if (val < 0.0f)
+                lb = b > lb ? b : lb;
+        }
+        t = __builtin_bit_cast(float, block_max_u32<THREADS>(hb, sh));
+        neg_lo = __builtin_bit_cast(float, block_max_u32<THREADS>(lb, sh));
     } else if constexpr (!PERCENTILE) {
         uint32_t m = 0;
 #pragma unroll
@@ -313,11 +332,25 @@ __global__ __launch_bounds__(THREADS) void quantize_rows_kernel(
         t = (float)__dadd_rn(lo, step);
     }
 
-    const float s32 = __fdiv_rn(t, 127.0f);
+    // symmetric: S = t / 127; asymmetric: S = (hi - lo) / 255, the range
+    // over the 2^8 - 1 steps, and z shifts code -lo/S down to -128
+    const float s32 = MODE == 3 ? __fdiv_rn(__fadd_rn(t, neg_lo), 255.0f) : __fdiv_rn(t, 127.0f);
     const uint16_t s16 = f32_to_f16_bits(s32);
     const float s = f16_bits_to_f32(s16);
-    if (threadIdx.x == 0)
+    float zf = 0.0f;
+    if constexpr (MODE == 3) {
+        if (s != 0.0f) {
+            zf = __builtin_rintf(__fdiv_rn(neg_lo, s)) - 128.0f;
+            zf = zf > 127.0f ? 127.0f : zf;
+            zf = zf < -128.0f ? -128.0f : zf;
+        }
+    }
+    constexpr float kLo = MODE == 3 ? -128.0f : -127.0f;
+    if (threadIdx.x == 0) {
         scales[row] = s16;
+        if constexpr (MODE == 3)
+            zeros[row] = (int8_t)(int)zf;
+    }
 
     // Codes.  The contract is rint(binary32(w / s)); a true division per
     // weight costs about ten VALU instructions, so the quotient is first
@@ -350,8 +383,9 @@ __global__ __launch_bounds__(THREADS) void quantize_rows_kernel(
                 const float d = __builtin_fabsf(__builtin_fabsf(est - r) - 0.5f);
                 if (__builtin_expect(d < kNearHalf && __builtin_fabsf(est) < 256.0f, 0))
                     r = __builtin_rintf(__fdiv_rn(v[j * 4 + e], s));
+                r += zf; // exact: integers of magnitude below 2^24
                 r = r > 127.0f ? 127.0f : r;
-                r = r < -127.0f ? -127.0f : r;
+                r = r < kLo ? kLo : r;
                 code = (int)r;
             }
             packed |= ((uint32_t)code & 0xffu) << (8 * e);
@@ -362,36 +396,42 @@ __global__ __launch_bounds__(THREADS) void quantize_rows_kernel(
 
 template <int THREADS, int VPT, bool F16>
 hipError_t launch_typed(const void *w, int64_t n, int64_t k, int mode, int64_t rank_i, double frac_f,
-                        const float *bounds, int8_t *q, uint16_t *scales, hipStream_t stream)
+                        const float *bounds, int8_t *q, uint16_t *scales, int8_t *zeros,
+                        hipStream_t stream)
 {
     const dim3 grid((unsigned)n), block(THREADS);
     if (mode == 0)
         hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, 0, F16>), grid, block, 0, stream,
-                           w, (int)k, rank_i, frac_f, bounds, q, scales);
+                           w, (int)k, rank_i, frac_f, bounds, q, scales, zeros);
     else if (mode == 1)
         hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, 1, F16>), grid, block, 0, stream,
-                           w, (int)k, rank_i, frac_f, bounds, q, scales);
-    else if constexpr (!F16)
+                           w, (int)k, rank_i, frac_f, bounds, q, scales, zeros);
+    else if constexpr (F16)
+        return hipErrorInvalidValue; // fixed range and asymmetric: fp32 weights only
+    else if (mode == 2)
         hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, 2, false>), grid, block, 0, stream,
-                           w, (int)k, rank_i, frac_f, bounds, q, scales);
+                           w, (int)k, rank_i, frac_f, bounds, q, scales, zeros);
     else
-        return hipErrorInvalidValue; // fixed range is offered for fp32 weights only
+        hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, 3, false>), grid, block, 0, stream,
+                           w, (int)k, rank_i, frac_f, bounds, q, scales, zeros);
     return hipGetLastError();
 }
 
 template <int THREADS, int VPT>
 hipError_t launch_cfg(const void *w, bool f16, int64_t n, int64_t k, int mode, int64_t rank_i,
-                      double frac_f, const float *bounds, int8_t *q, uint16_t *scales, hipStream_t stream)
+                      double frac_f, const float *bounds, int8_t *q, uint16_t *scales, int8_t *zeros,
+                      hipStream_t stream)
 {
-    return f16 ? launch_typed<THREADS, VPT, true>(w, n, k, mode, rank_i, frac_f, bounds, q, scales, stream)
-               : launch_typed<THREADS, VPT, false>(w, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
+    return f16 ? launch_typed<THREADS, VPT, true>(w, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream)
+               : launch_typed<THREADS, VPT, false>(w, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros,
+                                                   stream);
 }
 
 } // namespace
 
 hipError_t launch_quantize(const void *w, bool w_is_f16, int64_t n, int64_t k, int mode,
                            int64_t rank_i, double frac_f, const float *bounds, int8_t *q,
-                           uint16_t *scales, hipStream_t stream)
+                           uint16_t *scales, int8_t *zeros, hipStream_t stream)
 {
     // float4 slots per row; a workgroup of THREADS holds THREADS * VPT of them.
     // Rows up to 1024 values get one wave each: every reduction is then a
@@ -399,24 +439,24 @@ hipError_t launch_quantize(const void *w, bool w_is_f16, int64_t n, int64_t k, i
     // percentile; no gain at 2048).
     const int64_t nvec = k / 4;
     if (nvec <= kWave * 1)
-        return launch_cfg<64, 1>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
+        return launch_cfg<64, 1>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
     if (nvec <= kWave * 2)
-        return launch_cfg<64, 2>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
+        return launch_cfg<64, 2>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
     if (nvec <= kWave * 4)
-        return launch_cfg<64, 4>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
+        return launch_cfg<64, 4>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
     if (nvec <= 256 * 1)
-        return launch_cfg<256, 1>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
+        return launch_cfg<256, 1>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
     if (nvec <= 256 * 2)
-        return launch_cfg<256, 2>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
+        return launch_cfg<256, 2>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
     if (nvec <= 256 * 4)
-        return launch_cfg<256, 4>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
+        return launch_cfg<256, 4>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
     if (nvec <= 256 * 8)
-        return launch_cfg<256, 8>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
+        return launch_cfg<256, 8>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
     if (nvec <= 256 * 16)
-        return launch_cfg<256, 16>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
+        return launch_cfg<256, 16>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
     if (nvec <= 1024 * 8)
-        return launch_cfg<1024, 8>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
-    return launch_cfg<1024, 16>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, stream);
+        return launch_cfg<1024, 8>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
+    return launch_cfg<1024, 16>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
 }
 
 } // namespace qw

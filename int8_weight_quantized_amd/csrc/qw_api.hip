@@ -138,7 +138,41 @@ qw_status quantize_common(const void *w, int wbytes, int64_t n, int64_t k, doubl
         }
     }
     return launch_status(qw::launch_quantize(w, wbytes == 2, n, k, mode, rank_i, frac_f, nullptr, q,
-                                             scales, static_cast<hipStream_t>(stream)));
+                                             scales, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+// Shared body of the symmetric and asymmetric W8A16 entry points (zeros ==
+// nullptr: symmetric).
+qw_status gemm_common(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros,
+                      uint16_t *y, int64_t m, int64_t n, int64_t k, int path, void *stream)
+{
+    if (path != QW_PATH_AUTO && path != QW_PATH_GEMV && path != QW_PATH_MFMA &&
+        path != QW_PATH_SKINNY)
+        return QW_ERROR_INVALID_VALUE;
+    bool noop = false;
+    const qw_status st = check_gemm_args(x, q, scales, y, m, n, k, noop);
+    if (st != QW_SUCCESS || noop)
+        return st;
+    if (zeros) {
+        if (misaligned(zeros))
+            return QW_ERROR_MISALIGNED;
+        if (overlaps(y, (uint64_t)m * (uint64_t)n * 2u, zeros, (uint64_t)n))
+            return QW_ERROR_INVALID_VALUE;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (path == QW_PATH_AUTO)
+        path = qw::auto_path(m, n, k);
+    if (path == QW_PATH_GEMV) {
+        if (!qw::gemv_supported(m, k))
+            return QW_ERROR_UNSUPPORTED;
+        return launch_status(qw::launch_gemv(x, q, scales, zeros, y, m, n, k, s));
+    }
+    if (path == QW_PATH_SKINNY) {
+        if (m > 16 * 65535) // grid.y holds one 16-row activation tile per block row
+            return QW_ERROR_UNSUPPORTED;
+        return launch_status(qw::launch_skinny_gemm(x, q, scales, zeros, y, m, n, k, s));
+    }
+    return launch_status(qw::launch_mfma_gemm(x, q, scales, zeros, y, m, n, k, s));
 }
 
 } // namespace
@@ -176,7 +210,29 @@ QW_API qw_status qw_quantize_weights_fixed_range(const float *w, int64_t n, int6
         overlaps(scales, (uint64_t)n * 2u, q, elems) || overlaps(q, elems, bounds, (uint64_t)n * 4u) ||
         overlaps(scales, (uint64_t)n * 2u, bounds, (uint64_t)n * 4u))
         return QW_ERROR_INVALID_VALUE;
-    return launch_status(qw::launch_quantize(w, false, n, k, 2, 0, 0.0, bounds, q, scales,
+    return launch_status(qw::launch_quantize(w, false, n, k, 2, 0, 0.0, bounds, q, scales, nullptr,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+QW_API qw_status qw_quantize_weights_asym(const float *w, int64_t n, int64_t k, int8_t *q,
+                                          uint16_t *scales, int8_t *zeros, void *stream)
+{
+    if (n < 0 || k <= 0)
+        return QW_ERROR_INVALID_VALUE;
+    if (n == 0)
+        return QW_SUCCESS;
+    if (!w || !q || !scales || !zeros)
+        return QW_ERROR_INVALID_VALUE;
+    if (k % 16 != 0 || k > QW_QUANTIZE_MAX_K || n > kMaxDim)
+        return QW_ERROR_UNSUPPORTED;
+    if (misaligned(w) || misaligned(q) || misaligned(scales) || misaligned(zeros))
+        return QW_ERROR_MISALIGNED;
+    const uint64_t elems = (uint64_t)n * (uint64_t)k, nn = (uint64_t)n;
+    if (overlaps(q, elems, w, elems * 4u) || overlaps(scales, nn * 2u, w, elems * 4u) ||
+        overlaps(zeros, nn, w, elems * 4u) || overlaps(scales, nn * 2u, q, elems) ||
+        overlaps(zeros, nn, q, elems) || overlaps(zeros, nn, scales, nn * 2u))
+        return QW_ERROR_INVALID_VALUE;
+    return launch_status(qw::launch_quantize(w, false, n, k, 3, 0, 0.0, nullptr, q, scales, zeros,
                                              static_cast<hipStream_t>(stream)));
 }
 
@@ -184,27 +240,23 @@ QW_API qw_status qw_w8a16_gemm_path(const uint16_t *x, const int8_t *q, const ui
                                     uint16_t *y, int64_t m, int64_t n, int64_t k, int path,
                                     void *stream)
 {
-    if (path != QW_PATH_AUTO && path != QW_PATH_GEMV && path != QW_PATH_MFMA &&
-        path != QW_PATH_SKINNY)
+    return gemm_common(x, q, scales, nullptr, y, m, n, k, path, stream);
+}
+
+QW_API qw_status qw_w8a16_gemm_asym_path(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                                         const int8_t *zeros, uint16_t *y, int64_t m, int64_t n,
+                                         int64_t k, int path, void *stream)
+{
+    if (m > 0 && n > 0 && !zeros)
         return QW_ERROR_INVALID_VALUE;
-    bool noop = false;
-    const qw_status st = check_gemm_args(x, q, scales, y, m, n, k, noop);
-    if (st != QW_SUCCESS || noop)
-        return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (path == QW_PATH_AUTO)
-        path = qw::auto_path(m, n, k);
-    if (path == QW_PATH_GEMV) {
-        if (!qw::gemv_supported(m, k))
-            return QW_ERROR_UNSUPPORTED;
-        return launch_status(qw::launch_gemv(x, q, scales, y, m, n, k, s));
-    }
-    if (path == QW_PATH_SKINNY) {
-        if (m > 16 * 65535) // grid.y holds one 16-row activation tile per block row
-            return QW_ERROR_UNSUPPORTED;
-        return launch_status(qw::launch_skinny_gemm(x, q, scales, y, m, n, k, s));
-    }
-    return launch_status(qw::launch_mfma_gemm(x, q, scales, y, m, n, k, s));
+    return gemm_common(x, q, scales, zeros, y, m, n, k, path, stream);
+}
+
+QW_API qw_status qw_w8a16_gemm_asym(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                                    const int8_t *zeros, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                                    void *stream)
+{
+    return qw_w8a16_gemm_asym_path(x, q, scales, zeros, y, m, n, k, QW_PATH_AUTO, stream);
 }
 
 QW_API qw_status qw_w8a16_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,

@@ -27,32 +27,47 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // integers below 2048, representable in binary16).  Per 4 codes: one XOR,
 // two byte permutes, two packed subtracts.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void i8x4_to_half2x2(uint32_t codes, half2_t &lo, half2_t &hi)
+//
+// Subtracting 1152 + z instead of 1152 yields q - z, the asymmetric
+// dequantization's integer part, at no extra cost: q - z lies in [-255,
+// 255], and every operand and result of the subtraction is an integer
+// below 2048, so it is exact in fp16.  `bias` holds 1152 + z in both halves
+// (zero_point_bias below).
+__device__ __forceinline__ void i8x4_to_half2x2(uint32_t codes, half2_t &lo, half2_t &hi,
+                                                half2_t bias = (half2_t){(_Float16)1152.0f, (_Float16)1152.0f})
 {
     const uint32_t u = codes ^ 0x80808080u;
     // v_perm_b32: bytes 0..3 come from the second operand, 4..7 from the first.
     const uint32_t plo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u); // [u0,64,u1,64]
     const uint32_t phi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u); // [u2,64,u3,64]
-    const half2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
     lo = __builtin_bit_cast(half2_t, plo) - bias;
     hi = __builtin_bit_cast(half2_t, phi) - bias;
 }
 
-// 16 int8 codes (one 16-byte load) -> 8 packed half2 values, in k order.
-__device__ __forceinline__ void i8x16_to_half2x8(const u32x4_t v, half2_t h[8])
+// The cast bias for zero point z (z = 0: the plain int8 -> fp16 cast).
+__device__ __forceinline__ half2_t zero_point_bias(int z)
 {
-    i8x4_to_half2x2(v.x, h[0], h[1]);
-    i8x4_to_half2x2(v.y, h[2], h[3]);
-    i8x4_to_half2x2(v.z, h[4], h[5]);
-    i8x4_to_half2x2(v.w, h[6], h[7]);
+    const _Float16 b = (_Float16)(float)(1152 + z); // exact: 1024 <= 1152 + z <= 1279
+    return (half2_t){b, b};
+}
+
+// 16 int8 codes (one 16-byte load) -> 8 packed half2 values, in k order.
+__device__ __forceinline__ void i8x16_to_half2x8(const u32x4_t v, half2_t h[8],
+                                                 half2_t bias = (half2_t){(_Float16)1152.0f, (_Float16)1152.0f})
+{
+    i8x4_to_half2x2(v.x, h[0], h[1], bias);
+    i8x4_to_half2x2(v.y, h[2], h[3], bias);
+    i8x4_to_half2x2(v.z, h[4], h[5], bias);
+    i8x4_to_half2x2(v.w, h[6], h[7], bias);
 }
 
 // 8 int8 codes -> one half8 MFMA operand, in k order.
-__device__ __forceinline__ half8_t i8x8_to_half8(uint32_t a, uint32_t b)
+__device__ __forceinline__ half8_t i8x8_to_half8(uint32_t a, uint32_t b,
+                                                 half2_t bias = (half2_t){(_Float16)1152.0f, (_Float16)1152.0f})
 {
     half2_t h0, h1, h2, h3;
-    i8x4_to_half2x2(a, h0, h1);
-    i8x4_to_half2x2(b, h2, h3);
+    i8x4_to_half2x2(a, h0, h1, bias);
+    i8x4_to_half2x2(b, h2, h3, bias);
     half8_t r = {h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
     return r;
 }

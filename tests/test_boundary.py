@@ -30,8 +30,8 @@ def test_header_declares_the_entry_points():
     decl = _declared_functions()
     for name in ("qw_quantize_weights", "qw_quantize_weights_f16", "qw_w8a16_gemm", "qw_w8a16_gemm_path",
                  "qw_w8a16_gemm_auto_path", "qw_w8a16_gemm_mfma_tile", "qw_w8a8_gemm",
-                 "qw_w8a8_gemm_mfma_tile", "qw_quantize_weights_fixed_range", "qw_status_string",
-                 "qw_version"):
+                 "qw_w8a8_gemm_mfma_tile", "qw_quantize_weights_fixed_range", "qw_quantize_weights_asym",
+                 "qw_w8a16_gemm_asym", "qw_w8a16_gemm_asym_path", "qw_status_string", "qw_version"):
         assert name in decl
 
 
@@ -78,6 +78,7 @@ A = 1 << 20      # 16-byte aligned
 B = 2 << 20
 C = 3 << 20
 D = 4 << 20
+E = 5 << 20
 
 
 @pytest.mark.parametrize("args,status", [
@@ -132,6 +133,31 @@ def test_quantize_fixed_range_rejects(args, status):
     assert qw.quantize_weights_fixed_range_raw(*args) == status
 
 
+@pytest.mark.parametrize("args,status", [
+    ((A, -1, 16, B, C, D), qw.QW_ERROR_INVALID_VALUE),              # n < 0
+    ((A, 4, 0, B, C, D), qw.QW_ERROR_INVALID_VALUE),                # k == 0
+    ((A, 4, 16, B, C, 0), qw.QW_ERROR_INVALID_VALUE),               # null zeros
+    ((A, 4, 24, B, C, D), qw.QW_ERROR_UNSUPPORTED),                 # k % 16
+    ((A, 4, 16, B, C, D + 1), qw.QW_ERROR_MISALIGNED),              # zeros
+    ((A, 4, 16, B, C, C), qw.QW_ERROR_INVALID_VALUE),               # zeros overlap scales
+    ((A, 4, 16, B, C, B + 16), qw.QW_ERROR_INVALID_VALUE),          # zeros overlap q
+    ((A, 4, 16, B, C, A + 240), qw.QW_ERROR_INVALID_VALUE),         # zeros inside w
+])
+def test_quantize_asym_rejects(args, status):
+    assert qw.quantize_weights_asym_raw(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, B, C, 0, D, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),         # null zeros
+    ((A, B, C, E + 1, D, 1, 4, 16), qw.QW_ERROR_MISALIGNED),        # zeros
+    ((A, B, C, D, D, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),         # y overlaps zeros
+    ((A, B, C, E, D, 1, 4, 24), qw.QW_ERROR_UNSUPPORTED),           # k % 16
+    ((A, B, C, E, D, -1, 4, 16), qw.QW_ERROR_INVALID_VALUE),
+])
+def test_gemm_asym_rejects(args, status):
+    assert qw.w8a16_gemm_asym_raw(*args) == status
+
+
 def test_quantize_empty_is_noop():
     # n == 0: nothing to do, null pointers allowed
     assert qw.quantize_weights_raw(0, 0, 16, 100.0, 0, 0) == qw.QW_SUCCESS
@@ -160,7 +186,6 @@ def test_gemm_rejects(args, status):
     assert qw.w8a16_gemm_raw(*args) == status
 
 
-E = 5 << 20
 
 
 @pytest.mark.parametrize("args,status", [
