@@ -76,6 +76,13 @@ def _declare(lib):
     lib.oracle_quantize_asym.restype = ctypes.c_int
     lib.oracle_gemm_asym.argtypes = [u16p, i8p, u16p, i8p, i64, i64, i64, f64p]
     lib.oracle_gemm_asym_sampled.argtypes = [u16p, i8p, u16p, i8p, i64, i64p, i64p, i64, f64p]
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.oracle_quantize_outliers.argtypes = [f32p, i64, i64, ctypes.c_double, i8p, u16p, i32p, f32p, i64]
+    lib.oracle_quantize_outliers.restype = ctypes.c_int
+    lib.oracle_outlier_capacity.argtypes = [i64, ctypes.c_double]
+    lib.oracle_outlier_capacity.restype = ctypes.c_int64
+    lib.oracle_gemm_outliers.argtypes = [u16p, i8p, u16p, i32p, f32p, i64, i64, i64, i64, f64p]
+    lib.oracle_gemm_outliers_sampled.argtypes = [u16p, i8p, u16p, i32p, f32p, i64, i64, i64p, i64p, i64, f64p]
     lib.oracle_quantize_fixed.argtypes = [f32p, i64, i64, f32p, i8p, u16p]
     lib.oracle_quantize_fixed.restype = ctypes.c_int
     lib.oracle_w8a8_gemm.argtypes = [i8p, u16p, i8p, u16p, i64, i64, i64, f64p]
@@ -167,6 +174,70 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_quantize_fixed rejected its arguments (rc=%d)" % rc)
         return q, s
+
+    def outlier_capacity(self, k: int, pct: float) -> int:
+        return int(self._l.oracle_outlier_capacity(k, float(pct)))
+
+    def quantize_outliers(self, w, pct: float, cap: int = None):
+        """Outlier-aware quantization: returns (q int8 [n,k], scale bits uint16
+        [n], outlier columns int32 [n,cap] (-1 unused), outlier values float32
+        [n,cap])."""
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        n, k = w.shape
+        if cap is None:
+            cap = self.outlier_capacity(k, pct)
+        q = np.empty((n, k), dtype=np.int8)
+        s = np.empty((n,), dtype=np.uint16)
+        idx = np.empty((n, cap), dtype=np.int32)
+        val = np.empty((n, cap), dtype=np.float32)
+        rc = self._l.oracle_quantize_outliers(_ptr(w, ctypes.c_float), n, k, float(pct), _ptr(q, ctypes.c_int8),
+                                              _ptr(s, ctypes.c_uint16), _ptr(idx, ctypes.c_int32),
+                                              _ptr(val, ctypes.c_float), cap)
+        if rc != 0:
+            raise ValueError("oracle_quantize_outliers rejected its arguments (rc=%d)" % rc)
+        return q, s, idx, val
+
+    def gemm_outliers(self, x_f16, q, s_bits, idx, val) -> np.ndarray:
+        x = np.ascontiguousarray(np.asarray(x_f16, dtype=np.float16)).view(np.uint16)
+        q = np.ascontiguousarray(q, dtype=np.int8)
+        s = np.ascontiguousarray(s_bits, dtype=np.uint16)
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        val = np.ascontiguousarray(val, dtype=np.float32)
+        m, k = x.shape
+        n = q.shape[0]
+        cap = idx.shape[1] if idx.ndim == 2 else 0
+        if q.shape != (n, k) or s.shape != (n,) or idx.shape != (n, cap) or val.shape != (n, cap):
+            raise ValueError("shape mismatch")
+        if cap and (idx.max() >= k or idx.min() < -1):
+            raise IndexError("outlier column out of range")
+        ref = np.empty((m, n), dtype=np.float64)
+        self._l.oracle_gemm_outliers(_ptr(x, ctypes.c_uint16), _ptr(q, ctypes.c_int8), _ptr(s, ctypes.c_uint16),
+                                     _ptr(idx, ctypes.c_int32), _ptr(val, ctypes.c_float), cap, m, n, k,
+                                     _ptr(ref, ctypes.c_double))
+        return ref
+
+    def gemm_outliers_sampled(self, x_f16, q, s_bits, idx, val, mi, ni) -> np.ndarray:
+        x = np.ascontiguousarray(np.asarray(x_f16, dtype=np.float16)).view(np.uint16)
+        q = np.ascontiguousarray(q, dtype=np.int8)
+        s = np.ascontiguousarray(s_bits, dtype=np.uint16)
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        val = np.ascontiguousarray(val, dtype=np.float32)
+        mi = np.ascontiguousarray(mi, dtype=np.int64)
+        ni = np.ascontiguousarray(ni, dtype=np.int64)
+        k = x.shape[1]
+        cap = idx.shape[1]
+        if q.shape[1] != k or mi.shape != ni.shape or idx.shape != (q.shape[0], cap) or val.shape != idx.shape:
+            raise ValueError("shape mismatch")
+        if mi.size and (mi.min() < 0 or mi.max() >= x.shape[0] or ni.min() < 0 or ni.max() >= q.shape[0]):
+            raise IndexError("sample index out of range")
+        if cap and (idx.max() >= k or idx.min() < -1):
+            raise IndexError("outlier column out of range")
+        out = np.empty(mi.shape, dtype=np.float64)
+        self._l.oracle_gemm_outliers_sampled(_ptr(x, ctypes.c_uint16), _ptr(q, ctypes.c_int8),
+                                             _ptr(s, ctypes.c_uint16), _ptr(idx, ctypes.c_int32),
+                                             _ptr(val, ctypes.c_float), cap, k, _ptr(mi, ctypes.c_int64),
+                                             _ptr(ni, ctypes.c_int64), mi.size, _ptr(out, ctypes.c_double))
+        return out
 
     def quantize_asym(self, w):
         """Asymmetric per-row quantization: returns (q int8 [n,k], scale bits
@@ -304,6 +375,22 @@ def quantize(w, pct: float = 100.0):
 
 def quantize_fixed(w, bounds):
     return default().quantize_fixed(w, bounds)
+
+
+def outlier_capacity(k, pct):
+    return default().outlier_capacity(k, pct)
+
+
+def quantize_outliers(w, pct, cap=None):
+    return default().quantize_outliers(w, pct, cap)
+
+
+def gemm_outliers(x_f16, q, s_bits, idx, val):
+    return default().gemm_outliers(x_f16, q, s_bits, idx, val)
+
+
+def gemm_outliers_sampled(x_f16, q, s_bits, idx, val, mi, ni):
+    return default().gemm_outliers_sampled(x_f16, q, s_bits, idx, val, mi, ni)
 
 
 def quantize_asym(w):

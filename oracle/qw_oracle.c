@@ -292,6 +292,67 @@ int oracle_quantize(const float *w, int64_t n, int64_t k, double pct,
     return bad ? -1 : 0;
 }
 
+/* Outlier-aware quantization (dense int8 inliers plus a sparse list of
+ * exact outliers).  Source: GOBO review (nubint.ai), section on the method:
+ * weights are Gaussian apart from a small fraction of outliers (about
+ * 0.1%), which are kept exactly in a side list while the rest is
+ * quantized.  Reading: the outliers of row r are the elements with
+ * |w| > t[r], the row's clip bound (the same bound as oracle_quantize with
+ * the given percentile; pct = 100 has none).  They are stored in the row's
+ * `cap` slots of ol_idx / ol_val in ascending column order (value exact in
+ * binary32; unused slots: index -1, value 0) and their codes are 0; every
+ * other code is the clipped quantizer's.  Rows whose scale is 0 keep no
+ * outliers (all their codes are 0, as in oracle_quantize).  Returns 0, or
+ * -1 for invalid arguments or a row with more than `cap` outliers. */
+int oracle_quantize_outliers(const float *w, int64_t n, int64_t k, double pct, int8_t *q,
+                             uint16_t *scales, int32_t *ol_idx, float *ol_val, int64_t cap)
+{
+    if (cap < 0)
+        return -1;
+    float *thresh = (float *)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+    if (!thresh)
+        return -1;
+    int rc = oracle_quantize(w, n, k, pct, q, scales, thresh);
+    int over = 0;
+    for (int64_t r = 0; rc == 0 && r < n; ++r) {
+        const float *row = w + r * k;
+        int64_t used = 0;
+        for (int64_t e = 0; e < cap; ++e) {
+            ol_idx[r * cap + e] = -1;
+            ol_val[r * cap + e] = 0.0f;
+        }
+        if (oracle_f16_to_f32(scales[r]) == 0.0f)
+            continue;
+        for (int64_t j = 0; j < k; ++j) {
+            if (fabsf(row[j]) > thresh[r]) {
+                if (used == cap) {
+                    over = 1;
+                    break;
+                }
+                ol_idx[r * cap + used] = (int32_t)j;
+                ol_val[r * cap + used] = row[j];
+                q[r * k + j] = 0;
+                ++used;
+            }
+        }
+    }
+    free(thresh);
+    return (rc != 0 || over) ? -1 : 0;
+}
+
+/* Slots per row that always hold a row's outliers: the elements above the
+ * type-7 bound lie among the k - 1 - floor(pos) largest, pos = (pct/100)(k-1)
+ * in binary64; none for pct = 100. */
+int64_t oracle_outlier_capacity(int64_t k, double pct)
+{
+    if (pct == 100.0)
+        return 0;
+    double frac_of_range = pct / 100.0;
+    double pos = frac_of_range * (double)(k - 1);
+    int64_t i = (int64_t)floor(pos);
+    return i >= k - 1 ? 0 : k - 1 - i;
+}
+
 /* Fixed-range clip: the bound of row r is given (bounds[r], finite and
  * >= 0, e.g. a range fixed during training) instead of being measured on
  * the row; the scale and codes then follow exactly as above.  Source:
@@ -415,6 +476,45 @@ void oracle_gemm_sampled(const uint16_t *x, const int8_t *q, const uint16_t *sca
     for (int64_t c = 0; c < count; ++c)
         out[c] = dot_one(x + mi[c] * k, q + ni[c] * k, 0.0,
                          (double)oracle_f16_to_f32(scales[ni[c]]), k);
+}
+
+/* Outlier-aware matmul: the dense int8 part plus the exact outliers,
+ * ref[m][n] = sum_k x[m][k] * (q[n][k] * S[n]) + sum_e x[m][idx[n][e]] * val[n][e]
+ * over the used slots (idx >= 0), in binary64. */
+static double outliers_one(const uint16_t *xrow, const int32_t *idx, const float *val, int64_t cap)
+{
+    double acc = 0.0;
+    for (int64_t e = 0; e < cap; ++e) {
+        if (idx[e] < 0)
+            continue;
+        double xv = (double)oracle_f16_to_f32(xrow[idx[e]]);
+        acc += xv * (double)val[e];
+    }
+    return acc;
+}
+
+void oracle_gemm_outliers(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                          const int32_t *ol_idx, const float *ol_val, int64_t cap,
+                          int64_t m, int64_t n, int64_t k, double *ref)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            const double dense = dot_one(x + i * k, q + j * k, 0.0, (double)oracle_f16_to_f32(scales[j]), k);
+            ref[i * n + j] = dense + outliers_one(x + i * k, ol_idx + j * cap, ol_val + j * cap, cap);
+        }
+}
+
+void oracle_gemm_outliers_sampled(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                                  const int32_t *ol_idx, const float *ol_val, int64_t cap, int64_t k,
+                                  const int64_t *mi, const int64_t *ni, int64_t count, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < count; ++c) {
+        const double dense = dot_one(x + mi[c] * k, q + ni[c] * k, 0.0,
+                                     (double)oracle_f16_to_f32(scales[ni[c]]), k);
+        out[c] = dense + outliers_one(x + mi[c] * k, ol_idx + ni[c] * cap, ol_val + ni[c] * cap, cap);
+    }
 }
 
 /* Asymmetric weights: ref[m][n] = sum_k x[m][k] * ((q[n][k] - z[n]) * S[n]),

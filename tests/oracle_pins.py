@@ -469,6 +469,98 @@ def pin_fixed_range_of_measured_bound(o, seed=16):
 
 
 # --------------------------------------------------------------------------
+# outlier-aware quantizer and matmul
+# --------------------------------------------------------------------------
+
+def _capacity(k, pct):
+    if pct == 100.0:
+        return 0
+    i = math.floor((pct / 100.0) * (k - 1))
+    return 0 if i >= k - 1 else k - 1 - i
+
+
+def pin_outliers_split(o, seed=20):
+    """The side list holds exactly the elements above the (pinned) clip
+    bound, in ascending column order with their exact values; their codes are
+    0 and every other code is the clipped quantizer's; the slot count never
+    exceeds k - 1 - floor(pos)."""
+    rng = np.random.default_rng(seed)
+    for (n, k, pct) in ((6, 1024, 99.99), (5, 4096, 99.9), (7, 48, 90.0), (4, 64, 100.0), (3, 33, 50.0)):
+        w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+        hit = rng.choice(n * k, size=max(1, n * k // 1000), replace=False)
+        w.flat[hit] = (rng.standard_normal(hit.size) * 0.2).astype(np.float32)
+        w[0, : min(k, 8)] = w[0, 0]  # ties at the top of a row
+        cap = _capacity(k, pct)
+        assert o.outlier_capacity(k, pct) == cap
+        q, sb, idx, val = o.quantize_outliers(w, pct)
+        q0, s0, t = o.quantize(w, pct)
+        assert np.array_equal(sb, s0)
+        for r in range(n):
+            if f16_from_bits(sb[r:r + 1])[0] == 0:
+                assert np.all(idx[r] == -1)
+                continue
+            cols = np.nonzero(np.abs(w[r]) > t[r])[0]
+            assert len(cols) <= cap
+            used = idx[r][idx[r] >= 0]
+            assert np.array_equal(used, cols), (r, used, cols)
+            assert np.all(idx[r][len(cols):] == -1) and np.all(val[r][len(cols):] == 0.0)
+            assert np.array_equal(val[r][: len(cols)], w[r][cols])
+            assert np.all(q[r][cols] == 0)
+            keep = np.ones(k, bool)
+            keep[cols] = False
+            assert np.array_equal(q[r][keep], q0[r][keep])
+    if _capacity(64, 90.0) > 0:
+        w = np.linspace(-1, 1, 4 * 64, dtype=np.float32).reshape(4, 64)
+        try:
+            o.quantize_outliers(w, 90.0, cap=_capacity(64, 90.0) - 1)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError("too few slots must be rejected")
+
+
+def pin_gemm_outliers(o, seed=21):
+    """The reference is the (pinned) dense W8A16 reference plus the side
+    list's products (numpy binary64), and exact on exact inputs."""
+    rng = np.random.default_rng(seed)
+    m, n, k, cap = 5, 24, 256, 3
+    x = rng.standard_normal((m, k)).astype(np.float16)
+    q = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+    s = rng.uniform(1e-4, 1e-2, size=n).astype(np.float16).view(np.uint16)
+    idx = np.full((n, cap), -1, dtype=np.int32)
+    val = np.zeros((n, cap), dtype=np.float32)
+    for r in range(n):
+        c = int(rng.integers(0, cap + 1))
+        idx[r, :c] = np.sort(rng.choice(k, size=c, replace=False))
+        val[r, :c] = rng.standard_normal(c) * 0.5
+    ref = o.gemm_outliers(x, q, s, idx, val)
+    side = np.zeros((m, n))
+    xd = x.astype(np.float64)
+    for r in range(n):
+        for e in range(cap):
+            if idx[r, e] >= 0:
+                side[:, r] += xd[:, idx[r, e]] * float(val[r, e])
+    want = o.gemm(x, q, s) + side
+    assert np.abs(ref - want).max() <= 1e-12 * max(1.0, np.abs(want).max())
+    mi = rng.integers(0, m, size=19)
+    ni = rng.integers(0, n, size=19)
+    assert np.array_equal(o.gemm_outliers_sampled(x, q, s, idx, val, mi, ni), ref[mi, ni])
+    xi = rng.integers(-1, 2, size=(m, k)).astype(np.float16)
+    e = rng.integers(0, 11, size=n)
+    sp = (2.0 ** (-e)).astype(np.float16).view(np.uint16)
+    vd = (rng.integers(-512, 512, size=(n, cap)) / 64.0).astype(np.float32)
+    vd[idx < 0] = 0.0
+    ref2 = o.gemm_outliers(xi, q, sp, idx, vd)
+    dense = np.ldexp((xi.astype(np.int64) @ q.astype(np.int64).T).astype(np.float64), -e[None, :])
+    side2 = np.zeros((m, n))
+    for r in range(n):
+        for c in range(cap):
+            if idx[r, c] >= 0:
+                side2[:, r] += xi[:, idx[r, c]].astype(np.float64) * float(vd[r, c])
+    assert np.array_equal(ref2, dense + side2)
+
+
+# --------------------------------------------------------------------------
 # asymmetric (zero-point) quantizer and matmul
 # --------------------------------------------------------------------------
 
@@ -650,6 +742,8 @@ FAST_PINS = (
     pin_cosine_vs_unquantized,
     pin_fixed_range_bruteforce,
     pin_fixed_range_of_measured_bound,
+    pin_outliers_split,
+    pin_gemm_outliers,
     pin_asym_quantize_bruteforce,
     pin_asym_quantize_invariants,
     pin_gemm_asym,

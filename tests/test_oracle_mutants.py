@@ -47,6 +47,12 @@ MUTANTS = {
                         "double xv = (double)oracle_f16_to_f32(xrow[k - 1 - j]);"),
     "gemm_scale_of_wrong_row": ("ref[i * n + j] = dot_one(x + i * k, q + j * k, 0.0,\n                                     (double)oracle_f16_to_f32(scales[j]), k);",
                                 "ref[i * n + j] = dot_one(x + i * k, q + j * k, 0.0,\n                                     (double)oracle_f16_to_f32(scales[i % n]), k);"),
+    # outlier-aware quantizer and matmul
+    "outliers_at_bound": ("if (fabsf(row[j]) > thresh[r]) {", "if (fabsf(row[j]) >= thresh[r]) {"),
+    "outliers_keep_code": ("                q[r * k + j] = 0;\n                ++used;", "                ++used;"),
+    "gemm_outliers_dropped": ("acc += xv * (double)val[e];", "acc += 0.0 * xv * (double)val[e];"),
+    "gemm_outliers_wrong_column": ("double xv = (double)oracle_f16_to_f32(xrow[idx[e]]);",
+                                   "double xv = (double)oracle_f16_to_f32(xrow[e]);"),
     # asymmetric quantizer and matmul
     "asym_divide_by_256": ("float s32 = range / 255.0f;", "float s32 = range / 256.0f;"),
     "asym_range_without_zero": ("float hi = 0.0f, lo = 0.0f;", "float hi = -INFINITY, lo = INFINITY;"),
