@@ -231,6 +231,56 @@ def time_w8a8(wl, launches=40, warmup=10):
             "act_quantize_plus_gemm_us": pair_ms * 1e3}
 
 
+class OutlierRunner:
+    """Rotating operand sets for the outlier-aware W8A16 GEMM: weights
+    quantized once with side lists (the library's quantizer)."""
+
+    def __init__(self, wl, sets):
+        import torch
+
+        import int8_weight_quantized_amd as qw
+        import synthetic
+        self.qw, self.torch, self.wl, self.sets = qw, torch, wl, sets
+        x, w = synthetic.make_inputs(wl)
+        dev = "cuda:0"
+        xd = torch.from_numpy(x).to(dev)
+        self.x = [xd] + [xd.clone() for _ in range(sets - 1)]
+        wd = torch.from_numpy(w).to(dev)
+        q0, s0, i0, v0 = qw.quantize_weights_outliers(wd, wl.clip_percentile)
+        del wd
+        self.cap = i0.shape[1]
+        self.q = [q0] + [q0.clone() for _ in range(sets - 1)]
+        self.s = [s0] + [s0.clone() for _ in range(sets - 1)]
+        self.i = [i0.contiguous()] + [i0.contiguous().clone() for _ in range(sets - 1)]
+        self.v = [v0.contiguous()] + [v0.contiguous().clone() for _ in range(sets - 1)]
+        self.y = [torch.empty((wl.m, wl.n), dtype=torch.float16, device=dev) for _ in range(sets)]
+        self.stream = int(torch.cuda.current_stream().cuda_stream)
+
+    def gemm(self, i):
+        wl = self.wl
+        st = self.qw.w8a16_gemm_outliers_raw(self.x[i].data_ptr(), self.q[i].data_ptr(), self.s[i].data_ptr(),
+                                             self.i[i].data_ptr(), self.v[i].data_ptr(), self.cap,
+                                             self.y[i].data_ptr(), wl.m, wl.n, wl.k, self.stream, 0)
+        if st:
+            raise RuntimeError(self.qw.status_string(st))
+
+
+def time_outliers(wl, launches=40, warmup=10):
+    """Cold figures of the outlier-aware GEMM (dense int8 part plus exact side
+    lists) on one workload."""
+    import torch
+    r = OutlierRunner(wl, rotation_count(gemm_bytes(wl.m, wl.n, wl.k)))
+    avg_ms, med_ms = time_gemm_only(r, launches, warmup)
+    fl = gemm_flops(wl.m, wl.n, wl.k)
+    out = {"workload": wl.name, "kernel": gemm_kernel_name(wl.m, wl.n, wl.k) + "+outliers",
+           "slots_per_row": r.cap, "cold_sets": r.sets, "avg_us": avg_ms * 1e3, "median_us": med_ms * 1e3,
+           "TFLOPs": fl / (avg_ms * 1e-3) / 1e12,
+           "mfma_frac": fl / (avg_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS}
+    del r
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_full_steps(runner, steps, warmup):
     """Warm up, then time exactly `steps` steps bracketed by synchronizations;
     HIP events on the launch stream time each kernel inside the region."""
@@ -450,6 +500,10 @@ def main():
                      "transformer_big_ffn_outliers_m4096_k1024_n4096"):
             w8a8.append(time_w8a8(synthetic.BY_NAME[name]))
 
+    outl = []
+    if not args.no_secondary and not args.only_step:
+        outl.append(time_outliers(synthetic.BY_NAME["transformer_big_ffn_outliers_m4096_k1024_n4096"]))
+
     result = {
         "metric": METRIC,
         "value": value,
@@ -470,6 +524,7 @@ def main():
         "kernels": kernels,
         "gemm_cold": secondary,
         "w8a8_cold": w8a8,
+        "outliers_cold": outl,
     }
     if not args.no_cpu_baseline and not args.only_step:
         result["cpu_baseline"] = cpu_baseline(wl)

@@ -148,6 +148,81 @@ QW_API qw_status qw_quantize_weights_fixed_range(const float *w, int64_t n, int6
                                                  uint16_t *scales, void *stream);
 
 /*
+ * qw_outlier_capacity -- side-list slots per row that always hold the
+ * outliers of qw_quantize_weights_outliers for this row length and clip
+ * percentile: k - 1 - floor(pos), pos = (clip_percentile / 100) * (k - 1) in
+ * binary64 (the elements above the type-7 bound are among the k - 1 - i
+ * largest); 0 for clip_percentile = 100.  Returns -1 for k <= 0 or a
+ * percentile outside (0, 100].
+ */
+QW_API int64_t qw_outlier_capacity(int64_t k, double clip_percentile);
+
+/*
+ * qw_quantize_weights_outliers -- outlier-aware quantization: dense int8
+ * codes for the inliers plus an exact side list of the outliers.
+ *
+ * Source: GOBO review (nubint.ai), method section: Transformer weights are
+ * Gaussian apart from a small fraction of outliers (about 0.1%), which are
+ * kept at full precision in a side list while the rest is quantized.  The
+ * outliers of row r are the elements with |w| > t[r], the clip bound of
+ * qw_quantize_weights with the same clip_percentile; the scale and the
+ * other codes are exactly qw_quantize_weights's, the outliers' codes are 0.
+ * Rows whose scale is 0 keep no outliers (their codes are all 0).
+ *
+ *   w, n, k, clip_percentile, q, scales, stream as qw_quantize_weights
+ *   ol_idx  int32 [n][cap] (written): the row's outlier columns in
+ *           ascending order, then -1 in the unused slots
+ *   ol_val  fp32 [n][cap] (written): the outliers' values, exact; 0 in the
+ *           unused slots
+ *   cap     slots per row, qw_outlier_capacity(k, clip_percentile) <= cap
+ *           <= k (cap == 0 is allowed when the capacity is 0)
+ *
+ * Errors: as qw_quantize_weights, plus QW_ERROR_INVALID_VALUE for cap below
+ * the capacity or above k, null side-list pointers, or side lists
+ * overlapping w, q, scales or each other, and QW_ERROR_MISALIGNED for
+ * misaligned side lists.
+ */
+QW_API qw_status qw_quantize_weights_outliers(const float *w, int64_t n, int64_t k,
+                                              double clip_percentile, int8_t *q,
+                                              uint16_t *scales, int32_t *ol_idx, float *ol_val,
+                                              int64_t cap, void *stream);
+
+/*
+ * qw_w8a16_gemm_outliers -- W8A16 plus the exact outlier side lists:
+ *
+ *   Y[i][c] = binary16_RNE( S[c] * sum_j X[i][j] * q[c][j]
+ *                           + sum_e X[i][ol_idx[c][e]] * ol_val[c][e] )
+ *
+ * over the used slots, in fp32 (the GOBO reading above: the dense int8
+ * part plus the full-precision outliers).  The GEMV and skinny kernels add
+ * the side list in their epilogues; the MFMA kernel adds it (in units of
+ * S[c], value / S[c] in binary32) while the activation columns pass through
+ * LDS, for up to 4 slots per row (wider lists run on the skinny kernel, and
+ * QW_PATH_MFMA with more than 4 slots is QW_ERROR_UNSUPPORTED).  Accuracy
+ * contract as qw_w8a16_gemm.
+ *
+ *   ol_idx, ol_val, cap  as written by qw_quantize_weights_outliers: used
+ *           slots first, columns ascending and < k (columns outside [0, k)
+ *           end the row's list; entries out of order may be skipped by the
+ *           MFMA kernel); rows with S[c] == 0 must have no used slots
+ *   (other arguments as qw_w8a16_gemm; cap == 0 is the plain GEMM)
+ *
+ * Errors: as qw_w8a16_gemm, plus QW_ERROR_INVALID_VALUE for cap < 0 or
+ * cap > k, null side lists with cap > 0, or y overlapping them, and
+ * QW_ERROR_MISALIGNED for misaligned side lists.
+ * qw_w8a16_gemm_outliers_path forces the kernel as qw_w8a16_gemm_path does.
+ */
+QW_API qw_status qw_w8a16_gemm_outliers(const uint16_t *x, const int8_t *q,
+                                        const uint16_t *scales, const int32_t *ol_idx,
+                                        const float *ol_val, int64_t cap, uint16_t *y,
+                                        int64_t m, int64_t n, int64_t k, void *stream);
+QW_API qw_status qw_w8a16_gemm_outliers_path(const uint16_t *x, const int8_t *q,
+                                             const uint16_t *scales, const int32_t *ol_idx,
+                                             const float *ol_val, int64_t cap, uint16_t *y,
+                                             int64_t m, int64_t n, int64_t k, int path,
+                                             void *stream);
+
+/*
  * qw_quantize_weights_asym -- asymmetric (zero-point) per-row int8
  * quantization.
  *

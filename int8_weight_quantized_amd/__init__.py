@@ -72,6 +72,14 @@ def _load():
     lib.qw_quantize_weights_f16.restype = ctypes.c_int
     lib.qw_quantize_weights_fixed_range.argtypes = [vp, i64, i64, vp, vp, vp, vp]
     lib.qw_quantize_weights_fixed_range.restype = ctypes.c_int
+    lib.qw_outlier_capacity.argtypes = [i64, ctypes.c_double]
+    lib.qw_outlier_capacity.restype = ctypes.c_int64
+    lib.qw_quantize_weights_outliers.argtypes = [vp, i64, i64, ctypes.c_double, vp, vp, vp, vp, i64, vp]
+    lib.qw_quantize_weights_outliers.restype = ctypes.c_int
+    lib.qw_w8a16_gemm_outliers.argtypes = [vp, vp, vp, vp, vp, i64, vp, i64, i64, i64, vp]
+    lib.qw_w8a16_gemm_outliers.restype = ctypes.c_int
+    lib.qw_w8a16_gemm_outliers_path.argtypes = [vp, vp, vp, vp, vp, i64, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.qw_w8a16_gemm_outliers_path.restype = ctypes.c_int
     lib.qw_quantize_weights_asym.argtypes = [vp, i64, i64, vp, vp, vp, vp]
     lib.qw_quantize_weights_asym.restype = ctypes.c_int
     lib.qw_w8a16_gemm_asym.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
@@ -157,6 +165,26 @@ def quantize_weights_f16_raw(w_ptr: int, n: int, k: int, clip_percentile: float,
 def quantize_weights_fixed_range_raw(w_ptr: int, n: int, k: int, bounds_ptr: int, q_ptr: int, s_ptr: int,
                                      stream: int = 0) -> int:
     return int(library().qw_quantize_weights_fixed_range(w_ptr, n, k, bounds_ptr, q_ptr, s_ptr, stream))
+
+
+def outlier_capacity(k: int, clip_percentile: float) -> int:
+    """Side-list slots per row that always hold the outliers (host only)."""
+    c = int(library().qw_outlier_capacity(k, float(clip_percentile)))
+    if c < 0:
+        raise ValueError("bad k or clip percentile")
+    return c
+
+
+def quantize_weights_outliers_raw(w_ptr: int, n: int, k: int, clip_percentile: float, q_ptr: int, s_ptr: int,
+                                  idx_ptr: int, val_ptr: int, cap: int, stream: int = 0) -> int:
+    return int(library().qw_quantize_weights_outliers(w_ptr, n, k, float(clip_percentile), q_ptr, s_ptr, idx_ptr,
+                                                      val_ptr, cap, stream))
+
+
+def w8a16_gemm_outliers_raw(x_ptr: int, q_ptr: int, s_ptr: int, idx_ptr: int, val_ptr: int, cap: int, y_ptr: int,
+                            m: int, n: int, k: int, stream: int = 0, path: int = 0) -> int:
+    return int(library().qw_w8a16_gemm_outliers_path(x_ptr, q_ptr, s_ptr, idx_ptr, val_ptr, cap, y_ptr, m, n, k,
+                                                     int(path), stream))
 
 
 def quantize_weights_asym_raw(w_ptr: int, n: int, k: int, q_ptr: int, s_ptr: int, z_ptr: int,
@@ -285,6 +313,51 @@ def quantize_weights_fixed_range(w, bounds, out=None):
     return q, s
 
 
+def quantize_weights_outliers(w, clip_percentile: float):
+    """Outlier-aware quantization of a cuda float32 [N, K] weight: returns
+    (q int8 [N, K], scales float16 [N], ol_idx int32 [N, C], ol_val float32
+    [N, C]) with C = outlier_capacity(K, clip_percentile)."""
+    torch = _torch()
+    _check(w, "w", torch.float32, 2)
+    n, k = w.shape
+    cap = outlier_capacity(k, clip_percentile)
+    q = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    s = torch.empty((n,), dtype=torch.float16, device=w.device)
+    idx = torch.empty((n, max(cap, 1)), dtype=torch.int32, device=w.device)[:, :cap]
+    val = torch.empty((n, max(cap, 1)), dtype=torch.float32, device=w.device)[:, :cap]
+    st = quantize_weights_outliers_raw(w.data_ptr(), n, k, clip_percentile, q.data_ptr(), s.data_ptr(),
+                                       idx.data_ptr(), val.data_ptr(), cap, _stream_of(w))
+    if st != QW_SUCCESS:
+        raise QwError(st, "qw_quantize_weights_outliers")
+    return q, s, idx, val
+
+
+def w8a16_gemm_outliers(x, q, scales, ol_idx, ol_val, out=None, path: str = "auto"):
+    """Y = X * dequant(q)^T plus the exact outlier side lists: x cuda fp16
+    [M, K], q int8 [N, K], scales fp16 [N], ol_idx int32 [N, C], ol_val
+    float32 [N, C] -> fp16 [M, N]."""
+    torch = _torch()
+    _check(x, "x", torch.float16, 2)
+    _check(q, "q", torch.int8, 2)
+    _check(scales, "scales", torch.float16, 1)
+    m, k = x.shape
+    n = q.shape[0]
+    cap = ol_idx.shape[1]
+    if ol_idx.dtype != torch.int32 or ol_val.dtype != torch.float32 or tuple(ol_val.shape) != (n, cap) \
+            or tuple(ol_idx.shape) != (n, cap) or not ol_idx.is_contiguous() or not ol_val.is_contiguous():
+        raise ValueError("side lists must be contiguous int32 / float32 [N, C]")
+    if q.shape[1] != k or scales.shape[0] != n:
+        raise ValueError("shape mismatch")
+    y = torch.empty((m, n), dtype=torch.float16, device=x.device) if out is None else out
+    if path not in PATHS:
+        raise ValueError("path must be one of %s" % sorted(PATHS))
+    st = w8a16_gemm_outliers_raw(x.data_ptr(), q.data_ptr(), scales.data_ptr(), ol_idx.data_ptr(),
+                                 ol_val.data_ptr(), cap, y.data_ptr(), m, n, k, _stream_of(x), PATHS[path])
+    if st != QW_SUCCESS:
+        raise QwError(st, "qw_w8a16_gemm_outliers")
+    return y
+
+
 def quantize_weights_asym(w):
     """Asymmetric per-row int8 quantization of a cuda float32 [N, K] weight:
     returns (q int8 [N, K], scales float16 [N], zeros int8 [N]) with
@@ -358,7 +431,9 @@ def w8a8_gemm(qx, sx, q, scales, out=None):
 
 
 __all__ = ["quantize_weights", "quantize_weights_fixed_range", "quantize_weights_asym", "w8a16_gemm_asym",
+           "quantize_weights_outliers", "w8a16_gemm_outliers", "outlier_capacity",
            "quantize_activations", "w8a16_gemm", "w8a8_gemm", "QwError",
            "status_string", "version", "library", "auto_path", "mfma_tile", "w8a8_tile",
-           "quantize_weights_raw", "quantize_weights_f16_raw", "quantize_weights_fixed_range_raw", "quantize_weights_asym_raw", "w8a16_gemm_asym_raw", "w8a16_gemm_raw", "w8a8_gemm_raw",
+           "quantize_weights_raw", "quantize_weights_f16_raw", "quantize_weights_fixed_range_raw", "quantize_weights_asym_raw", "w8a16_gemm_asym_raw",
+           "quantize_weights_outliers_raw", "w8a16_gemm_outliers_raw", "w8a16_gemm_raw", "w8a8_gemm_raw",
            "PATHS", "LIBRARY_PATH"]

@@ -35,9 +35,19 @@ namespace {
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 typedef int int4v __attribute__((ext_vector_type(4)));
+typedef int int2v __attribute__((ext_vector_type(2)));
 typedef int int16v __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 64; // k per step
+
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks)
 {
@@ -150,13 +160,14 @@ using stage_t = std::integral_constant<int, I>;
 // A8 (W8A8): x holds int8 activation codes with one fp16 scale per row in
 // sx; the MFMA is v_mfma_i32_32x32x32_i8 with exact int32 accumulators and
 // the epilogue multiplies by S[n] * Sx[m].  Otherwise x is fp16 and sx is
-// unused.
-template <int NW, int BN, int BM, bool A8>
+// unused.  OL: exact outlier side lists (at most kMfmaOutlierSlots per
+// weight row) are added while their activation column sits in LDS.
+template <int NW, int BN, int BM, bool A8, bool OL = false>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm_dma_kernel(
     const void *__restrict__ xv, const uint16_t *__restrict__ sx, const int8_t *__restrict__ q,
-    const uint16_t *__restrict__ scales, const int8_t *__restrict__ zeros, uint16_t *__restrict__ y,
-    int m, int n, int k, int tiles_m, int tiles_n)
+    const uint16_t *__restrict__ scales, const int8_t *__restrict__ zeros, OutlierList ol,
+    uint16_t *__restrict__ y, int m, int n, int k, int tiles_m, int tiles_n)
 {
     using C = DmaCfg<NW, BN, BM, A8>;
     constexpr int kSJ = C::kSJ;
@@ -166,6 +177,9 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
     __shared__ __attribute__((aligned(1024))) uint8_t ring1[C::kStageAlloc];
     __shared__ __attribute__((aligned(16))) float scale_lds[BN];
     __shared__ __attribute__((aligned(16))) float xscale_lds[A8 ? BM : 1];
+    // OL: the workgroup's side lists, (column, value / S as float bits) per
+    // slot; unused slots hold column INT_MAX
+    __shared__ __attribute__((aligned(16))) int2v ol_lds[OL ? BN * kMfmaOutlierSlots : 1];
     auto ring = [&](auto s) -> uint8_t * {
         if constexpr (decltype(s)::value == 0)
             return ring0;
@@ -352,6 +366,82 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
         for (int r = tid; r < BM; r += C::kThreads)
             xscale_lds[r] = m0 + r < m ? f16_bits_to_f32(sx[m0 + r]) : 0.0f;
     }
+    // Outliers are accumulated in code units (value / S, binary32), like the
+    // dense products, so the epilogue's single multiply by S covers both.
+    if constexpr (OL) {
+        for (int e = tid; e < BN * kMfmaOutlierSlots; e += C::kThreads) {
+            const int c = e / kMfmaOutlierSlots, slot = e % kMfmaOutlierSlots;
+            int col = 0x7fffffff;
+            float o = 0.0f;
+            if (n0 + c < n && slot < ol.cap) {
+                const int64_t at = (int64_t)(n0 + c) * ol.cap + slot;
+                const int kk = ol.idx[at];
+                if (kk >= 0 && kk < k) {
+                    col = kk;
+                    o = __fdiv_rn(ol.val[at], f16_bits_to_f32(scales[n0 + c]));
+                }
+            }
+            ol_lds[e] = (int2v){col, __builtin_bit_cast(int, o)};
+        }
+    }
+    // lane l < kWaveN walks the side list of its wave's channel l in column
+    // order; ocur is its next slot
+    int ocur = 0;
+
+    // Add x[row][col] * o for each outlier (channel c of this wave, column
+    // col) of the current k step to the accumulators of every activation row
+    // of the tile.  Channel c's accumulator is register
+    // R = 4 ((c % 32) / 8) + c % 4 of MFMA tile I = c / 32 in the lanes whose
+    // group l / 32 is (c % 8) / 4, one row 32 j + l % 32 per tile row j.  So
+    // that every register index is a compile-time constant, the (I, R) pairs
+    // with a hit are collected in a wave-uniform mask and visited in a fixed
+    // unrolled order; in pair (I, R) each lane fetches its half's channel's
+    // entry from the owning lane.
+    auto add_outliers = [&](int t, const uint8_t *st) __attribute__((always_inline)) {
+        const int kend = (t + 1) * kBK; // every slot still ahead has column >= t * kBK
+        const bool own = lane < C::kWaveN;
+        const int cl = wave * C::kWaveN + lane;
+        for (;;) {
+            int2v ent = {0x7fffffff, 0};
+            if (own && ocur < kMfmaOutlierSlots)
+                ent = ol_lds[cl * kMfmaOutlierSlots + ocur];
+            const bool hit = ent.x < kend;
+            const uint64_t hits = __builtin_amdgcn_ballot_w64(hit);
+            if (hits == 0)
+                break;
+            uint32_t pairs = 0;
+            for (uint64_t rest = hits; rest != 0; rest &= rest - 1) {
+                const int c = __builtin_ctzll(rest);
+                pairs |= 1u << ((c / 32) * 16 + 4 * ((c % 32) / 8) + c % 4);
+            }
+            // lane-dependent part of the source lane, made opaque here so that
+            // the per-pair arithmetic is not hoisted out of the loop (32 live
+            // values would not fit beside the accumulators)
+            int half4 = 4 * lgrp;
+            __asm__ volatile("" : "+v"(half4));
+            static_for<0, C::kSI * 16>([&](auto G) {
+                constexpr int kI = decltype(G)::value / 16, kR = decltype(G)::value % 16;
+                if (pairs & (1u << decltype(G)::value)) {
+                    const int src = half4 + (32 * kI + 8 * (kR / 4) + kR % 4);
+                    const int col = __builtin_amdgcn_ds_bpermute(src * 4, ent.x) - t * kBK;
+                    const float o = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src * 4, ent.y));
+                    // (col < 0 only for a list out of column order: skipped,
+                    // never read outside the stage)
+                    if (((hits >> src) & 1u) && col >= 0) {
+#pragma unroll
+                        for (int j = 0; j < kSJ; ++j) {
+                            const int xr = 32 * j + lrow;
+                            const uint8_t *px = st + C::kWBytes + xr * 2 * kBK +
+                                                16 * ((col / 8) ^ (half4 >= 0 ? xslot(xr) : 0)) + 2 * (col % 8);
+                            acc[kI][j][kR] += (float)*reinterpret_cast<const _Float16 *>(px) * o;
+                        }
+                    }
+                }
+            });
+            if (hit)
+                ++ocur;
+        }
+    };
 
     // Step t (stage t % 2) waits for its own copies of tile t, the barrier
     // publishes everyone's copies and certifies that tile t-1's stage is no
@@ -368,6 +458,8 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
         // whole step, right before the wait for them
         __builtin_amdgcn_sched_barrier(0);
         compute(ring(s));
+        if constexpr (OL)
+            add_outliers(t, ring(s));
     };
     // steady state: pairs of steps whose next tile is full
     int t = 0;
@@ -449,15 +541,30 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
 
 template <int NW, int BN, int BM, bool A8>
 hipError_t launch_dma(const void *x, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
-                      const int8_t *zeros, uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
+                      const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                      hipStream_t stream)
 {
     const int64_t tiles_m = (m + BM - 1) / BM;
     const int64_t tiles_n = (n + BN - 1) / BN;
     const int64_t blocks = tiles_m * tiles_n;
     if (blocks > 0x7fffffff)
         return hipErrorInvalidConfiguration;
+    // side lists: not with the 256 x 128 tile (its registers are nearly all
+    // taken by accumulators and operands; the launcher maps it to 256 x 64)
+    if constexpr (!A8 && !(BN == 256 && BM == 128)) {
+        if (ol.idx != nullptr) {
+            if (ol.cap > kMfmaOutlierSlots)
+                return hipErrorInvalidValue;
+            hipLaunchKernelGGL((mfma_gemm_dma_kernel<NW, BN, BM, false, true>), dim3((unsigned)blocks),
+                               dim3(NW * kWave), 0, stream, x, sx, q, scales, zeros, ol, y, (int)m, (int)n,
+                               (int)k, (int)tiles_m, (int)tiles_n);
+            return hipGetLastError();
+        }
+    }
+    if (ol.idx != nullptr)
+        return hipErrorInvalidValue;
     hipLaunchKernelGGL((mfma_gemm_dma_kernel<NW, BN, BM, A8>), dim3((unsigned)blocks), dim3(NW * kWave),
-                       0, stream, x, sx, q, scales, zeros, y, (int)m, (int)n, (int)k, (int)tiles_m,
+                       0, stream, x, sx, q, scales, zeros, ol, y, (int)m, (int)n, (int)k, (int)tiles_m,
                        (int)tiles_n);
     return hipGetLastError();
 }
@@ -508,20 +615,23 @@ int tile_choice(int64_t m, int64_t n)
 
 template <bool A8>
 hipError_t launch_tiles(const void *x, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
-                        const int8_t *zeros, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                        const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k,
                         hipStream_t stream)
 {
-    switch (tile_choice<A8>(m, n)) {
+    int tile = tile_choice<A8>(m, n);
+    if (ol.idx != nullptr && tile == 256128)
+        tile = 256064;
+    switch (tile) {
     case 256128:
-        return launch_dma<4, 256, 128, A8>(x, sx, q, scales, zeros, y, m, n, k, stream);
+        return launch_dma<4, 256, 128, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
     case 256064:
-        return launch_dma<4, 256, 64, A8>(x, sx, q, scales, zeros, y, m, n, k, stream);
+        return launch_dma<4, 256, 64, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
     case 128128:
         if constexpr (!A8)
-            return launch_dma<4, 128, 128, A8>(x, sx, q, scales, zeros, y, m, n, k, stream);
+            return launch_dma<4, 128, 128, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
         [[fallthrough]];
     default:
-        return launch_dma<4, 128, 64, A8>(x, sx, q, scales, zeros, y, m, n, k, stream);
+        return launch_dma<4, 128, 64, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
     }
 }
 
@@ -538,17 +648,17 @@ int w8a8_tile_choice(int64_t m, int64_t n)
 }
 
 hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
-                            const int8_t *zeros, uint16_t *y, int64_t m, int64_t n, int64_t k,
-                            hipStream_t stream)
+                            const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n,
+                            int64_t k, hipStream_t stream)
 {
-    return launch_tiles<false>(x, nullptr, q, scales, zeros, y, m, n, k, stream);
+    return launch_tiles<false>(x, nullptr, q, scales, zeros, ol, y, m, n, k, stream);
 }
 
 hipError_t launch_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t *q,
                             const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
                             hipStream_t stream)
 {
-    return launch_tiles<true>(qx, sx, q, scales, nullptr, y, m, n, k, stream);
+    return launch_tiles<true>(qx, sx, q, scales, nullptr, OutlierList{nullptr, nullptr, 0}, y, m, n, k, stream);
 }
 
 } // namespace qw

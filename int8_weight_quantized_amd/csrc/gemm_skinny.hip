@@ -41,8 +41,8 @@ constexpr int kSkinnyTargetWaves = 2048; // enough in-flight loads to fill HBM
 template <int RT, int KSPLIT>
 __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
     const uint16_t *__restrict__ x, const int8_t *__restrict__ q,
-    const uint16_t *__restrict__ scales, const int8_t *__restrict__ zeros, uint16_t *__restrict__ y,
-    int m, int n, int k)
+    const uint16_t *__restrict__ scales, const int8_t *__restrict__ zeros, OutlierList ol,
+    uint16_t *__restrict__ y, int m, int n, int k)
 {
     // Per wave, a staging slice for the weight codes of one iteration:
     // [tile][row][256 bytes + 16 pad].  After the main loop the same memory
@@ -188,8 +188,21 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            ytile[r][16 * t + 4 * g + i] = f32_to_f16_bits(acc[t][i] * f16_bits_to_f32(sc[t][i]));
+        for (int i = 0; i < 4; ++i) {
+            float out = acc[t][i] * f16_bits_to_f32(sc[t][i]);
+            // exact outliers of channel n0 + 16 t + 4 g + i, with X read
+            // from global memory (a few activation rows: L2-resident)
+            const int yn = n0 + 16 * t + 4 * g + i;
+            if (ol.idx != nullptr && yn < n && col_ok) {
+                for (int e = 0; e < ol.cap; ++e) {
+                    const int kk = ol.idx[(int64_t)yn * ol.cap + e];
+                    if (kk < 0 || kk >= k)
+                        break; // used slots come first
+                    out += f16_bits_to_f32(xrow[kk]) * ol.val[(int64_t)yn * ol.cap + e];
+                }
+            }
+            ytile[r][16 * t + 4 * g + i] = f32_to_f16_bits(out);
+        }
     // the tile is written and read back by the same wave: LDS keeps a
     // wave's accesses in order; the barrier only stops the compiler from
     // moving the reads above the writes
@@ -215,17 +228,19 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
 }
 
 template <int RT, int KSPLIT>
-hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros, uint16_t *y,
+hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros,
+                      OutlierList ol, uint16_t *y,
                       int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
     const dim3 grid((unsigned)((n + 16 * RT - 1) / (16 * RT)), (unsigned)((m + 15) / 16));
     hipLaunchKernelGGL((skinny_gemm_kernel<RT, KSPLIT>), grid, dim3(KSPLIT * kWave), 0, stream,
-                       x, q, scales, zeros, y, (int)m, (int)n, (int)k);
+                       x, q, scales, zeros, ol, y, (int)m, (int)n, (int)k);
     return hipGetLastError();
 }
 
 template <int RT>
-hipError_t launch_rt(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros, uint16_t *y,
+hipError_t launch_rt(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros,
+                     OutlierList ol, uint16_t *y,
                      int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
     // split k until the grid holds about kSkinnyTargetWaves waves, keeping
@@ -237,27 +252,27 @@ hipError_t launch_rt(const uint16_t *x, const int8_t *q, const uint16_t *scales,
         ksplit *= 2;
     switch (ksplit) {
     case 1:
-        return launch_cfg<RT, 1>(x, q, scales, zeros, y, m, n, k, stream);
+        return launch_cfg<RT, 1>(x, q, scales, zeros, ol, y, m, n, k, stream);
     case 2:
-        return launch_cfg<RT, 2>(x, q, scales, zeros, y, m, n, k, stream);
+        return launch_cfg<RT, 2>(x, q, scales, zeros, ol, y, m, n, k, stream);
     case 4:
-        return launch_cfg<RT, 4>(x, q, scales, zeros, y, m, n, k, stream);
+        return launch_cfg<RT, 4>(x, q, scales, zeros, ol, y, m, n, k, stream);
     case 8:
-        return launch_cfg<RT, 8>(x, q, scales, zeros, y, m, n, k, stream);
+        return launch_cfg<RT, 8>(x, q, scales, zeros, ol, y, m, n, k, stream);
     default:
-        return launch_cfg<RT, 16>(x, q, scales, zeros, y, m, n, k, stream);
+        return launch_cfg<RT, 16>(x, q, scales, zeros, ol, y, m, n, k, stream);
     }
 }
 
 } // namespace
 
 hipError_t launch_skinny_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
-                              const int8_t *zeros, uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
+                              const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
     // two 16-row weight tiles per wave: the activation operand is reused
     // twice; four tiles measured slower (fewer waves, longer dependent
     // MFMA chains)
-    return launch_rt<2>(x, q, scales, zeros, y, m, n, k, stream);
+    return launch_rt<2>(x, q, scales, zeros, ol, y, m, n, k, stream);
 }
 
 } // namespace qw

@@ -45,8 +45,8 @@ struct GemvItem {
 template <int MT, int RU, int CH>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     const uint16_t *__restrict__ x, const int8_t *__restrict__ q,
-    const uint16_t *__restrict__ scales, const int8_t *__restrict__ zeros, uint16_t *__restrict__ y,
-    int m, int n, int k, int chunks, int total_waves)
+    const uint16_t *__restrict__ scales, const int8_t *__restrict__ zeros, OutlierList ol,
+    uint16_t *__restrict__ y, int m, int n, int k, int chunks, int total_waves)
 {
     extern __shared__ u32x4_t xs[];
     const int tid = threadIdx.x;
@@ -162,7 +162,21 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
                 const int64_t row = gw + (int64_t)j * total_waves;
                 if (j < my_rows && mm < m) {
                     const float s = f16_bits_to_f32(scales[row]);
-                    y[(int64_t)mm * n + row] = f32_to_f16_bits(acc[0] * s);
+                    float out = acc[0] * s;
+                    // exact outliers of this row, with X from the LDS copy
+                    // (entry e holds x[mm][c kChunkK + 16 l + 8 h + 0..7])
+                    if (ol.idx != nullptr) {
+                        const _Float16 *xh = reinterpret_cast<const _Float16 *>(xs);
+                        for (int e = 0; e < ol.cap; ++e) {
+                            const int kk = ol.idx[row * ol.cap + e];
+                            if (kk < 0 || kk >= k)
+                                break; // used slots come first
+                            const int c = kk / kChunkK, l = (kk % kChunkK) / 16, h = (kk % 16) / 8;
+                            const float xv = (float)xh[((((mm * chunks + c) * 2 + h) * kWave + l) * 8) + kk % 8];
+                            out += xv * ol.val[row * ol.cap + e];
+                        }
+                    }
+                    y[(int64_t)mm * n + row] = f32_to_f16_bits(out);
                 }
             }
         }
@@ -180,7 +194,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
 
 template <int MT, int RU, int CH, int WPC>
 hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros,
-                      uint16_t *y,
+                      OutlierList ol, uint16_t *y,
                       int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
     const int chunks = (int)((k + kChunkK - 1) / kChunkK);
@@ -201,7 +215,7 @@ hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales
     }
     const int blocks = (int)((waves + kGemvWaves - 1) / kGemvWaves);
     hipLaunchKernelGGL((gemv_kernel<MT, RU, CH>), dim3(blocks), dim3(kGemvThreads), lds, stream,
-                       x, q, scales, zeros, y, (int)m, (int)n, (int)k, chunks, (int)waves);
+                       x, q, scales, zeros, ol, y, (int)m, (int)n, (int)k, chunks, (int)waves);
     return hipGetLastError();
 }
 
@@ -219,18 +233,18 @@ bool gemv_supported(int64_t m, int64_t k)
 }
 
 hipError_t launch_gemv(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros,
-                       uint16_t *y,
+                       OutlierList ol, uint16_t *y,
                        int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
     // (MT, RU, CH, waves per CU) from measured sweeps; WPC stays within what
     // each configuration's register use lets a CU hold at once
     if (m <= 1)
-        return launch_cfg<1, 2, 4, 28>(x, q, scales, zeros, y, m, n, k, stream);
+        return launch_cfg<1, 2, 4, 28>(x, q, scales, zeros, ol, y, m, n, k, stream);
     if (m <= 2)
-        return launch_cfg<2, 1, 4, 32>(x, q, scales, zeros, y, m, n, k, stream);
+        return launch_cfg<2, 1, 4, 32>(x, q, scales, zeros, ol, y, m, n, k, stream);
     if (m <= 4)
-        return launch_cfg<4, 2, 2, 16>(x, q, scales, zeros, y, m, n, k, stream);
-    return launch_cfg<8, 2, 2, 16>(x, q, scales, zeros, y, m, n, k, stream);
+        return launch_cfg<4, 2, 2, 16>(x, q, scales, zeros, ol, y, m, n, k, stream);
+    return launch_cfg<8, 2, 2, 16>(x, q, scales, zeros, ol, y, m, n, k, stream);
 }
 
 } // namespace qw

@@ -245,12 +245,13 @@ __device__ __forceinline__ float4_t load4(const void *row, int idx)
 // MODE: 0 absmax bound, 1 percentile bound, 2 fixed range (the bound of
 // row r is bounds[r], given by the caller; no reduction), 3 asymmetric
 // (range [min(0, min w), max(0, max w)] over 255 steps, int8 zero point
-// per row written to zeros).
-template <int THREADS, int VPT, int MODE, bool F16>
+// per row written to zeros).  OUTL: the elements above the bound are
+// written to the row's outlier slots (ascending column) and get code 0.
+template <int THREADS, int VPT, int MODE, bool F16, bool OUTL = false>
 __global__ __launch_bounds__(THREADS) void quantize_rows_kernel(
     const void *__restrict__ w, int k, int64_t rank_i, double frac_f,
     const float *__restrict__ bounds, int8_t *__restrict__ q, uint16_t *__restrict__ scales,
-    int8_t *__restrict__ zeros)
+    int8_t *__restrict__ zeros, OutlierSlots ol)
 {
     constexpr bool PERCENTILE = MODE == 1;
     __shared__ QuantShared<THREADS> sh;
@@ -375,7 +376,8 @@ __global__ __launch_bounds__(THREADS) void quantize_rows_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             int code = 0;
-            if (s != 0.0f) {
+            const bool outlier = OUTL && __builtin_fabsf(v[j * 4 + e]) > t;
+            if (s != 0.0f && !outlier) {
                 const float est = v[j * 4 + e] * rs;
                 float r = __builtin_rintf(est);
                 // distance of est to the nearest half-integer (exact: est - r
@@ -392,38 +394,108 @@ __global__ __launch_bounds__(THREADS) void quantize_rows_kernel(
         }
         __builtin_nontemporal_store(packed, dst + idx);
     }
+
+    if constexpr (OUTL) {
+        // Compact the outliers into the row's slots in column order: slice
+        // j of every thread covers columns 4 (tid + j THREADS) + [0, 4), so
+        // slices in order and threads in order within a slice are columns in
+        // order.  One block-wide exclusive scan of the per-thread counts per
+        // slice; at most the host-checked capacity is ever reached (the
+        // elements above the type-7 bound are among the k - 1 - i largest),
+        // and the slot check below only guards the writes.
+        int32_t *oi = ol.idx + row * (int64_t)ol.cap;
+        float *ov = ol.val + row * (int64_t)ol.cap;
+        const int wave = threadIdx.x / kWave;
+        constexpr int W = THREADS / kWave;
+        uint32_t base = 0;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            uint32_t mine = 0;
+            if (s != 0.0f && valid[j]) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    mine += __builtin_fabsf(v[j * 4 + e]) > t ? 1u : 0u;
+            }
+            const uint32_t incl = wave_inclusive_scan_u32(mine);
+            if (__lane_id() == kWave - 1)
+                sh.red[wave] = incl;
+            __syncthreads();
+            uint32_t before = 0, total = 0;
+#pragma unroll
+            for (int wv = 0; wv < W; ++wv) {
+                const uint32_t c = sh.red[wv];
+                before += wv < wave ? c : 0u;
+                total += c;
+            }
+            __syncthreads();
+            uint32_t slot = base + before + incl - mine;
+            if (mine != 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (__builtin_fabsf(v[j * 4 + e]) > t) {
+                        if (slot < (uint32_t)ol.cap) {
+                            oi[slot] = 4 * (threadIdx.x + j * THREADS) + e;
+                            ov[slot] = v[j * 4 + e];
+                        }
+                        ++slot;
+                    }
+                }
+            }
+            base += total;
+        }
+        for (uint32_t p = base + threadIdx.x; p < (uint32_t)ol.cap; p += THREADS) {
+            oi[p] = -1;
+            ov[p] = 0.0f;
+        }
+    }
 }
 
 template <int THREADS, int VPT, bool F16>
 hipError_t launch_typed(const void *w, int64_t n, int64_t k, int mode, int64_t rank_i, double frac_f,
                         const float *bounds, int8_t *q, uint16_t *scales, int8_t *zeros,
-                        hipStream_t stream)
+                        OutlierSlots ol, hipStream_t stream)
 {
     const dim3 grid((unsigned)n), block(THREADS);
+    if (ol.idx != nullptr) {
+        if constexpr (F16) {
+            return hipErrorInvalidValue; // side lists: fp32 weights only
+        } else {
+            if (mode == 0)
+                hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, 0, false, true>), grid, block, 0, stream,
+                                   w, (int)k, rank_i, frac_f, bounds, q, scales, zeros, ol);
+            else if (mode == 1)
+                hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, 1, false, true>), grid, block, 0, stream,
+                                   w, (int)k, rank_i, frac_f, bounds, q, scales, zeros, ol);
+            else
+                return hipErrorInvalidValue;
+            return hipGetLastError();
+        }
+    }
     if (mode == 0)
         hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, 0, F16>), grid, block, 0, stream,
-                           w, (int)k, rank_i, frac_f, bounds, q, scales, zeros);
+                           w, (int)k, rank_i, frac_f, bounds, q, scales, zeros, ol);
     else if (mode == 1)
         hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, 1, F16>), grid, block, 0, stream,
-                           w, (int)k, rank_i, frac_f, bounds, q, scales, zeros);
+                           w, (int)k, rank_i, frac_f, bounds, q, scales, zeros, ol);
     else if constexpr (F16)
         return hipErrorInvalidValue; // fixed range and asymmetric: fp32 weights only
     else if (mode == 2)
         hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, 2, false>), grid, block, 0, stream,
-                           w, (int)k, rank_i, frac_f, bounds, q, scales, zeros);
+                           w, (int)k, rank_i, frac_f, bounds, q, scales, zeros, ol);
     else
         hipLaunchKernelGGL((quantize_rows_kernel<THREADS, VPT, 3, false>), grid, block, 0, stream,
-                           w, (int)k, rank_i, frac_f, bounds, q, scales, zeros);
+                           w, (int)k, rank_i, frac_f, bounds, q, scales, zeros, ol);
     return hipGetLastError();
 }
 
 template <int THREADS, int VPT>
 hipError_t launch_cfg(const void *w, bool f16, int64_t n, int64_t k, int mode, int64_t rank_i,
                       double frac_f, const float *bounds, int8_t *q, uint16_t *scales, int8_t *zeros,
-                      hipStream_t stream)
+                      OutlierSlots ol, hipStream_t stream)
 {
-    return f16 ? launch_typed<THREADS, VPT, true>(w, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream)
-               : launch_typed<THREADS, VPT, false>(w, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros,
+    return f16 ? launch_typed<THREADS, VPT, true>(w, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, ol,
+                                                  stream)
+               : launch_typed<THREADS, VPT, false>(w, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, ol,
                                                    stream);
 }
 
@@ -431,7 +503,7 @@ hipError_t launch_cfg(const void *w, bool f16, int64_t n, int64_t k, int mode, i
 
 hipError_t launch_quantize(const void *w, bool w_is_f16, int64_t n, int64_t k, int mode,
                            int64_t rank_i, double frac_f, const float *bounds, int8_t *q,
-                           uint16_t *scales, int8_t *zeros, hipStream_t stream)
+                           uint16_t *scales, int8_t *zeros, OutlierSlots ol, hipStream_t stream)
 {
     // float4 slots per row; a workgroup of THREADS holds THREADS * VPT of them.
     // Rows up to 1024 values get one wave each: every reduction is then a
@@ -439,24 +511,24 @@ hipError_t launch_quantize(const void *w, bool w_is_f16, int64_t n, int64_t k, i
     // percentile; no gain at 2048).
     const int64_t nvec = k / 4;
     if (nvec <= kWave * 1)
-        return launch_cfg<64, 1>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
+        return launch_cfg<64, 1>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, ol, stream);
     if (nvec <= kWave * 2)
-        return launch_cfg<64, 2>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
+        return launch_cfg<64, 2>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, ol, stream);
     if (nvec <= kWave * 4)
-        return launch_cfg<64, 4>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
+        return launch_cfg<64, 4>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, ol, stream);
     if (nvec <= 256 * 1)
-        return launch_cfg<256, 1>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
+        return launch_cfg<256, 1>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, ol, stream);
     if (nvec <= 256 * 2)
-        return launch_cfg<256, 2>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
+        return launch_cfg<256, 2>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, ol, stream);
     if (nvec <= 256 * 4)
-        return launch_cfg<256, 4>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
+        return launch_cfg<256, 4>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, ol, stream);
     if (nvec <= 256 * 8)
-        return launch_cfg<256, 8>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
+        return launch_cfg<256, 8>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, ol, stream);
     if (nvec <= 256 * 16)
-        return launch_cfg<256, 16>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
+        return launch_cfg<256, 16>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, ol, stream);
     if (nvec <= 1024 * 8)
-        return launch_cfg<1024, 8>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
-    return launch_cfg<1024, 16>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, stream);
+        return launch_cfg<1024, 8>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, ol, stream);
+    return launch_cfg<1024, 16>(w, w_is_f16, n, k, mode, rank_i, frac_f, bounds, q, scales, zeros, ol, stream);
 }
 
 } // namespace qw

@@ -99,10 +99,24 @@ qw_status check_gemm_args(const uint16_t *x, const int8_t *q, const uint16_t *sc
     return QW_SUCCESS;
 }
 
+// Outlier slots per row that always suffice for the type-7 bound: the
+// elements above it lie among the k - 1 - floor(pos) largest
+// (pos = (pct / 100) (k - 1) in binary64); none at pct = 100.
+int64_t outlier_capacity(int64_t k, double clip_percentile)
+{
+    if (clip_percentile == 100.0)
+        return 0;
+    const double frac_of_range = clip_percentile / 100.0;
+    const double pos = frac_of_range * (double)(k - 1);
+    const int64_t i = (int64_t)floor(pos);
+    return i >= k - 1 ? 0 : k - 1 - i;
+}
+
 // Shared body of the fp32 and fp16 quantizer entry points (wbytes = bytes
-// per input weight).
+// per input weight), with optional outlier side lists (fp32 only).
 qw_status quantize_common(const void *w, int wbytes, int64_t n, int64_t k, double clip_percentile,
-                          int8_t *q, uint16_t *scales, void *stream)
+                          int8_t *q, uint16_t *scales, void *stream,
+                          qw::OutlierSlots ol = qw::OutlierSlots{nullptr, nullptr, 0})
 {
     if (n < 0 || k <= 0)
         return QW_ERROR_INVALID_VALUE;
@@ -121,6 +135,24 @@ qw_status quantize_common(const void *w, int wbytes, int64_t n, int64_t k, doubl
         overlaps(scales, (uint64_t)n * 2u, w, elems * (uint64_t)wbytes) ||
         overlaps(scales, (uint64_t)n * 2u, q, elems))
         return QW_ERROR_INVALID_VALUE;
+    if (ol.idx != nullptr || ol.val != nullptr) {
+        if (!ol.idx || !ol.val || ol.cap < 0 || wbytes != 4)
+            return QW_ERROR_INVALID_VALUE;
+        if (ol.cap < outlier_capacity(k, clip_percentile) || ol.cap > k)
+            return QW_ERROR_INVALID_VALUE;
+        if (misaligned(ol.idx) || misaligned(ol.val))
+            return QW_ERROR_MISALIGNED;
+        const uint64_t sb = (uint64_t)n * (uint64_t)ol.cap * 4u;
+        const void *outs[3] = {q, scales, ol.val};
+        const uint64_t outb[3] = {elems, (uint64_t)n * 2u, sb};
+        if (overlaps(ol.idx, sb, w, elems * 4u) || overlaps(ol.val, sb, w, elems * 4u))
+            return QW_ERROR_INVALID_VALUE;
+        for (int i = 0; i < 3; ++i)
+            if (overlaps(ol.idx, sb, outs[i], outb[i]) || (i < 2 && overlaps(ol.val, sb, outs[i], outb[i])))
+                return QW_ERROR_INVALID_VALUE;
+        if (ol.cap == 0)
+            ol = qw::OutlierSlots{nullptr, nullptr, 0};
+    }
 
     // Clip position of the type-7 percentile, in binary64 on the host:
     // pos = (pct / 100) * (k - 1), i = floor(pos), f = pos - i.
@@ -138,13 +170,14 @@ qw_status quantize_common(const void *w, int wbytes, int64_t n, int64_t k, doubl
         }
     }
     return launch_status(qw::launch_quantize(w, wbytes == 2, n, k, mode, rank_i, frac_f, nullptr, q,
-                                             scales, nullptr, static_cast<hipStream_t>(stream)));
+                                             scales, nullptr, ol, static_cast<hipStream_t>(stream)));
 }
 
-// Shared body of the symmetric and asymmetric W8A16 entry points (zeros ==
-// nullptr: symmetric).
+// Shared body of the W8A16 entry points (zeros == nullptr: symmetric;
+// ol.idx == nullptr: no outlier side lists).
 qw_status gemm_common(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros,
-                      uint16_t *y, int64_t m, int64_t n, int64_t k, int path, void *stream)
+                      uint16_t *y, int64_t m, int64_t n, int64_t k, int path, void *stream,
+                      qw::OutlierList ol = qw::OutlierList{nullptr, nullptr, 0})
 {
     if (path != QW_PATH_AUTO && path != QW_PATH_GEMV && path != QW_PATH_MFMA &&
         path != QW_PATH_SKINNY)
@@ -159,20 +192,36 @@ qw_status gemm_common(const uint16_t *x, const int8_t *q, const uint16_t *scales
         if (overlaps(y, (uint64_t)m * (uint64_t)n * 2u, zeros, (uint64_t)n))
             return QW_ERROR_INVALID_VALUE;
     }
+    if (ol.idx != nullptr) {
+        const uint64_t sb = (uint64_t)n * (uint64_t)ol.cap * 4u;
+        if (misaligned(ol.idx) || misaligned(ol.val))
+            return QW_ERROR_MISALIGNED;
+        if (overlaps(y, (uint64_t)m * (uint64_t)n * 2u, ol.idx, sb) ||
+            overlaps(y, (uint64_t)m * (uint64_t)n * 2u, ol.val, sb))
+            return QW_ERROR_INVALID_VALUE;
+        if (ol.cap == 0)
+            ol = qw::OutlierList{nullptr, nullptr, 0};
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (path == QW_PATH_AUTO)
+    if (path == QW_PATH_AUTO) {
         path = qw::auto_path(m, n, k);
+        // side lists wider than the MFMA kernel stages in LDS: skinny kernel
+        if (path == QW_PATH_MFMA && ol.idx != nullptr && ol.cap > qw::kMfmaOutlierSlots)
+            path = QW_PATH_SKINNY;
+    }
+    if (path == QW_PATH_MFMA && ol.idx != nullptr && ol.cap > qw::kMfmaOutlierSlots)
+        return QW_ERROR_UNSUPPORTED;
     if (path == QW_PATH_GEMV) {
         if (!qw::gemv_supported(m, k))
             return QW_ERROR_UNSUPPORTED;
-        return launch_status(qw::launch_gemv(x, q, scales, zeros, y, m, n, k, s));
+        return launch_status(qw::launch_gemv(x, q, scales, zeros, ol, y, m, n, k, s));
     }
     if (path == QW_PATH_SKINNY) {
         if (m > 16 * 65535) // grid.y holds one 16-row activation tile per block row
             return QW_ERROR_UNSUPPORTED;
-        return launch_status(qw::launch_skinny_gemm(x, q, scales, zeros, y, m, n, k, s));
+        return launch_status(qw::launch_skinny_gemm(x, q, scales, zeros, ol, y, m, n, k, s));
     }
-    return launch_status(qw::launch_mfma_gemm(x, q, scales, zeros, y, m, n, k, s));
+    return launch_status(qw::launch_mfma_gemm(x, q, scales, zeros, ol, y, m, n, k, s));
 }
 
 } // namespace
@@ -189,6 +238,27 @@ QW_API qw_status qw_quantize_weights_f16(const uint16_t *w, int64_t n, int64_t k
                                          int8_t *q, uint16_t *scales, void *stream)
 {
     return quantize_common(w, 2, n, k, clip_percentile, q, scales, stream);
+}
+
+QW_API int64_t qw_outlier_capacity(int64_t k, double clip_percentile)
+{
+    if (k <= 0 || !(clip_percentile > 0.0 && clip_percentile <= 100.0))
+        return -1;
+    return outlier_capacity(k, clip_percentile);
+}
+
+QW_API qw_status qw_quantize_weights_outliers(const float *w, int64_t n, int64_t k, double clip_percentile,
+                                              int8_t *q, uint16_t *scales, int32_t *ol_idx, float *ol_val,
+                                              int64_t cap, void *stream)
+{
+    if (n < 0 || k <= 0 || cap < 0)
+        return QW_ERROR_INVALID_VALUE;
+    if (n > 0 && (!ol_idx || !ol_val))
+        return QW_ERROR_INVALID_VALUE;
+    if (cap > k || cap > kMaxDim)
+        return QW_ERROR_INVALID_VALUE;
+    return quantize_common(w, 4, n, k, clip_percentile, q, scales, stream,
+                           qw::OutlierSlots{ol_idx, ol_val, (int)cap});
 }
 
 QW_API qw_status qw_quantize_weights_fixed_range(const float *w, int64_t n, int64_t k,
@@ -211,7 +281,7 @@ QW_API qw_status qw_quantize_weights_fixed_range(const float *w, int64_t n, int6
         overlaps(scales, (uint64_t)n * 2u, bounds, (uint64_t)n * 4u))
         return QW_ERROR_INVALID_VALUE;
     return launch_status(qw::launch_quantize(w, false, n, k, 2, 0, 0.0, bounds, q, scales, nullptr,
-                                             static_cast<hipStream_t>(stream)));
+                                             qw::OutlierSlots{nullptr, nullptr, 0}, static_cast<hipStream_t>(stream)));
 }
 
 QW_API qw_status qw_quantize_weights_asym(const float *w, int64_t n, int64_t k, int8_t *q,
@@ -233,7 +303,7 @@ QW_API qw_status qw_quantize_weights_asym(const float *w, int64_t n, int64_t k, 
         overlaps(zeros, nn, q, elems) || overlaps(zeros, nn, scales, nn * 2u))
         return QW_ERROR_INVALID_VALUE;
     return launch_status(qw::launch_quantize(w, false, n, k, 3, 0, 0.0, nullptr, q, scales, zeros,
-                                             static_cast<hipStream_t>(stream)));
+                                             qw::OutlierSlots{nullptr, nullptr, 0}, static_cast<hipStream_t>(stream)));
 }
 
 QW_API qw_status qw_w8a16_gemm_path(const uint16_t *x, const int8_t *q, const uint16_t *scales,
@@ -250,6 +320,26 @@ QW_API qw_status qw_w8a16_gemm_asym_path(const uint16_t *x, const int8_t *q, con
     if (m > 0 && n > 0 && !zeros)
         return QW_ERROR_INVALID_VALUE;
     return gemm_common(x, q, scales, zeros, y, m, n, k, path, stream);
+}
+
+QW_API qw_status qw_w8a16_gemm_outliers_path(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                                             const int32_t *ol_idx, const float *ol_val, int64_t cap,
+                                             uint16_t *y, int64_t m, int64_t n, int64_t k, int path,
+                                             void *stream)
+{
+    if (cap < 0 || cap > k || cap > kMaxDim)
+        return QW_ERROR_INVALID_VALUE;
+    if (m > 0 && n > 0 && cap > 0 && (!ol_idx || !ol_val))
+        return QW_ERROR_INVALID_VALUE;
+    return gemm_common(x, q, scales, nullptr, y, m, n, k, path, stream,
+                       qw::OutlierList{cap > 0 ? ol_idx : nullptr, ol_val, (int)cap});
+}
+
+QW_API qw_status qw_w8a16_gemm_outliers(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                                        const int32_t *ol_idx, const float *ol_val, int64_t cap,
+                                        uint16_t *y, int64_t m, int64_t n, int64_t k, void *stream)
+{
+    return qw_w8a16_gemm_outliers_path(x, q, scales, ol_idx, ol_val, cap, y, m, n, k, QW_PATH_AUTO, stream);
 }
 
 QW_API qw_status qw_w8a16_gemm_asym(const uint16_t *x, const int8_t *q, const uint16_t *scales,

@@ -9,40 +9,60 @@
 
 namespace qw {
 
+// Per-row outlier side lists in ELL form: `cap` slots per row, columns in
+// ascending order, unused slots column -1 and value 0 (idx == nullptr: no
+// side lists).
+struct OutlierSlots {
+    int32_t *idx;
+    float *val;
+    int cap;
+};
+struct OutlierList {
+    const int32_t *idx;
+    const float *val;
+    int cap;
+};
+// Side-list slots per row the MFMA kernel stages in LDS; wider lists go to
+// the skinny kernel.
+constexpr int kMfmaOutlierSlots = 4;
+
 // Per-row quantizer of fp32 (w_is_f16 false) or fp16 weights.  mode 0:
 // absmax bound; mode 1: percentile bound with the rank i (0-based,
 // ascending) and interpolation fraction f computed on the host in binary64
 // (i < k - 1 in mode 1); mode 2 (fp32 weights only): the bound of row r is
 // bounds[r] (device pointer, unused in the other modes); mode 3 (fp32
 // weights only): asymmetric, range [min(0, min w), max(0, max w)], int8
-// zero point per row written to zeros.
+// zero point per row written to zeros.  With ol.idx set (modes 0 and 1,
+// fp32 weights): the elements above the bound go to the side lists and
+// their codes are 0 (rows whose scale is 0 keep none).
 hipError_t launch_quantize(const void *w, bool w_is_f16, int64_t n, int64_t k, int mode,
                            int64_t rank_i, double frac_f, const float *bounds, int8_t *q,
-                           uint16_t *scales, int8_t *zeros, hipStream_t stream);
+                           uint16_t *scales, int8_t *zeros, OutlierSlots ol, hipStream_t stream);
 
 // The three W8A16 kernels take an optional per-row int8 zero point
 // (`zeros`, nullptr for symmetric weights): the weight is then
-// S[n] * (q[n][k] - z[n]).
+// S[n] * (q[n][k] - z[n]); and optional outlier side lists (ol.idx ==
+// nullptr: none), whose entries are added exactly: y += x[col] * value.
 
 // Decode GEMV (VALU dot products).  Requires m <= 8 and
 // m * ceil(k / 1024) <= 32 (the activations fit the LDS budget).
 bool gemv_supported(int64_t m, int64_t k);
 hipError_t launch_gemv(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros,
-                       uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream);
+                       OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
 // Skinny MFMA GEMM: weights dequantized in registers, any m (intended for
 // m <= 32), n, k with k % 16 == 0.
 hipError_t launch_skinny_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
-                              const int8_t *zeros, uint16_t *y, int64_t m, int64_t n, int64_t k,
-                              hipStream_t stream);
+                              const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n,
+                              int64_t k, hipStream_t stream);
 
 // Kernel the automatic path picks for a shape (QW_PATH_* value).
 int auto_path(int64_t m, int64_t n, int64_t k);
 
 // MFMA tiled GEMM, any m, n, k with k % 16 == 0.
 hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
-                            const int8_t *zeros, uint16_t *y, int64_t m, int64_t n, int64_t k,
-                            hipStream_t stream);
+                            const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n,
+                            int64_t k, hipStream_t stream);
 
 // Output tile of the MFMA GEMM for this shape on the current device,
 // encoded BN * 1000 + BM.

@@ -31,7 +31,9 @@ def test_header_declares_the_entry_points():
     for name in ("qw_quantize_weights", "qw_quantize_weights_f16", "qw_w8a16_gemm", "qw_w8a16_gemm_path",
                  "qw_w8a16_gemm_auto_path", "qw_w8a16_gemm_mfma_tile", "qw_w8a8_gemm",
                  "qw_w8a8_gemm_mfma_tile", "qw_quantize_weights_fixed_range", "qw_quantize_weights_asym",
-                 "qw_w8a16_gemm_asym", "qw_w8a16_gemm_asym_path", "qw_status_string", "qw_version"):
+                 "qw_w8a16_gemm_asym", "qw_w8a16_gemm_asym_path", "qw_outlier_capacity",
+                 "qw_quantize_weights_outliers", "qw_w8a16_gemm_outliers", "qw_w8a16_gemm_outliers_path",
+                 "qw_status_string", "qw_version"):
         assert name in decl
 
 
@@ -156,6 +158,52 @@ def test_quantize_asym_rejects(args, status):
 ])
 def test_gemm_asym_rejects(args, status):
     assert qw.w8a16_gemm_asym_raw(*args) == status
+
+
+def test_outlier_capacity_matches_oracle():
+    import oracle
+    for k in (16, 48, 64, 1024, 1040, 4096, 4112, 65536):
+        for pct in (100.0, 99.9999, 99.99, 99.9, 99.0, 95.0, 90.0, 50.0, 1e-6):
+            assert qw.outlier_capacity(k, pct) == oracle.outlier_capacity(k, pct), (k, pct)
+    with pytest.raises(ValueError):
+        qw.outlier_capacity(16, 0.0)
+
+
+F = 6 << 20
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, 4, 1024, 99.99, B, C, D, E, 0), qw.QW_ERROR_INVALID_VALUE),      # cap below capacity (1)
+    ((A, 4, 16, 99.99, B, C, D, E, 17), qw.QW_ERROR_INVALID_VALUE),       # cap above k
+    ((A, 4, 16, 90.0, B, C, 0, E, 2), qw.QW_ERROR_INVALID_VALUE),         # null idx
+    ((A, 4, 16, 90.0, B, C, D, 0, 2), qw.QW_ERROR_INVALID_VALUE),         # null val
+    ((A, 4, 16, 90.0, B, C, D + 4, E, 2), qw.QW_ERROR_MISALIGNED),
+    ((A, 4, 16, 90.0, B, C, D, E + 8, 2), qw.QW_ERROR_MISALIGNED),
+    ((A, 4, 16, 90.0, B, C, D, D + 16, 2), qw.QW_ERROR_INVALID_VALUE),    # val overlaps idx (4 x 2 x 4 B)
+    ((A, 4, 16, 90.0, B, C, A + 32, E, 2), qw.QW_ERROR_INVALID_VALUE),    # idx inside w
+    ((A, 4, 16, 90.0, B, C, D, C, 2), qw.QW_ERROR_INVALID_VALUE),         # val overlaps scales
+    ((A, 4, 16, 0.0, B, C, D, E, 2), qw.QW_ERROR_INVALID_VALUE),          # bad percentile
+])
+def test_quantize_outliers_rejects(args, status):
+    assert qw.quantize_weights_outliers_raw(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, B, C, D, E, -1, F, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),       # cap < 0
+    ((A, B, C, D, E, 17, F, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),       # cap > k
+    ((A, B, C, 0, E, 2, F, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),        # null idx
+    ((A, B, C, D + 4, E, 2, F, 1, 4, 16), qw.QW_ERROR_MISALIGNED),
+    ((A, B, C, D, E, 2, D, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),        # y overlaps idx
+    ((A, B, C, D, E, 2, F, 1, 4, 24), qw.QW_ERROR_UNSUPPORTED),          # k % 16
+])
+def test_gemm_outliers_rejects(args, status):
+    assert qw.w8a16_gemm_outliers_raw(*args) == status
+
+
+def test_gemm_outliers_mfma_slot_limit():
+    # the MFMA kernel stages at most 4 slots per row; forcing it with more
+    # is refused before anything is launched
+    assert qw.w8a16_gemm_outliers_raw(A, B, C, D, E, 5, F, 64, 64, 64, 0, 2) == qw.QW_ERROR_UNSUPPORTED
 
 
 def test_quantize_empty_is_noop():
