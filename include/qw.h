@@ -355,6 +355,38 @@ QW_API int qw_w8a16_gemm_auto_path(int64_t m, int64_t n, int64_t k);
 QW_API int qw_w8a16_gemm_mfma_tile(int64_t m, int64_t n, int64_t k);
 
 /*
+ * qw_w8a16_gemm_tune -- per-shape autotuning of the W8A16 kernel choice.
+ *
+ * Source: LightSeq article ("最高加速9倍！字節跳動開源8比特混合精度
+ * Transformer引擎（1）", section on quantized inference speed): int8 GEMMs
+ * were slower than fp16 at some shapes until each shape was tuned
+ * automatically; LightSeq deck, TVM part: per-shape parameter search with
+ * the token count padded to a multiple of 8.  This call runs every
+ * candidate (the GEMV when m and k allow it, the skinny kernel, and the
+ * MFMA kernel with each of its four tiles) on the given buffers and
+ * stream, times each with HIP events (two untimed rounds, then seven rounds
+ * of one launch per candidate; the median decides), and records the
+ * fastest for the bucket (current device, n, k,
+ * m rounded up to a multiple of 8).  Every later automatic kernel choice
+ * for that bucket (qw_w8a16_gemm, its asymmetric and outlier variants,
+ * qw_w8a16_gemm_auto_path, qw_w8a16_gemm_mfma_tile) uses the record.
+ *
+ * Arguments, layout and errors as qw_w8a16_gemm; y holds the winner's
+ * result.  The call synchronizes with `stream` and is meant for set-up, not
+ * for the steady state.  Records are process-wide host state (a map under a
+ * mutex); QW_ERROR_LAUNCH if a launch or an event call fails.
+ *
+ * qw_w8a16_gemm_tuned_choice -- the record for the bucket of (m, n, k) on
+ * the current device: path * 1000000 + tile (tile = BN * 1000 + BM for
+ * QW_PATH_MFMA, 0 otherwise), or -1 if none (or bad shape).
+ * qw_w8a16_gemm_tune_reset -- forget every record.
+ */
+QW_API qw_status qw_w8a16_gemm_tune(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                                    uint16_t *y, int64_t m, int64_t n, int64_t k, void *stream);
+QW_API int qw_w8a16_gemm_tuned_choice(int64_t m, int64_t n, int64_t k);
+QW_API void qw_w8a16_gemm_tune_reset(void);
+
+/*
  * qw_w8a8_gemm -- Y = (QX * Q^T) scaled by Sx[i] * S[c]: both operands int8
  * with one fp16 scale per row (W8A8).
  *

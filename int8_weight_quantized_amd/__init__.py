@@ -72,6 +72,12 @@ def _load():
     lib.qw_quantize_weights_f16.restype = ctypes.c_int
     lib.qw_quantize_weights_fixed_range.argtypes = [vp, i64, i64, vp, vp, vp, vp]
     lib.qw_quantize_weights_fixed_range.restype = ctypes.c_int
+    lib.qw_w8a16_gemm_tune.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.qw_w8a16_gemm_tune.restype = ctypes.c_int
+    lib.qw_w8a16_gemm_tuned_choice.argtypes = [i64, i64, i64]
+    lib.qw_w8a16_gemm_tuned_choice.restype = ctypes.c_int
+    lib.qw_w8a16_gemm_tune_reset.argtypes = []
+    lib.qw_w8a16_gemm_tune_reset.restype = None
     lib.qw_outlier_capacity.argtypes = [i64, ctypes.c_double]
     lib.qw_outlier_capacity.restype = ctypes.c_int64
     lib.qw_quantize_weights_outliers.argtypes = [vp, i64, i64, ctypes.c_double, vp, vp, vp, vp, i64, vp]
@@ -165,6 +171,44 @@ def quantize_weights_f16_raw(w_ptr: int, n: int, k: int, clip_percentile: float,
 def quantize_weights_fixed_range_raw(w_ptr: int, n: int, k: int, bounds_ptr: int, q_ptr: int, s_ptr: int,
                                      stream: int = 0) -> int:
     return int(library().qw_quantize_weights_fixed_range(w_ptr, n, k, bounds_ptr, q_ptr, s_ptr, stream))
+
+
+def w8a16_gemm_tune_raw(x_ptr: int, q_ptr: int, s_ptr: int, y_ptr: int, m: int, n: int, k: int,
+                        stream: int = 0) -> int:
+    return int(library().qw_w8a16_gemm_tune(x_ptr, q_ptr, s_ptr, y_ptr, m, n, k, stream))
+
+
+def tuned_choice(m: int, n: int, k: int):
+    """The tuning record for the bucket of (m, n, k) on the current device:
+    (path name, (BN, BM) or None), or None when the shape has none."""
+    c = int(library().qw_w8a16_gemm_tuned_choice(m, n, k))
+    if c < 0:
+        return None
+    path, tile = divmod(c, 1000000)
+    name = {v: k2 for k2, v in PATHS.items()}[path]
+    return name, ((tile // 1000, tile % 1000) if tile else None)
+
+
+def tune_reset() -> None:
+    library().qw_w8a16_gemm_tune_reset()
+
+
+def w8a16_gemm_tune(x, q, scales, out=None):
+    """Time every kernel and MFMA tile for this shape on these tensors,
+    record the fastest for the shape bucket, and return Y (the winner's)."""
+    torch = _torch()
+    _check(x, "x", torch.float16, 2)
+    _check(q, "q", torch.int8, 2)
+    _check(scales, "scales", torch.float16, 1)
+    m, k = x.shape
+    n = q.shape[0]
+    if q.shape[1] != k or scales.shape[0] != n:
+        raise ValueError("shape mismatch")
+    y = torch.empty((m, n), dtype=torch.float16, device=x.device) if out is None else out
+    st = w8a16_gemm_tune_raw(x.data_ptr(), q.data_ptr(), scales.data_ptr(), y.data_ptr(), m, n, k, _stream_of(x))
+    if st != QW_SUCCESS:
+        raise QwError(st, "qw_w8a16_gemm_tune")
+    return y
 
 
 def outlier_capacity(k: int, clip_percentile: float) -> int:
@@ -432,6 +476,7 @@ def w8a8_gemm(qx, sx, q, scales, out=None):
 
 __all__ = ["quantize_weights", "quantize_weights_fixed_range", "quantize_weights_asym", "w8a16_gemm_asym",
            "quantize_weights_outliers", "w8a16_gemm_outliers", "outlier_capacity",
+           "w8a16_gemm_tune", "tuned_choice", "tune_reset", "w8a16_gemm_tune_raw",
            "quantize_activations", "w8a16_gemm", "w8a8_gemm", "QwError",
            "status_string", "version", "library", "auto_path", "mfma_tile", "w8a8_tile",
            "quantize_weights_raw", "quantize_weights_f16_raw", "quantize_weights_fixed_range_raw", "quantize_weights_asym_raw", "w8a16_gemm_asym_raw",

@@ -41,6 +41,7 @@ UNITS = {
     "gemv.hip": [],
     "gemm_mfma.hip": [],
     "gemm_skinny.hip": [],
+    "tune.hip": [],
 }
 
 

@@ -616,9 +616,9 @@ int tile_choice(int64_t m, int64_t n)
 template <bool A8>
 hipError_t launch_tiles(const void *x, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
                         const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k,
-                        hipStream_t stream)
+                        hipStream_t stream, int forced_tile = 0)
 {
-    int tile = tile_choice<A8>(m, n);
+    int tile = forced_tile != 0 ? forced_tile : tile_choice<A8>(m, n);
     if (ol.idx != nullptr && tile == 256128)
         tile = 256064;
     switch (tile) {
@@ -652,6 +652,15 @@ hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *
                             int64_t k, hipStream_t stream)
 {
     return launch_tiles<false>(x, nullptr, q, scales, zeros, ol, y, m, n, k, stream);
+}
+
+hipError_t launch_mfma_gemm_tile(int tile, const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                                 const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n,
+                                 int64_t k, hipStream_t stream)
+{
+    if (tile != 256128 && tile != 256064 && tile != 128128 && tile != 128064)
+        return hipErrorInvalidValue;
+    return launch_tiles<false>(x, nullptr, q, scales, zeros, ol, y, m, n, k, stream, tile);
 }
 
 hipError_t launch_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t *q,

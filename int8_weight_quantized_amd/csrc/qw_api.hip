@@ -204,6 +204,13 @@ qw_status gemm_common(const uint16_t *x, const int8_t *q, const uint16_t *scales
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (path == QW_PATH_AUTO) {
+        // a tuning record for this shape bucket wins over the heuristic
+        const int tuned = qw::tuned_choice(m, n, k);
+        const int tpath = tuned / qw::kChoicePath;
+        if (tuned >= 0 && (tpath != QW_PATH_GEMV || qw::gemv_supported(m, k)) &&
+            (tpath != QW_PATH_MFMA || ol.idx == nullptr || ol.cap <= qw::kMfmaOutlierSlots) &&
+            (tpath != QW_PATH_SKINNY || m <= 16 * 65535))
+            return launch_status(qw::launch_choice(tuned, x, q, scales, zeros, ol, y, m, n, k, s));
         path = qw::auto_path(m, n, k);
         // side lists wider than the MFMA kernel stages in LDS: skinny kernel
         if (path == QW_PATH_MFMA && ol.idx != nullptr && ol.cap > qw::kMfmaOutlierSlots)
@@ -359,7 +366,37 @@ QW_API int qw_w8a16_gemm_auto_path(int64_t m, int64_t n, int64_t k)
 {
     if (m < 0 || n < 0 || k <= 0 || k % 16 != 0)
         return -1;
+    const int tuned = qw::tuned_choice(m, n, k);
+    if (tuned >= 0 && (tuned / qw::kChoicePath != QW_PATH_GEMV || qw::gemv_supported(m, k)))
+        return tuned / qw::kChoicePath;
     return qw::auto_path(m, n, k);
+}
+
+QW_API qw_status qw_w8a16_gemm_tune(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y,
+                                    int64_t m, int64_t n, int64_t k, void *stream)
+{
+    bool noop = false;
+    const qw_status st = check_gemm_args(x, q, scales, y, m, n, k, noop);
+    if (st != QW_SUCCESS || noop)
+        return st;
+    int best = -1;
+    const hipError_t e = qw::tune_gemm(x, q, scales, y, m, n, k, static_cast<hipStream_t>(stream), best);
+    if (e != hipSuccess)
+        return QW_ERROR_LAUNCH;
+    qw::record_tuned_choice(m, n, k, best);
+    return QW_SUCCESS;
+}
+
+QW_API int qw_w8a16_gemm_tuned_choice(int64_t m, int64_t n, int64_t k)
+{
+    if (m <= 0 || n <= 0 || k <= 0 || k % 16 != 0)
+        return -1;
+    return qw::tuned_choice(m, n, k);
+}
+
+QW_API void qw_w8a16_gemm_tune_reset(void)
+{
+    qw::reset_tuned_choices();
 }
 
 QW_API int qw_w8a16_gemm_mfma_tile(int64_t m, int64_t n, int64_t k)
@@ -369,6 +406,9 @@ QW_API int qw_w8a16_gemm_mfma_tile(int64_t m, int64_t n, int64_t k)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return -1;
+    const int tuned = qw::tuned_choice(m, n, k);
+    if (tuned >= 0 && tuned / qw::kChoicePath == QW_PATH_MFMA)
+        return tuned % qw::kChoicePath;
     return qw::mfma_tile_choice(m, n);
 }
 

@@ -78,4 +78,22 @@ int w8a8_tile_choice(int64_t m, int64_t n);
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
+// Per-shape tuning records (tune.hip).  A choice encodes the kernel and the
+// MFMA tile as path * kChoicePath + tile (tile 0 for GEMV and skinny).
+constexpr int kChoicePath = 1000000;
+int tuned_choice(int64_t m, int64_t n, int64_t k);               // -1: none
+void record_tuned_choice(int64_t m, int64_t n, int64_t k, int choice);
+void reset_tuned_choices();
+hipError_t launch_choice(int choice, const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                         const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                         hipStream_t stream);
+// Times every candidate on the caller's buffers and stream (synchronizes
+// with it) and returns the fastest in `best`; y holds the winner's result.
+hipError_t tune_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y, int64_t m,
+                     int64_t n, int64_t k, hipStream_t stream, int &best);
+// The MFMA GEMM with a given tile (BN * 1000 + BM).
+hipError_t launch_mfma_gemm_tile(int tile, const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                                 const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n,
+                                 int64_t k, hipStream_t stream);
+
 } // namespace qw

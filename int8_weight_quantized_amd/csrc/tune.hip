@@ -1,0 +1,143 @@
+// tune.hip -- per-shape kernel autotuning for the W8A16 GEMM.
+//
+// The LightSeq article (section on quantized inference speed) reports int8
+// GEMMs slower than fp16 at some shapes until each shape's GEMM was tuned
+// automatically, and the LightSeq deck (TVM part) searches kernel
+// parameters per dynamic shape with the token count padded to a multiple of
+// 8.  Here the search space is the kernel (GEMV, skinny, MFMA) and the MFMA
+// tile shape; a tuning call times every candidate on the caller's buffers
+// and stream and records the fastest for the shape bucket (device, n, k,
+// m rounded up to a multiple of 8).  The automatic kernel choice of every
+// W8A16 entry point consults these records first.
+//
+// The records are the library's only mutable host state: a small map under
+// a mutex, kept until the process ends or qw_w8a16_gemm_tune_reset.  No
+// device memory is allocated; timing uses HIP events on the caller's
+// stream, so a tuning call synchronizes with that stream.
+#include <stdint.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "qw.h"
+#include "qw_internal.h"
+
+namespace qw {
+namespace {
+
+std::mutex g_tune_mutex;
+std::map<std::tuple<int, int64_t, int64_t, int64_t>, int> g_tuned; // (dev, n, k, m8) -> choice
+
+int64_t bucket_m(int64_t m)
+{
+    return (m + 7) / 8 * 8;
+}
+
+} // namespace
+
+int tuned_choice(int64_t m, int64_t n, int64_t k)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return -1;
+    std::lock_guard<std::mutex> lock(g_tune_mutex);
+    const auto it = g_tuned.find(std::make_tuple(dev, n, k, bucket_m(m)));
+    return it == g_tuned.end() ? -1 : it->second;
+}
+
+void record_tuned_choice(int64_t m, int64_t n, int64_t k, int choice)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return;
+    std::lock_guard<std::mutex> lock(g_tune_mutex);
+    g_tuned[std::make_tuple(dev, n, k, bucket_m(m))] = choice;
+}
+
+void reset_tuned_choices()
+{
+    std::lock_guard<std::mutex> lock(g_tune_mutex);
+    g_tuned.clear();
+}
+
+hipError_t launch_choice(int choice, const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                         const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                         hipStream_t stream)
+{
+    const int path = choice / kChoicePath;
+    const int tile = choice % kChoicePath;
+    if (path == QW_PATH_GEMV)
+        return launch_gemv(x, q, scales, zeros, ol, y, m, n, k, stream);
+    if (path == QW_PATH_SKINNY)
+        return launch_skinny_gemm(x, q, scales, zeros, ol, y, m, n, k, stream);
+    return launch_mfma_gemm_tile(tile, x, q, scales, zeros, ol, y, m, n, k, stream);
+}
+
+hipError_t tune_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y, int64_t m,
+                     int64_t n, int64_t k, hipStream_t stream, int &best)
+{
+    int cands[8];
+    int nc = 0;
+    if (gemv_supported(m, k))
+        cands[nc++] = QW_PATH_GEMV * kChoicePath;
+    if (m <= 16 * 65535)
+        cands[nc++] = QW_PATH_SKINNY * kChoicePath;
+    for (int tile : {256128, 256064, 128128, 128064})
+        cands[nc++] = QW_PATH_MFMA * kChoicePath + tile;
+
+    hipEvent_t ev[2];
+    if (hipEventCreate(&ev[0]) != hipSuccess)
+        return hipErrorOutOfMemory;
+    if (hipEventCreate(&ev[1]) != hipSuccess) {
+        (void)hipEventDestroy(ev[0]);
+        return hipErrorOutOfMemory;
+    }
+    // Candidates are timed round-robin, one launch each per round, so that
+    // clock ramp-up and drift under load hit every candidate alike (timed
+    // one after another, the first candidates ran at a lower clock and the
+    // ranking followed the order); two untimed rounds first.
+    constexpr int kWarm = 2, kRounds = 7;
+    const OutlierList none{nullptr, nullptr, 0};
+    float times[8][kRounds];
+    hipError_t err = hipSuccess;
+    for (int r = 0; r < kWarm + kRounds && err == hipSuccess; ++r) {
+        for (int c = 0; c < nc && err == hipSuccess; ++c) {
+            const bool timed = r >= kWarm;
+            if (timed)
+                err = hipEventRecord(ev[0], stream);
+            if (err == hipSuccess)
+                err = launch_choice(cands[c], x, q, scales, nullptr, none, y, m, n, k, stream);
+            if (timed && err == hipSuccess)
+                err = hipEventRecord(ev[1], stream);
+            if (timed && err == hipSuccess)
+                err = hipEventSynchronize(ev[1]);
+            if (timed && err == hipSuccess)
+                err = hipEventElapsedTime(&times[c][r - kWarm], ev[0], ev[1]);
+        }
+    }
+    best = -1;
+    float best_ms = 0.0f;
+    for (int c = 0; c < nc && err == hipSuccess; ++c) {
+        float *t = times[c];
+        for (int a = 1; a < kRounds; ++a) // insertion sort; the median decides
+            for (int b = a; b > 0 && t[b] < t[b - 1]; --b) {
+                const float tmp = t[b];
+                t[b] = t[b - 1];
+                t[b - 1] = tmp;
+            }
+        const float ms = t[kRounds / 2];
+        if (best < 0 || ms < best_ms) {
+            best = cands[c];
+            best_ms = ms;
+        }
+    }
+    (void)hipEventDestroy(ev[0]);
+    (void)hipEventDestroy(ev[1]);
+    if (err != hipSuccess)
+        return err;
+    // leave the winner's result in y
+    return launch_choice(best, x, q, scales, nullptr, none, y, m, n, k, stream);
+}
+
+} // namespace qw

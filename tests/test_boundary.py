@@ -33,6 +33,7 @@ def test_header_declares_the_entry_points():
                  "qw_w8a8_gemm_mfma_tile", "qw_quantize_weights_fixed_range", "qw_quantize_weights_asym",
                  "qw_w8a16_gemm_asym", "qw_w8a16_gemm_asym_path", "qw_outlier_capacity",
                  "qw_quantize_weights_outliers", "qw_w8a16_gemm_outliers", "qw_w8a16_gemm_outliers_path",
+                 "qw_w8a16_gemm_tune", "qw_w8a16_gemm_tuned_choice", "qw_w8a16_gemm_tune_reset",
                  "qw_status_string", "qw_version"):
         assert name in decl
 
@@ -265,6 +266,24 @@ def test_w8a8_rejects(args, status):
 def test_w8a8_empty_is_noop():
     assert qw.w8a8_gemm_raw(0, 0, 0, 0, 0, 0, 4, 16) == qw.QW_SUCCESS
     assert qw.w8a8_gemm_raw(0, 0, 0, 0, 0, 3, 0, 16) == qw.QW_SUCCESS
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, B, C, D, -1, 4, 16), qw.QW_ERROR_INVALID_VALUE),
+    ((0, B, C, D, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),
+    ((A, B, C, D, 1, 4, 24), qw.QW_ERROR_UNSUPPORTED),
+    ((A + 2, B, C, D, 1, 4, 16), qw.QW_ERROR_MISALIGNED),
+    ((A, B, C, A + 16, 1, 4, 16), qw.QW_ERROR_INVALID_VALUE),       # y overlaps x
+])
+def test_gemm_tune_rejects(args, status):
+    assert qw.w8a16_gemm_tune_raw(*args) == status
+
+
+def test_tuned_choice_without_records():
+    qw.tune_reset()
+    assert qw.tuned_choice(8, 4608, 4096) is None
+    assert qw.library().qw_w8a16_gemm_tuned_choice(0, 4, 16) == -1
+    assert qw.library().qw_w8a16_gemm_tuned_choice(1, 4, 24) == -1
 
 
 def test_gemm_path_checks():
