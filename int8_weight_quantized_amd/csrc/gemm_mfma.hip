@@ -457,9 +457,12 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
         // MFMAs, and the scheduler would otherwise sink them below the
         // whole step, right before the wait for them
         __builtin_amdgcn_sched_barrier(0);
-        compute(ring(s));
+        // outliers before this step's MFMAs: their adds then depend only on
+        // the previous step's MFMAs, long finished (after them, each add
+        // would wait for this step's whole MFMA chain on its accumulator)
         if constexpr (OL)
             add_outliers(t, ring(s));
+        compute(ring(s));
     };
     // steady state: pairs of steps whose next tile is full
     int t = 0;
