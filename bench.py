@@ -218,11 +218,13 @@ def time_w8a8(wl, launches=40, warmup=10):
     aq_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / launches
     pair_ms = sum(e[0].elapsed_time(e[2]) for e in ev) / launches
     ops = gemm_flops(wl.m, wl.n, wl.k)
-    tile = r.qw.w8a8_tile(wl.m, wl.n, wl.k)
+    mfma = r.qw.auto_path(wl.m, wl.n, wl.k) == "mfma"  # the W8A8 kernel choice follows the W8A16 one
+    tile = list(r.qw.w8a8_tile(wl.m, wl.n, wl.k)) if mfma else None
     sets = r.sets
     del r
     torch.cuda.empty_cache()
-    return {"workload": wl.name, "kernel": "w8a8_mfma", "mfma_tile": list(tile), "cold_sets": sets,
+    return {"workload": wl.name, "kernel": "w8a8_mfma" if mfma else "w8a8_skinny", "mfma_tile": tile,
+            "cold_sets": sets,
             "avg_us": avg_ms * 1e3, "median_us": med_ms * 1e3,
             "TOPs": ops / (avg_ms * 1e-3) / 1e12,
             "mfma_i8_frac": ops / (avg_ms * 1e-3) / 1e12 / MFMA_I8_PEAK_TOPS,

@@ -265,7 +265,9 @@ QW_API qw_status qw_quantize_weights_asym(const float *w, int64_t n, int64_t k, 
  * The int8 -> fp16 cast is exact; products are formed exactly and summed in
  * binary32 (fp32 accumulation); the per-channel scale is applied to the
  * fp32 sum (algebraically the same as scaling each weight first, with less
- * rounding).  Accuracy contract: max |Y - exact| <= 2e-3 * max|exact| + 1e-3.
+ * rounding), and the MFMA kernels round that product to binary16 in one
+ * fused step (a zero product is written as +0).  Accuracy contract:
+ * max |Y - exact| <= 2e-3 * max|exact| + 1e-3.
  *
  *   x       fp16 bits [m][k]
  *   q       int8 [n][k] codes (as written by qw_quantize_weights)
@@ -401,12 +403,15 @@ QW_API void qw_w8a16_gemm_tune_reset(void);
  * weights' quantizer, qw_quantize_weights_f16 with clip_percentile 100.
  *
  *   acc[i][c] = sum_j QX[i][j] * Q[c][j]       exact, int32
- *   Y[i][c]   = binary16_RNE( binary32(float(acc) * (S[c] * Sx[i])) )
+ *   Y[i][c]   = binary16_RNE( float(acc) * (S[c] * Sx[i]) )
  *
  * float(acc) rounds to binary32 only when |acc| >= 2^24; S[c] * Sx[i] is
- * exact in binary32.  Accuracy contract: |Y - exact| <= 2^-10 |exact| +
- * 2^-24 element-wise (one binary16 rounding plus at most two binary32
- * roundings); bit-exact when |acc| < 2^24 and the scales are powers of two.
+ * exact in binary32.  The MFMA kernel rounds the product to binary16 in
+ * one fused step (v_fma_mix), the skinny kernel through binary32; a zero
+ * product may be written as +0 whatever the sign of acc.  Accuracy
+ * contract: |Y - exact| <= 2^-10 |exact| + 2^-24 element-wise (one
+ * binary16 rounding plus at most two binary32 roundings); bit-exact when
+ * |acc| < 2^24 and the scales are powers of two.
  *
  *   qx      int8 [m][k] activation codes
  *   sx      fp16 bits [m], one scale per activation row
@@ -417,9 +422,12 @@ QW_API void qw_w8a16_gemm_tune_reset(void);
  *   k       16 <= k <= QW_W8A8_MAX_K, k % 16 == 0
  *   stream  hipStream_t
  *
- * One kernel for every m: the LDS-tiled MFMA GEMM on
- * v_mfma_i32_32x32x32_i8, tile shape picked as for qw_w8a16_gemm's MFMA
- * path.  All pointers 16-byte aligned.
+ * Kernels: for a few activation rows (where qw_w8a16_gemm would not pick
+ * its MFMA GEMM) the skinny kernel on v_mfma_i32_16x16x64_i8, else the
+ * LDS-tiled MFMA GEMM on v_mfma_i32_32x32x32_i8, tile shape picked as for
+ * qw_w8a16_gemm's MFMA path.  qw_w8a8_gemm_path forces QW_PATH_SKINNY or
+ * QW_PATH_MFMA (QW_PATH_GEMV is QW_ERROR_INVALID_VALUE).  All pointers
+ * 16-byte aligned.
  *
  * Errors: QW_ERROR_INVALID_VALUE (null pointer with m, n > 0, negative
  * size, k <= 0, y overlapping qx, sx, q or scales), QW_ERROR_UNSUPPORTED
@@ -429,6 +437,9 @@ QW_API void qw_w8a16_gemm_tune_reset(void);
 QW_API qw_status qw_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t *q,
                               const uint16_t *scales, uint16_t *y, int64_t m, int64_t n,
                               int64_t k, void *stream);
+QW_API qw_status qw_w8a8_gemm_path(const int8_t *qx, const uint16_t *sx, const int8_t *q,
+                                   const uint16_t *scales, uint16_t *y, int64_t m, int64_t n,
+                                   int64_t k, int path, void *stream);
 
 /*
  * qw_w8a8_gemm_mfma_tile -- the output tile qw_w8a8_gemm uses for this

@@ -93,6 +93,8 @@ def _load():
     lib.qw_w8a16_gemm_asym_path.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.qw_w8a16_gemm_asym_path.restype = ctypes.c_int
     lib.qw_w8a8_gemm.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.qw_w8a8_gemm_path.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.qw_w8a8_gemm_path.restype = ctypes.c_int
     lib.qw_w8a8_gemm.restype = ctypes.c_int
     lib.qw_w8a8_gemm_mfma_tile.argtypes = [i64, i64, i64]
     lib.qw_w8a8_gemm_mfma_tile.restype = ctypes.c_int
@@ -247,8 +249,8 @@ def w8a16_gemm_raw(x_ptr: int, q_ptr: int, s_ptr: int, y_ptr: int, m: int, n: in
 
 
 def w8a8_gemm_raw(qx_ptr: int, sx_ptr: int, q_ptr: int, s_ptr: int, y_ptr: int, m: int, n: int,
-                  k: int, stream: int = 0) -> int:
-    return int(library().qw_w8a8_gemm(qx_ptr, sx_ptr, q_ptr, s_ptr, y_ptr, m, n, k, stream))
+                  k: int, stream: int = 0, path: int = 0) -> int:
+    return int(library().qw_w8a8_gemm_path(qx_ptr, sx_ptr, q_ptr, s_ptr, y_ptr, m, n, k, int(path), stream))
 
 
 # ---------------------------------------------------------------------------

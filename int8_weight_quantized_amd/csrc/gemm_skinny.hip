@@ -30,26 +30,37 @@
 #include "qw_device.h"
 #include "qw_internal.h"
 
+#include <type_traits>
+
 namespace qw {
 namespace {
 
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef int int4v __attribute__((ext_vector_type(4)));
 
 constexpr int kSkinnyUnroll = 4;
 constexpr int kSkinnyTargetWaves = 2048; // enough in-flight loads to fill HBM
 
-template <int RT, int KSPLIT>
+// A8 (W8A8): the activations are int8 codes with one fp16 scale per row
+// (sx); the 16 codes a lane holds per step are exactly the A operand of one
+// v_mfma_i32_16x16x64_i8 (k slots 16 g .. 16 g + 15 of the 64-wide step),
+// the activation codes the B operand with the same assignment, the
+// accumulators are exact int32, and the epilogue scales by S[n] * Sx[m].
+// Zero points and side lists are W8A16 only (null with A8).
+template <int RT, int KSPLIT, bool A8 = false, bool ZP = false>
 __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
-    const uint16_t *__restrict__ x, const int8_t *__restrict__ q,
+    const void *__restrict__ xv, const uint16_t *__restrict__ sx, const int8_t *__restrict__ q,
     const uint16_t *__restrict__ scales, const int8_t *__restrict__ zeros, OutlierList ol,
     uint16_t *__restrict__ y, int m, int n, int k)
 {
+    const uint16_t *__restrict__ x = static_cast<const uint16_t *>(xv);
+    using acc_t = std::conditional_t<A8, int4v, float4v>;
     // Per wave, a staging slice for the weight codes of one iteration:
     // [tile][row][256 bytes + 16 pad].  After the main loop the same memory
     // holds the partial tiles of waves 1 .. KSPLIT-1.
     constexpr int kStageRow = 64 * kSkinnyUnroll + 16; // 256 codes + pad
     constexpr int kStageBytes = KSPLIT * RT * 16 * kStageRow;
-    constexpr int kPartialBytes = (KSPLIT > 1 ? KSPLIT - 1 : 1) * RT * kWave * (int)sizeof(float4v);
+    constexpr int kPartialBytes = (KSPLIT > 1 ? KSPLIT - 1 : 1) * RT * kWave * (int)sizeof(acc_t);
     __shared__ __attribute__((aligned(16))) uint8_t smem[kStageBytes > kPartialBytes ? kStageBytes : kPartialBytes];
     // the finished fp16 tile, [activation row][channel], padded rows
     __shared__ __attribute__((aligned(16))) uint16_t ytile[16][16 * RT + 8];
@@ -76,6 +87,7 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
         qrow[t] = q + (int64_t)(row_ok[t] ? row : 0) * k;
     }
     const uint16_t *xrow = x + (int64_t)(col < m ? col : 0) * k;
+    const int8_t *qxrow = static_cast<const int8_t *>(xv) + (int64_t)(col < m ? col : 0) * k;
     const bool col_ok = col < m;
 
     // the scales of the outputs this lane ends up holding (channels
@@ -92,15 +104,17 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
 
     // asymmetric weights: the cast subtracts the zero point of weight row
     // n0 + 16 t + r (zeros == nullptr: symmetric)
+    // (a template parameter: the symmetric kernels keep the constant bias
+    // and its registers free)
     half2_t zbias[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t)
-        zbias[t] = zero_point_bias(zeros != nullptr && row_ok[t] ? (int)zeros[n0 + 16 * t + r] : 0);
+        zbias[t] = zero_point_bias(ZP && row_ok[t] ? (int)zeros[n0 + 16 * t + r] : 0);
 
-    float4v acc[RT];
+    acc_t acc[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t)
-        acc[t] = (float4v){0.f, 0.f, 0.f, 0.f};
+        acc[t] = (acc_t){};
 
     for (int s = s_begin; s < s_end; s += kSkinnyUnroll) {
         u32x4_t wv[kSkinnyUnroll][RT];
@@ -147,26 +161,37 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
             xa[u] = (u32x4_t){0u, 0u, 0u, 0u};
             xb[u] = (u32x4_t){0u, 0u, 0u, 0u};
             if (ok && col_ok) {
-                xa[u] = *reinterpret_cast<const u32x4_t *>(xrow + kk);
-                xb[u] = *reinterpret_cast<const u32x4_t *>(xrow + kk + 8);
+                if constexpr (A8) {
+                    xa[u] = *reinterpret_cast<const u32x4_t *>(qxrow + kk);
+                } else {
+                    xa[u] = *reinterpret_cast<const u32x4_t *>(xrow + kk);
+                    xb[u] = *reinterpret_cast<const u32x4_t *>(xrow + kk + 8);
+                }
             }
         }
 #pragma unroll
         for (int u = 0; u < kSkinnyUnroll; ++u) {
-            const half8_t b0 = __builtin_bit_cast(half8_t, xa[u]);
-            const half8_t b1 = __builtin_bit_cast(half8_t, xb[u]);
+            if constexpr (A8) {
 #pragma unroll
-            for (int t = 0; t < RT; ++t) {
-                const half8_t a0 = i8x8_to_half8(wv[u][t].x, wv[u][t].y, zbias[t]);
-                const half8_t a1 = i8x8_to_half8(wv[u][t].z, wv[u][t].w, zbias[t]);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, acc[t], 0, 0, 0);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, acc[t], 0, 0, 0);
+                for (int t = 0; t < RT; ++t)
+                    acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(int4v, wv[u][t]),
+                                                                   __builtin_bit_cast(int4v, xa[u]), acc[t], 0, 0, 0);
+            } else {
+                const half8_t b0 = __builtin_bit_cast(half8_t, xa[u]);
+                const half8_t b1 = __builtin_bit_cast(half8_t, xb[u]);
+#pragma unroll
+                for (int t = 0; t < RT; ++t) {
+                    const half8_t a0 = i8x8_to_half8(wv[u][t].x, wv[u][t].y, zbias[t]);
+                    const half8_t a1 = i8x8_to_half8(wv[u][t].z, wv[u][t].w, zbias[t]);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, acc[t], 0, 0, 0);
+                }
             }
         }
     }
 
     if (KSPLIT > 1) {
-        float4v *partial = reinterpret_cast<float4v *>(smem); // [KSPLIT-1][RT][kWave]
+        acc_t *partial = reinterpret_cast<acc_t *>(smem); // [KSPLIT-1][RT][kWave]
         __syncthreads(); // every wave is done with its staging slice
         if (wave > 0) {
 #pragma unroll
@@ -182,6 +207,7 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
             for (int t = 0; t < RT; ++t)
                 acc[t] += partial[(w * RT + t) * kWave + lane];
     }
+    const float xscale = A8 && col_ok ? f16_bits_to_f32(sx[col]) : 0.0f;
     // lane holds channels n0 + 16 t + 4 g + i (i = 0..3) of activation row
     // m0 + r: scale, round, and transpose through LDS so that the stores
     // are whole 16-byte pieces of Y rows
@@ -189,11 +215,15 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
     for (int t = 0; t < RT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float out = acc[t][i] * f16_bits_to_f32(sc[t][i]);
+            float out;
+            if constexpr (A8) // exact int32 sum, then S[n] * Sx[m] (exact in fp32)
+                out = (float)acc[t][i] * (f16_bits_to_f32(sc[t][i]) * xscale);
+            else
+                out = acc[t][i] * f16_bits_to_f32(sc[t][i]);
             // exact outliers of channel n0 + 16 t + 4 g + i, with X read
             // from global memory (a few activation rows: L2-resident)
             const int yn = n0 + 16 * t + 4 * g + i;
-            if (ol.idx != nullptr && yn < n && col_ok) {
+            if (!A8 && ol.idx != nullptr && yn < n && col_ok) {
                 for (int e = 0; e < ol.cap; ++e) {
                     const int kk = ol.idx[(int64_t)yn * ol.cap + e];
                     if (kk < 0 || kk >= k)
@@ -227,40 +257,53 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
     }
 }
 
-template <int RT, int KSPLIT>
-hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros,
-                      OutlierList ol, uint16_t *y,
-                      int64_t m, int64_t n, int64_t k, hipStream_t stream)
+template <int RT, int KSPLIT, bool A8>
+hipError_t launch_cfg(const void *x, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
+                      const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                      hipStream_t stream)
 {
     const dim3 grid((unsigned)((n + 16 * RT - 1) / (16 * RT)), (unsigned)((m + 15) / 16));
-    hipLaunchKernelGGL((skinny_gemm_kernel<RT, KSPLIT>), grid, dim3(KSPLIT * kWave), 0, stream,
-                       x, q, scales, zeros, ol, y, (int)m, (int)n, (int)k);
+    if constexpr (!A8) {
+        if (zeros != nullptr) {
+            hipLaunchKernelGGL((skinny_gemm_kernel<RT, KSPLIT, false, true>), grid, dim3(KSPLIT * kWave), 0,
+                               stream, x, sx, q, scales, zeros, ol, y, (int)m, (int)n, (int)k);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((skinny_gemm_kernel<RT, KSPLIT, A8>), grid, dim3(KSPLIT * kWave), 0, stream,
+                       x, sx, q, scales, zeros, ol, y, (int)m, (int)n, (int)k);
     return hipGetLastError();
 }
 
-template <int RT>
-hipError_t launch_rt(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros,
-                     OutlierList ol, uint16_t *y,
-                     int64_t m, int64_t n, int64_t k, hipStream_t stream)
+template <int RT, bool A8>
+hipError_t launch_rt(const void *x, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
+                     const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                     hipStream_t stream)
 {
     // split k until the grid holds about kSkinnyTargetWaves waves, keeping
     // at least one 64-wide step per wave
     const int64_t tiles = ((n + 16 * RT - 1) / (16 * RT)) * ((m + 15) / 16);
     const int64_t steps = (k + 63) / 64;
+    // (the int8 variant stops at 8 waves: with 16 the 128-register limit of
+    // a 1024-thread workgroup made it spill)
+    constexpr int kMaxSplit = A8 ? 8 : 16;
     int ksplit = 1;
-    while (ksplit < 16 && tiles * ksplit < kSkinnyTargetWaves && steps >= 2 * ksplit)
+    while (ksplit < kMaxSplit && tiles * ksplit < kSkinnyTargetWaves && steps >= 2 * ksplit)
         ksplit *= 2;
     switch (ksplit) {
     case 1:
-        return launch_cfg<RT, 1>(x, q, scales, zeros, ol, y, m, n, k, stream);
+        return launch_cfg<RT, 1, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
     case 2:
-        return launch_cfg<RT, 2>(x, q, scales, zeros, ol, y, m, n, k, stream);
+        return launch_cfg<RT, 2, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
     case 4:
-        return launch_cfg<RT, 4>(x, q, scales, zeros, ol, y, m, n, k, stream);
+        return launch_cfg<RT, 4, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
     case 8:
-        return launch_cfg<RT, 8>(x, q, scales, zeros, ol, y, m, n, k, stream);
+        return launch_cfg<RT, 8, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
     default:
-        return launch_cfg<RT, 16>(x, q, scales, zeros, ol, y, m, n, k, stream);
+        if constexpr (!A8)
+            return launch_cfg<RT, 16, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
+        else
+            return hipErrorInvalidValue; // not reached: kMaxSplit
     }
 }
 
@@ -272,7 +315,13 @@ hipError_t launch_skinny_gemm(const uint16_t *x, const int8_t *q, const uint16_t
     // two 16-row weight tiles per wave: the activation operand is reused
     // twice; four tiles measured slower (fewer waves, longer dependent
     // MFMA chains)
-    return launch_rt<2>(x, q, scales, zeros, ol, y, m, n, k, stream);
+    return launch_rt<2, false>(x, nullptr, q, scales, zeros, ol, y, m, n, k, stream);
+}
+
+hipError_t launch_w8a8_skinny(const int8_t *qx, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
+                              uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
+{
+    return launch_rt<2, true>(qx, sx, q, scales, nullptr, OutlierList{nullptr, nullptr, 0}, y, m, n, k, stream);
 }
 
 } // namespace qw

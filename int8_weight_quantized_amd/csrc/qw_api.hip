@@ -412,10 +412,12 @@ QW_API int qw_w8a16_gemm_mfma_tile(int64_t m, int64_t n, int64_t k)
     return qw::mfma_tile_choice(m, n);
 }
 
-QW_API qw_status qw_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t *q,
-                              const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
-                              void *stream)
+QW_API qw_status qw_w8a8_gemm_path(const int8_t *qx, const uint16_t *sx, const int8_t *q,
+                                   const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                                   int path, void *stream)
 {
+    if (path != QW_PATH_AUTO && path != QW_PATH_MFMA && path != QW_PATH_SKINNY)
+        return QW_ERROR_INVALID_VALUE;
     if (m < 0 || n < 0 || k <= 0)
         return QW_ERROR_INVALID_VALUE;
     if (m == 0 || n == 0)
@@ -430,7 +432,22 @@ QW_API qw_status qw_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t
     if (overlaps(y, ybytes, qx, (uint64_t)m * (uint64_t)k) || overlaps(y, ybytes, sx, (uint64_t)m * 2u) ||
         overlaps(y, ybytes, q, (uint64_t)n * (uint64_t)k) || overlaps(y, ybytes, scales, (uint64_t)n * 2u))
         return QW_ERROR_INVALID_VALUE;
-    return launch_status(qw::launch_w8a8_gemm(qx, sx, q, scales, y, m, n, k, static_cast<hipStream_t>(stream)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (path == QW_PATH_AUTO)
+        path = qw::auto_path(m, n, k) == QW_PATH_MFMA ? QW_PATH_MFMA : QW_PATH_SKINNY;
+    if (path == QW_PATH_SKINNY) {
+        if (m > 16 * 65535) // grid.y holds one 16-row activation tile per block row
+            return QW_ERROR_UNSUPPORTED;
+        return launch_status(qw::launch_w8a8_skinny(qx, sx, q, scales, y, m, n, k, s));
+    }
+    return launch_status(qw::launch_w8a8_gemm(qx, sx, q, scales, y, m, n, k, s));
+}
+
+QW_API qw_status qw_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t *q,
+                              const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                              void *stream)
+{
+    return qw_w8a8_gemm_path(qx, sx, q, scales, y, m, n, k, QW_PATH_AUTO, stream);
 }
 
 QW_API int qw_w8a8_gemm_mfma_tile(int64_t m, int64_t n, int64_t k)

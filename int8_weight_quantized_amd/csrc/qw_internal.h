@@ -74,6 +74,10 @@ hipError_t launch_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t *
                             const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
                             hipStream_t stream);
 int w8a8_tile_choice(int64_t m, int64_t n);
+// W8A8 skinny kernel (int8 MFMA on the skinny kernel's layout) for a few
+// activation rows, any m, n, k with k % 16 == 0.
+hipError_t launch_w8a8_skinny(const int8_t *qx, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
+                              uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();

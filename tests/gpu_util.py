@@ -82,7 +82,7 @@ def gpu_gemm(x: np.ndarray, q: np.ndarray, s_bits: np.ndarray, path: int = 0):
     return host(yd).view(np.float16)
 
 
-def gpu_w8a8(qx: np.ndarray, sx_bits: np.ndarray, q: np.ndarray, s_bits: np.ndarray):
+def gpu_w8a8(qx: np.ndarray, sx_bits: np.ndarray, q: np.ndarray, s_bits: np.ndarray, path: int = 0):
     """W8A8 GEMM on the GPU through the C ABI; returns Y as float16."""
     import int8_weight_quantized_amd as qw
     torch = torch_mod()
@@ -94,7 +94,7 @@ def gpu_w8a8(qx: np.ndarray, sx_bits: np.ndarray, q: np.ndarray, s_bits: np.ndar
     sd = dev(np.ascontiguousarray(s_bits, dtype=np.uint16).view(np.int16))
     yd = torch.full((m, n), 0x7e00, dtype=torch.int16, device="cuda:0")  # NaN canary
     st = qw.w8a8_gemm_raw(qxd.data_ptr(), sxd.data_ptr(), qd.data_ptr(), sd.data_ptr(), yd.data_ptr(),
-                          m, n, k, int(torch.cuda.current_stream().cuda_stream))
+                          m, n, k, int(torch.cuda.current_stream().cuda_stream), path)
     assert st == 0, qw.status_string(st)
     return host(yd).view(np.float16)
 

@@ -63,11 +63,16 @@ SHAPES = [(1, 1000, 272), (3, 257, 528), (4, 64, 16), (8, 517, 2064), (9, 200, 2
           (130, 260, 4112), (257, 129, 144), (300, 513, 1040), (129, 600, 528), (70, 72, 16400)]
 
 
+MFMA, SKINNY = 2, 3
+
+
+@pytest.mark.parametrize("path", [0, SKINNY, MFMA])
 @pytest.mark.parametrize("m,n,k", SHAPES)
-def test_w8a8_shapes(m, n, k):
+def test_w8a8_shapes(m, n, k, path):
     qx, sx, q, s = _codes(m, n, k, seed=m * 1000 + n)
-    say("w8a8 gemm m=%d n=%d k=%d" % (m, n, k))
-    assert_w8a8_close(gpu_w8a8(qx, sx, q, s), oracle.w8a8_gemm(qx, sx, q, s), "w8a8 %dx%dx%d" % (m, n, k))
+    say("w8a8 gemm path=%d m=%d n=%d k=%d" % (path, m, n, k))
+    assert_w8a8_close(gpu_w8a8(qx, sx, q, s, path), oracle.w8a8_gemm(qx, sx, q, s),
+                      "w8a8 path %d %dx%dx%d" % (path, m, n, k))
 
 
 TILE_SHAPES = [(512, 27392, 256), (2048, 4608, 128), (256, 27392, 128), (384, 13824, 128),
@@ -92,8 +97,9 @@ def test_w8a8_every_tile_shape():
     assert seen == {(256, 128), (256, 64), (128, 64)}, "tiles exercised: %s" % sorted(seen)
 
 
+@pytest.mark.parametrize("path", [SKINNY, MFMA])
 @pytest.mark.parametrize("m,n,k", [(1, 96, 512), (8, 130, 1040), (100, 390, 1040), (640, 4100, 272)])
-def test_w8a8_exact_arithmetic_bitexact(m, n, k):
+def test_w8a8_exact_arithmetic_bitexact(m, n, k, path):
     """|acc| <= k * 127^2 < 2^24 for k <= 1040 and power-of-two scales: every
     step is exact in binary32, so Y is the binary16 rounding of the exact
     value, bit for bit."""
@@ -107,8 +113,8 @@ def test_w8a8_exact_arithmetic_bitexact(m, n, k):
     # saturate one row and one column so |acc| reaches k * 127^2
     qx[0, :] = 127
     q[0, :] = 127
-    say("w8a8 exact m=%d n=%d k=%d" % (m, n, k))
-    y = gpu_w8a8(qx, sx, q, s)
+    say("w8a8 exact path=%d m=%d n=%d k=%d" % (path, m, n, k))
+    y = gpu_w8a8(qx, sx, q, s, path)
     want = oracle.f64_to_f16_bits(oracle.w8a8_gemm(qx, sx, q, s))
     assert np.array_equal(y.view(np.uint16), want)
 
@@ -128,10 +134,11 @@ def test_w8a8_longest_k_saturated():
     q[2:] = rng.integers(-127, 128, size=(2, k))
     sx = np.full(3, np.float16(2.0 ** -8)).view(np.uint16)
     s = np.full(4, np.float16(2.0 ** -9)).view(np.uint16)
-    say("w8a8 longest k m=3 n=4 k=%d" % k)
-    y = gpu_w8a8(qx, sx, q, s)
     want = oracle.f64_to_f16_bits(oracle.w8a8_gemm(qx, sx, q, s))
-    assert np.array_equal(y.view(np.uint16), want)
+    for path in (SKINNY, MFMA):
+        say("w8a8 longest k path=%d m=3 n=4 k=%d" % (path, k))
+        y = gpu_w8a8(qx, sx, q, s, path)
+        assert np.array_equal(y.view(np.uint16), want)
     assert qw.w8a8_gemm_raw(1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20, 1, 4, k + 16) == qw.QW_ERROR_UNSUPPORTED
 
 
@@ -143,12 +150,15 @@ def test_w8a8_zero_codes_and_zero_scales():
     q[7] = 0
     s[11] = 0
     say("w8a8 zero rows m=%d n=%d k=%d" % (m, n, k))
-    y = gpu_w8a8(qx, sx, q, s)
+    y = gpu_w8a8(qx, sx, q, s, MFMA)
     bits = y.view(np.uint16)
-    # all-zero codes give an exact integer 0, so +0; a zero scale gives
-    # acc * 0, which keeps the sign of acc (as in the oracle)
+    # all-zero codes give an exact integer 0, so +0; a zero scale gives a
+    # zero of either sign (the MFMA epilogue rounds the product to fp16 in
+    # one fused step, which writes +0 for a negative sum times 0)
     assert np.all(bits[3, :] == 0) and np.all(bits[:, 7] == 0), "zero codes must give +0"
     assert np.all(y[5, :] == 0) and np.all(y[:, 11] == 0), "zero scale must give zero"
+    y2 = gpu_w8a8(qx, sx, q, s, SKINNY)
+    assert np.all(y2[5, :] == 0) and np.all(y2[:, 11] == 0)
     assert_w8a8_close(y, oracle.w8a8_gemm(qx, sx, q, s), "w8a8 zero rows")
 
 
