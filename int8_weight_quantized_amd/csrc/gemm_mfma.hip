@@ -162,7 +162,7 @@ using stage_t = std::integral_constant<int, I>;
 // the epilogue multiplies by S[n] * Sx[m].  Otherwise x is fp16 and sx is
 // unused.  OL: exact outlier side lists (at most kMfmaOutlierSlots per
 // weight row) are added while their activation column sits in LDS.
-template <int NW, int BN, int BM, bool A8, bool OL = false>
+template <int NW, int BN, int BM, bool A8, bool OL = false, bool ZP = false>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm_dma_kernel(
     const void *__restrict__ xv, const uint16_t *__restrict__ sx, const int8_t *__restrict__ q,
@@ -289,7 +289,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
 #pragma unroll
     for (int i = 0; i < C::kSI; ++i) {
         const int zr = n0 + wrow + 32 * i;
-        zbias[i] = zero_point_bias(zeros != nullptr && zr < n ? (int)zeros[zr] : 0);
+        zbias[i] = zero_point_bias(ZP && zr < n ? (int)zeros[zr] : 0); // ZP: symmetric kernels keep the constant
     }
 
     auto compute_a8 = [&](const uint8_t *st) {
@@ -566,6 +566,14 @@ hipError_t launch_dma(const void *x, const uint16_t *sx, const int8_t *q, const 
     }
     if (ol.idx != nullptr)
         return hipErrorInvalidValue;
+    if constexpr (!A8) {
+        if (zeros != nullptr) {
+            hipLaunchKernelGGL((mfma_gemm_dma_kernel<NW, BN, BM, false, false, true>), dim3((unsigned)blocks),
+                               dim3(NW * kWave), 0, stream, x, sx, q, scales, zeros, ol, y, (int)m, (int)n,
+                               (int)k, (int)tiles_m, (int)tiles_n);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((mfma_gemm_dma_kernel<NW, BN, BM, A8>), dim3((unsigned)blocks), dim3(NW * kWave),
                        0, stream, x, sx, q, scales, zeros, ol, y, (int)m, (int)n, (int)k, (int)tiles_m,
                        (int)tiles_n);
