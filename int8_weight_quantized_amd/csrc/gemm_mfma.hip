@@ -189,7 +189,9 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
 
     const int tid = threadIdx.x;
     const int lane = __lane_id();
-    const int wave = tid / kWave;
+    // wave-uniform (an SGPR): LDS-DMA destinations derived from it are
+    // scalar, so setting M0 needs no v_readfirstlane per copy
+    const int wave = __builtin_amdgcn_readlane(tid / kWave, 0);
 
     const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
     const int tn = tile / tiles_m;
@@ -210,9 +212,50 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
     const int xchunk_even = (lane % 8) ^ xslot(lane / 8);
     const int xchunk_odd = (lane % 8) ^ xslot(8 + lane / 8);
 
+    // Per-lane byte offsets of this wave's copies from the tile's first row
+    // at k = 0 (row clamped to the matrix); each full step then adds only
+    // the wave-uniform k0 to a scalar base, so the copies can use the
+    // scalar-base plus 32-bit-offset address form instead of per-step
+    // 64-bit address math.
+    uint32_t woff[C::kWInstr], xoff[C::kXInstr];
+#pragma unroll
+    for (int i = 0; i < C::kWInstr; ++i) {
+        const int row = (wave * C::kWInstr + i) * 16 + lane / 4;
+        woff[i] = (uint32_t)((min(n0 + row, n - 1) - n0) * k + wchunk * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < C::kXInstr; ++i) {
+        if constexpr (A8) {
+            const int row = (wave * C::kXInstr + i) * 16 + lane / 4;
+            xoff[i] = (uint32_t)((min(m0 + row, m - 1) - m0) * k + wchunk * 16);
+        } else {
+            const int row = (wave * C::kXInstr + i) * 8 + lane / 8;
+            xoff[i] = (uint32_t)(((min(m0 + row, m - 1) - m0) * k + ((i & 1) ? xchunk_odd : xchunk_even) * 8) * 2);
+        }
+    }
+    const int8_t *wtile = q + (int64_t)n0 * k;
+    const uint8_t *xtile = static_cast<const uint8_t *>(xv) + (int64_t)m0 * k * (A8 ? 1 : 2);
+
     // copy tile kt into stage array st; FULL: every chunk lies inside k
     auto issue = [&](int kt, uint8_t *st, auto full) {
         const int k0 = kt * kBK;
+        if constexpr (decltype(full)::value) {
+            const int8_t *wb = wtile + k0;
+            const uint8_t *xb = xtile + (int64_t)k0 * (A8 ? 1 : 2);
+#pragma unroll
+            for (int i = 0; i < C::kWInstr; ++i) {
+                uint8_t *dst = st + (wave * C::kWInstr + i) * 1024;
+                const int8_t *src = wb + woff[i];
+                __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 16, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < C::kXInstr; ++i) {
+                uint8_t *dst = st + C::kWBytes + (wave * C::kXInstr + i) * 1024;
+                const uint8_t *src = xb + xoff[i];
+                __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 16, 0, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < C::kWInstr; ++i) {
             uint8_t *dst = st + (wave * C::kWInstr + i) * 1024;
@@ -603,7 +646,14 @@ template <int BN, int BM, bool A8>
 bool fills(int64_t m, int64_t n)
 {
     const int64_t tiles = ((n + BN - 1) / BN) * ((m + BM - 1) / BM);
-    const int64_t slots = slots_per_cu<BN, BM, A8>() * (int64_t)device_cu_count();
+    // The fp16 128 x 128 tile is counted at two workgroups per CU even where
+    // its registers allow three: per-shape tuning measured it fastest at 256
+    // rows (N = 27392), where counting the third slot would pass it over
+    // for 128 x 64.
+    int64_t per_cu = slots_per_cu<BN, BM, A8>();
+    if (!A8 && BN == 128 && BM == 128 && per_cu > 2)
+        per_cu = 2;
+    const int64_t slots = per_cu * (int64_t)device_cu_count();
     return 4 * tiles >= 3 * slots;
 }
 
