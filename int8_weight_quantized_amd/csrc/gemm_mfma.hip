@@ -236,24 +236,37 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
     const int8_t *wtile = q + (int64_t)n0 * k;
     const uint8_t *xtile = static_cast<const uint8_t *>(xv) + (int64_t)m0 * k * (A8 ? 1 : 2);
 
+    // Copies of a tile that lies wholly inside k, in four groups: group g
+    // (0..3) is this wave's weight and activation copies i with i % 4 == g.
+    auto issue_group = [&](int kt, uint8_t *st, int g) {
+        const int k0 = kt * kBK;
+        const int8_t *wb = wtile + k0;
+        const uint8_t *xb = xtile + (int64_t)k0 * (A8 ? 1 : 2);
+#pragma unroll
+        for (int i = 0; i < C::kWInstr; ++i) {
+            if (i % 4 != g)
+                continue;
+            uint8_t *dst = st + (wave * C::kWInstr + i) * 1024;
+            const int8_t *src = wb + woff[i];
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 16, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < C::kXInstr; ++i) {
+            if (i % 4 != g)
+                continue;
+            uint8_t *dst = st + C::kWBytes + (wave * C::kXInstr + i) * 1024;
+            const uint8_t *src = xb + xoff[i];
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 16, 0, 0);
+        }
+    };
+
     // copy tile kt into stage array st; FULL: every chunk lies inside k
     auto issue = [&](int kt, uint8_t *st, auto full) {
         const int k0 = kt * kBK;
         if constexpr (decltype(full)::value) {
-            const int8_t *wb = wtile + k0;
-            const uint8_t *xb = xtile + (int64_t)k0 * (A8 ? 1 : 2);
 #pragma unroll
-            for (int i = 0; i < C::kWInstr; ++i) {
-                uint8_t *dst = st + (wave * C::kWInstr + i) * 1024;
-                const int8_t *src = wb + woff[i];
-                __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 16, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < C::kXInstr; ++i) {
-                uint8_t *dst = st + C::kWBytes + (wave * C::kXInstr + i) * 1024;
-                const uint8_t *src = xb + xoff[i];
-                __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 16, 0, 0);
-            }
+            for (int g = 0; g < 4; ++g)
+                issue_group(kt, st, g);
             return;
         }
 #pragma unroll
@@ -364,7 +377,16 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
                         __builtin_bit_cast(int4v, chi[i]), __builtin_bit_cast(int4v, bhi[j]), acc[i][j], 0, 0, 0);
     };
 
-    auto compute = [&](const uint8_t *st) {
+    // The 256-channel fp16 tiles spread a full step's copies over the step
+    // (see step below).  Their activation operands are then read one MFMA
+    // group ahead, so that the copies can sit between the groups without
+    // all of them live at once.  The 128-channel tiles measured slower with
+    // spread copies (3% on 128 x 128, 11% on 128 x 64) and keep them at the
+    // top of the step.
+    constexpr bool kSpreadTile = !A8 && !OL && BN == 256;
+
+    // before_group(s) runs ahead of MFMA group s = 0..3 of the fp16 path
+    auto compute = [&](const uint8_t *st, auto &&before_group) {
       if constexpr (A8) {
         compute_a8(st);
       } else {
@@ -375,13 +397,19 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
             chi[i] = *reinterpret_cast<const u32x4_t *>(st + w_off1 + i * 32 * kBK);
         }
         half8_t b[kSJ][4];
+        auto load_b = [&](int sidx) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < kSJ; ++j)
-#pragma unroll
-            for (int sidx = 0; sidx < 4; ++sidx)
+            for (int j = 0; j < kSJ; ++j)
                 b[j][sidx] = *reinterpret_cast<const half8_t *>(st + x_off[sidx] + j * 32 * 2 * kBK);
+        };
+#pragma unroll
+        for (int sidx = 0; sidx < (kSpreadTile ? 1 : 4); ++sidx)
+            load_b(sidx);
 #pragma unroll
         for (int sidx = 0; sidx < 4; ++sidx) {
+            before_group(sidx);
+            if (kSpreadTile && sidx + 1 < 4)
+                load_b(sidx + 1);
 #pragma unroll
             for (int i = 0; i < C::kSI; ++i) {
                 const u32x4_t c = sidx < 2 ? clo[i] : chi[i];
@@ -490,22 +518,35 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
     // publishes everyone's copies and certifies that tile t-1's stage is no
     // longer read, tile t + 1 is copied into that stage while tile t is
     // multiplied.  FULL: tile t + 1 lies inside k (no per-chunk checks).
+    //
+    // A full step of a 256-channel fp16 tile spreads its copies over the
+    // step: copy group g goes out right before MFMA group g (1-4% faster
+    // than all copies at the top).  Other steps issue every copy at
+    // the top.  Either way a scheduling barrier
+    // pins the copies where they are: nothing ties them to the MFMAs, and
+    // the scheduler would otherwise sink them below the whole step, right
+    // before the wait for them.
     auto step = [&](int t, auto s, auto full) {
         constexpr int S = decltype(s)::value;
+        constexpr bool kSpread = decltype(full)::value && kSpreadTile;
         QW_WAIT_VMCNT(0);
         ring_barrier();
-        if (decltype(full)::value || t + 1 < ktiles)
-            issue(t + 1, ring(stage_t<1 - S>{}), full);
-        // keep the copies at the top of the step: nothing ties them to the
-        // MFMAs, and the scheduler would otherwise sink them below the
-        // whole step, right before the wait for them
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!kSpread) {
+            if (decltype(full)::value || t + 1 < ktiles)
+                issue(t + 1, ring(stage_t<1 - S>{}), full);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         // outliers before this step's MFMAs: their adds then depend only on
         // the previous step's MFMAs, long finished (after them, each add
         // would wait for this step's whole MFMA chain on its accumulator)
         if constexpr (OL)
             add_outliers(t, ring(s));
-        compute(ring(s));
+        compute(ring(s), [&](int g) __attribute__((always_inline)) {
+            if constexpr (kSpread) {
+                issue_group(t + 1, ring(stage_t<1 - S>{}), g);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
     };
     // steady state: pairs of steps whose next tile is full
     int t = 0;
