@@ -59,6 +59,10 @@ typedef enum qw_status {
 /* Longest reduction qw_w8a8_gemm accepts: the int32 accumulator holds
  * k * 127 * 127 without overflow for k <= 2^17. */
 #define QW_W8A8_MAX_K 131072
+/* Longest reduction the LDS-tiled MFMA kernel (QW_PATH_MFMA) takes: its
+ * 32-bit in-tile offsets stay below 2^31 for k <= 2^23.  qw_w8a16_gemm runs
+ * longer rows on the skinny kernel. */
+#define QW_MFMA_MAX_K 8388608
 
 /*
  * qw_quantize_weights -- per-output-channel symmetric int8 quantization.
@@ -280,8 +284,9 @@ QW_API qw_status qw_quantize_weights_asym(const float *w, int64_t n, int64_t k, 
  *
  * The kernel is chosen from m, n and k: a bandwidth-bound VALU GEMV for
  * decode (m <= 2), a skinny MFMA kernel on register-dequantized weights for
- * a few activation rows (m <= 16, or m <= 64 when n <= 16384), and the
- * LDS-tiled MFMA GEMM (tile shape picked from the grid it fills) otherwise.
+ * a few activation rows (m <= 16, or m <= 64 when n <= 16384) and for
+ * k > QW_MFMA_MAX_K, and the LDS-tiled MFMA GEMM (tile shape picked from the
+ * grid it fills) otherwise.
  *
  * Errors: QW_ERROR_INVALID_VALUE (null pointer with m, n > 0, negative
  * size, k <= 0, y overlapping x, q or scales), QW_ERROR_UNSUPPORTED
@@ -305,8 +310,9 @@ typedef enum qw_gemm_path {
  * tests of each path and for measuring the decode/prefill crossover.  Same
  * arguments, result contract and errors as qw_w8a16_gemm, plus
  * QW_ERROR_INVALID_VALUE for an unknown path and QW_ERROR_UNSUPPORTED when
- * QW_PATH_GEMV is forced outside its limits (m > 8, or m * ceil(k / 1024)
- * > 32).
+ * a kernel is forced outside its limits: QW_PATH_GEMV with m > 8 or
+ * m * ceil(k / 1024) > 32, QW_PATH_MFMA with k > QW_MFMA_MAX_K,
+ * QW_PATH_SKINNY with m > 16 * 65535.
  */
 QW_API qw_status qw_w8a16_gemm_path(const uint16_t *x, const int8_t *q,
                                     const uint16_t *scales, uint16_t *y,

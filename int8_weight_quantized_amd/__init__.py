@@ -34,6 +34,8 @@ QW_ERROR_LAUNCH = 4
 
 PATHS = {"auto": 0, "gemv": 1, "mfma": 2, "skinny": 3}
 QUANTIZE_MAX_K = 65536
+MFMA_MAX_K = 8388608     # longest reduction of the LDS-tiled MFMA kernel
+W8A8_MAX_K = 131072
 
 
 class QwError(RuntimeError):

@@ -122,6 +122,10 @@ struct DmaCfg {
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
+// Word 3 of a raw (untyped, unswizzled, stride 0) buffer descriptor on the
+// CDNA family: data format 32 bits per element, every other field 0.
+constexpr int kBufferFlags = 0x00020000;
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
 #define QW_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14))
@@ -235,28 +239,37 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
     }
     const int8_t *wtile = q + (int64_t)n0 * k;
     const uint8_t *xtile = static_cast<const uint8_t *>(xv) + (int64_t)m0 * k * (A8 ? 1 : 2);
+    // Buffer resources over this workgroup's weight and activation rows, so
+    // that a full step's copies take the lane's 32-bit offset in a VGPR and
+    // the step's k offset in an SGPR: no per-copy address arithmetic.  The
+    // byte range (an unsigned 32-bit field; k <= 2^23 keeps it within 2^31)
+    // covers the tile's rows; every copy lies inside it.
+    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t *>(wtile), (short)0,
+        static_cast<int>(static_cast<uint32_t>(min((int64_t)BN, (int64_t)(n - n0)) * k)), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(xtile), (short)0,
+        static_cast<int>(static_cast<uint32_t>(min((int64_t)BM, (int64_t)(m - m0)) * k * (A8 ? 1 : 2))),
+        kBufferFlags);
 
     // Copies of a tile that lies wholly inside k, in four groups: group g
     // (0..3) is this wave's weight and activation copies i with i % 4 == g.
     auto issue_group = [&](int kt, uint8_t *st, int g) {
         const int k0 = kt * kBK;
-        const int8_t *wb = wtile + k0;
-        const uint8_t *xb = xtile + (int64_t)k0 * (A8 ? 1 : 2);
 #pragma unroll
         for (int i = 0; i < C::kWInstr; ++i) {
             if (i % 4 != g)
                 continue;
             uint8_t *dst = st + (wave * C::kWInstr + i) * 1024;
-            const int8_t *src = wb + woff[i];
-            __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, (lds_ptr_t)dst, 16, (int)woff[i], k0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < C::kXInstr; ++i) {
             if (i % 4 != g)
                 continue;
             uint8_t *dst = st + C::kWBytes + (wave * C::kXInstr + i) * 1024;
-            const uint8_t *src = xb + xoff[i];
-            __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, (lds_ptr_t)dst, 16, (int)xoff[i], k0 * (A8 ? 1 : 2), 0,
+                                                     0);
         }
     };
 
@@ -720,6 +733,8 @@ hipError_t launch_tiles(const void *x, const uint16_t *sx, const int8_t *q, cons
                         const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k,
                         hipStream_t stream, int forced_tile = 0)
 {
+    if (k > kMfmaMaxK) // the entry points route such rows elsewhere
+        return hipErrorInvalidValue;
     int tile = forced_tile != 0 ? forced_tile : tile_choice<A8>(m, n);
     if (ol.idx != nullptr && tile == 256128)
         tile = 256064;

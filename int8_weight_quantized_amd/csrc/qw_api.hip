@@ -47,7 +47,8 @@ int auto_path(int64_t m, int64_t n, int64_t k)
     // weight is narrow enough (n <= 16384) that MFMA tiles leave most CUs
     // idle (crossover sweep over m at (k, n) = (4096, 27392), (4096, 4608),
     // (1024, 4096)).
-    if (m <= 16 || (m <= 64 && n <= 16384))
+    // Rows longer than the MFMA kernel takes also go to the skinny kernel.
+    if (m <= 16 || (m <= 64 && n <= 16384) || k > kMfmaMaxK)
         return QW_PATH_SKINNY;
     return QW_PATH_MFMA;
 }
@@ -208,7 +209,8 @@ qw_status gemm_common(const uint16_t *x, const int8_t *q, const uint16_t *scales
         const int tuned = qw::tuned_choice(m, n, k);
         const int tpath = tuned / qw::kChoicePath;
         if (tuned >= 0 && (tpath != QW_PATH_GEMV || qw::gemv_supported(m, k)) &&
-            (tpath != QW_PATH_MFMA || ol.idx == nullptr || ol.cap <= qw::kMfmaOutlierSlots) &&
+            (tpath != QW_PATH_MFMA || ((ol.idx == nullptr || ol.cap <= qw::kMfmaOutlierSlots) &&
+                                       k <= qw::kMfmaMaxK)) &&
             (tpath != QW_PATH_SKINNY || m <= 16 * 65535))
             return launch_status(qw::launch_choice(tuned, x, q, scales, zeros, ol, y, m, n, k, s));
         path = qw::auto_path(m, n, k);
@@ -216,7 +218,7 @@ qw_status gemm_common(const uint16_t *x, const int8_t *q, const uint16_t *scales
         if (path == QW_PATH_MFMA && ol.idx != nullptr && ol.cap > qw::kMfmaOutlierSlots)
             path = QW_PATH_SKINNY;
     }
-    if (path == QW_PATH_MFMA && ol.idx != nullptr && ol.cap > qw::kMfmaOutlierSlots)
+    if (path == QW_PATH_MFMA && ((ol.idx != nullptr && ol.cap > qw::kMfmaOutlierSlots) || k > qw::kMfmaMaxK))
         return QW_ERROR_UNSUPPORTED;
     if (path == QW_PATH_GEMV) {
         if (!qw::gemv_supported(m, k))

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qw.h"
+
 namespace qw {
 
 // Per-row outlier side lists in ELL form: `cap` slots per row, columns in
@@ -25,6 +27,12 @@ struct OutlierList {
 // Side-list slots per row the MFMA kernel stages in LDS; wider lists go to
 // the skinny kernel.
 constexpr int kMfmaOutlierSlots = 4;
+// Longest row the MFMA kernel takes: its per-lane copy offsets within a
+// tile (at most 256 rows x k bytes) and a tile's byte range stay below 2^31.
+// Longer rows go to the skinny kernel, which indexes in 64 bits.
+constexpr int64_t kMfmaMaxK = QW_MFMA_MAX_K;
+static_assert(256 * kMfmaMaxK <= (int64_t(1) << 31) && 255 * kMfmaMaxK + 64 < (int64_t(1) << 31),
+              "MFMA in-tile offsets");
 
 // Per-row quantizer of fp32 (w_is_f16 false) or fp16 weights.  mode 0:
 // absmax bound; mode 1: percentile bound with the rank i (0-based,

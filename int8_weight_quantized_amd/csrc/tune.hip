@@ -83,8 +83,9 @@ hipError_t tune_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
         cands[nc++] = QW_PATH_GEMV * kChoicePath;
     if (m <= 16 * 65535)
         cands[nc++] = QW_PATH_SKINNY * kChoicePath;
-    for (int tile : {256128, 256064, 128128, 128064})
-        cands[nc++] = QW_PATH_MFMA * kChoicePath + tile;
+    if (k <= kMfmaMaxK)
+        for (int tile : {256128, 256064, 128128, 128064})
+            cands[nc++] = QW_PATH_MFMA * kChoicePath + tile;
 
     hipEvent_t ev[2];
     if (hipEventCreate(&ev[0]) != hipSuccess)

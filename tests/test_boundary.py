@@ -309,6 +309,26 @@ def test_auto_path_choice():
         qw.auto_path(1, 4, 24)
 
 
+def test_mfma_row_length_limit():
+    """Rows longer than QW_MFMA_MAX_K: the automatic choice takes the skinny
+    kernel, and a forced MFMA path is refused before anything is enqueued."""
+    big = qw.MFMA_MAX_K + 16
+    assert qw.auto_path(512, 27392, qw.MFMA_MAX_K) == "mfma"
+    assert qw.auto_path(512, 27392, big) == "skinny"
+    assert qw.library().qw_w8a16_gemm_auto_path(4096, 4096, big) == qw.PATHS["skinny"]
+    # fake addresses 1 TiB apart, so that the operands of this size do not overlap
+    x, q, s, y = 1 << 40, 2 << 40, 3 << 40, 4 << 40
+    assert qw.w8a16_gemm_raw(x, q, s, y, 512, 4, big, 0, qw.PATHS["mfma"]) == qw.QW_ERROR_UNSUPPORTED
+
+
+def test_header_size_limits_match_the_binding():
+    text = open(HEADER).read()
+    for name, value in (("QW_QUANTIZE_MAX_K", qw.QUANTIZE_MAX_K), ("QW_MFMA_MAX_K", qw.MFMA_MAX_K),
+                        ("QW_W8A8_MAX_K", qw.W8A8_MAX_K)):
+        m = re.search(r"#define %s (\d+)" % name, text)
+        assert m and int(m.group(1)) == value, name
+
+
 def test_gemm_empty_is_noop():
     assert qw.w8a16_gemm_raw(0, 0, 0, 0, 0, 4, 16) == qw.QW_SUCCESS
     assert qw.w8a16_gemm_raw(0, 0, 0, 0, 3, 0, 16) == qw.QW_SUCCESS

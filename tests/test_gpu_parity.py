@@ -152,6 +152,22 @@ def test_gemm_long_k(m, n, k):
         assert_gemm_close(y, oracle.gemm(x, q, s), "long-k path %d %dx%dx%d" % (path, m, n, k))
 
 
+def test_gemm_rows_beyond_mfma_limit():
+    """k = QW_MFMA_MAX_K + 16 with 65 activation rows, where the MFMA
+    kernel would otherwise run: the automatic choice takes the skinny kernel
+    (64-bit indexing); sampled outputs against the oracle."""
+    import int8_weight_quantized_amd as qw
+    m, n, k = 65, 16, qw.MFMA_MAX_K + 16
+    assert qw.auto_path(m, n, k) == "skinny"
+    x, q, s = _small_case(m, n, k, seed=11)
+    say("gemm auto beyond the MFMA row limit m=%d n=%d k=%d" % (m, n, k))
+    y = gpu_gemm(x, q, s)
+    rng = np.random.default_rng(5)
+    mi = np.r_[0, m - 1, 16, 64, rng.integers(0, m, 28)]
+    ni = np.r_[0, n - 1, 15, 8, rng.integers(0, n, 28)]
+    assert_gemm_close(y[mi, ni], oracle.gemm_sampled(x, q, s, mi, ni), "k beyond the MFMA limit (sampled)")
+
+
 @pytest.mark.parametrize("m,n,k", MFMA_SHAPES)
 def test_mfma_small_shapes(m, n, k):
     x, q, s = _small_case(m, n, k, seed=m * 1000 + n)
