@@ -218,7 +218,7 @@ def time_w8a8(wl, launches=40, warmup=10):
     aq_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / launches
     pair_ms = sum(e[0].elapsed_time(e[2]) for e in ev) / launches
     ops = gemm_flops(wl.m, wl.n, wl.k)
-    mfma = r.qw.auto_path(wl.m, wl.n, wl.k) == "mfma"  # the W8A8 kernel choice follows the W8A16 one
+    mfma = r.qw.w8a8_auto_path(wl.m, wl.n, wl.k) == "mfma"
     tile = list(r.qw.w8a8_tile(wl.m, wl.n, wl.k)) if mfma else None
     sets = r.sets
     del r
@@ -354,7 +354,8 @@ def cpu_baseline(wl, target_s=10.0, max_s=30.0):
 
 def sweep_paths(ms=(1, 2, 3, 4, 8, 16, 24, 32, 48, 64, 96, 128, 256, 512),
                 shapes=((4096, 27392), (4096, 4608), (1024, 4096))):
-    """Cold timing of each GEMM kernel across m (random codes; timing only)."""
+    """Cold timing of each W8A16 and W8A8 GEMM kernel across m (random codes;
+    timing only)."""
     import torch
 
     import int8_weight_quantized_amd as qw
@@ -368,12 +369,15 @@ def sweep_paths(ms=(1, 2, 3, 4, 8, 16, 24, 32, 48, 64, 96, 128, 256, 512),
                  for _ in range(sets)]
             s = [torch.rand((n,), device="cuda:0", generator=g).half() * 1e-3 for _ in range(sets)]
             x = [torch.randn((m, k), device="cuda:0", generator=g).half() for _ in range(sets)]
+            qx = [torch.randint(-127, 128, (m, k), dtype=torch.int8, device="cuda:0", generator=g)
+                  for _ in range(sets)]
+            sx = [torch.rand((m,), device="cuda:0", generator=g).half() * 1e-2 for _ in range(sets)]
             y = [torch.empty((m, n), dtype=torch.float16, device="cuda:0") for _ in range(sets)]
-            for name, path in (("gemv", 1), ("skinny", 3), ("mfma", 2)):
-                if name == "skinny" and m > 64:
-                    continue
-
+            for name, path in (("gemv", 1), ("skinny", 3), ("mfma", 2), ("w8a8_skinny", 3), ("w8a8_mfma", 2)):
                 def launch(i):
+                    if name.startswith("w8a8"):
+                        return qw.w8a8_gemm_raw(qx[i].data_ptr(), sx[i].data_ptr(), q[i].data_ptr(),
+                                                s[i].data_ptr(), y[i].data_ptr(), m, n, k, stream, path)
                     return qw.w8a16_gemm_raw(x[i].data_ptr(), q[i].data_ptr(), s[i].data_ptr(),
                                              y[i].data_ptr(), m, n, k, stream, path)
                 if launch(0) != 0:
@@ -391,11 +395,13 @@ def sweep_paths(ms=(1, 2, 3, 4, 8, 16, 24, 32, 48, 64, 96, 128, 256, 512),
                 ms_ = sorted(a.elapsed_time(b) for a, b in ev)
                 avg = sum(ms_) / len(ms_)
                 print(json.dumps({"sweep": "gemm_paths", "k": k, "n": n, "m": m, "kernel": name,
-                                  "auto": qw.auto_path(m, n, k), "avg_us": avg * 1e3,
+                                  "auto": qw.auto_path(m, n, k), "auto_w8a8": qw.w8a8_auto_path(m, n, k),
+                                  "avg_us": avg * 1e3,
                                   "median_us": ms_[len(ms_) // 2] * 1e3,
-                                  "TBps": gbytes / (avg * 1e-3) / 1e12,
+                                  "TBps": (w8a8_bytes(m, n, k) if name.startswith("w8a8") else gbytes)
+                                  / (avg * 1e-3) / 1e12,
                                   "TFLOPs": gemm_flops(m, n, k) / (avg * 1e-3) / 1e12}), flush=True)
-            del q, s, x, y
+            del q, s, x, qx, sx, y
             torch.cuda.empty_cache()
 
 

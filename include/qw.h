@@ -284,9 +284,10 @@ QW_API qw_status qw_quantize_weights_asym(const float *w, int64_t n, int64_t k, 
  *
  * The kernel is chosen from m, n and k: a bandwidth-bound VALU GEMV for
  * decode (m <= 2), a skinny MFMA kernel on register-dequantized weights for
- * a few activation rows (m <= 16, or m <= 64 when n <= 16384) and for
- * k > QW_MFMA_MAX_K, and the LDS-tiled MFMA GEMM (tile shape picked from the
- * grid it fills) otherwise.
+ * a few activation rows (m <= 16, and beyond while the weight bytes it
+ * reads again in its passes after the first, one per 16 or 32 rows, stay
+ * within 96 MiB) and for k > QW_MFMA_MAX_K, and the LDS-tiled MFMA GEMM
+ * (tile shape picked from the grid it fills) otherwise.
  *
  * Errors: QW_ERROR_INVALID_VALUE (null pointer with m, n > 0, negative
  * size, k <= 0, y overlapping x, q or scales), QW_ERROR_UNSUPPORTED
@@ -446,6 +447,12 @@ QW_API qw_status qw_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t
 QW_API qw_status qw_w8a8_gemm_path(const int8_t *qx, const uint16_t *sx, const int8_t *q,
                                    const uint16_t *scales, uint16_t *y, int64_t m, int64_t n,
                                    int64_t k, int path, void *stream);
+
+/*
+ * qw_w8a8_gemm_auto_path -- the kernel qw_w8a8_gemm runs for this shape:
+ * QW_PATH_SKINNY or QW_PATH_MFMA; -1 for a shape qw_w8a8_gemm rejects.
+ */
+QW_API int qw_w8a8_gemm_auto_path(int64_t m, int64_t n, int64_t k);
 
 /*
  * qw_w8a8_gemm_mfma_tile -- the output tile qw_w8a8_gemm uses for this

@@ -99,6 +99,8 @@ def _load():
     lib.qw_w8a8_gemm_path.restype = ctypes.c_int
     lib.qw_w8a8_gemm.restype = ctypes.c_int
     lib.qw_w8a8_gemm_mfma_tile.argtypes = [i64, i64, i64]
+    lib.qw_w8a8_gemm_auto_path.argtypes = [i64, i64, i64]
+    lib.qw_w8a8_gemm_auto_path.restype = ctypes.c_int
     lib.qw_w8a8_gemm_mfma_tile.restype = ctypes.c_int
     lib.qw_w8a16_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     lib.qw_w8a16_gemm.restype = ctypes.c_int
@@ -147,6 +149,14 @@ def mfma_tile(m: int, n: int, k: int):
     if t < 0:
         raise ValueError("no MFMA tile for m=%d n=%d k=%d (bad shape or no device)" % (m, n, k))
     return t // 1000, t % 1000
+
+
+def w8a8_auto_path(m: int, n: int, k: int) -> str:
+    """Name of the kernel qw_w8a8_gemm runs for this shape."""
+    p = int(library().qw_w8a8_gemm_auto_path(m, n, k))
+    if p < 0:
+        raise ValueError("unsupported W8A8 GEMM shape m=%d n=%d k=%d" % (m, n, k))
+    return PATH_NAMES[p]
 
 
 def w8a8_tile(m: int, n: int, k: int):

@@ -10,7 +10,7 @@
 // in registers and used as the MFMA "A" operand; the activations are the "B"
 // operand (16 columns, rows beyond m are zero).
 //
-// Work split: a workgroup of KSPLIT waves owns RT x 16 weight rows x 16
+// Work split: a workgroup of KSPLIT waves owns RT x 16 weight rows x MT x 16
 // activation rows; wave w walks the k steps [w*S/KSPLIT, (w+1)*S/KSPLIT)
 // of the S = ceil(k/64) steps of 64, four steps (256 codes of each row) per
 // iteration.  The MFMA layout wants lane l (row r = l % 16, group
@@ -22,7 +22,9 @@
 // codes a lane holds per step, the first 8 feed one MFMA (k slots
 // 8 g .. 8 g + 7 of a 32-wide k block), the last 8 a second one; the
 // activation operand is loaded once with the same k assignment and reused
-// by all RT row tiles.  KSPLIT is chosen so the grid has enough waves to
+// by all RT row tiles, and each cast weight operand feeds the MFMAs of all
+// MT activation tiles (so up to 16 MT activation rows take one pass over the
+// weights).  KSPLIT is chosen so the grid has enough waves to
 // keep HBM busy.  The KSPLIT partial tiles are summed in LDS in wave order
 // (deterministic), then scaled (the scales are loaded at the start, so their
 // latency hides under the main loop), rounded to fp16 and transposed
@@ -47,7 +49,7 @@ constexpr int kSkinnyTargetWaves = 2048; // enough in-flight loads to fill HBM
 // the activation codes the B operand with the same assignment, the
 // accumulators are exact int32, and the epilogue scales by S[n] * Sx[m].
 // Zero points and side lists are W8A16 only (null with A8).
-template <int RT, int KSPLIT, bool A8 = false, bool ZP = false>
+template <int RT, int MT, int KSPLIT, bool A8 = false, bool ZP = false>
 __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
     const void *__restrict__ xv, const uint16_t *__restrict__ sx, const int8_t *__restrict__ q,
     const uint16_t *__restrict__ scales, const int8_t *__restrict__ zeros, OutlierList ol,
@@ -60,10 +62,10 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
     // holds the partial tiles of waves 1 .. KSPLIT-1.
     constexpr int kStageRow = 64 * kSkinnyUnroll + 16; // 256 codes + pad
     constexpr int kStageBytes = KSPLIT * RT * 16 * kStageRow;
-    constexpr int kPartialBytes = (KSPLIT > 1 ? KSPLIT - 1 : 1) * RT * kWave * (int)sizeof(acc_t);
+    constexpr int kPartialBytes = (KSPLIT > 1 ? KSPLIT - 1 : 1) * RT * MT * kWave * (int)sizeof(acc_t);
     __shared__ __attribute__((aligned(16))) uint8_t smem[kStageBytes > kPartialBytes ? kStageBytes : kPartialBytes];
     // the finished fp16 tile, [activation row][channel], padded rows
-    __shared__ __attribute__((aligned(16))) uint16_t ytile[16][16 * RT + 8];
+    __shared__ __attribute__((aligned(16))) uint16_t ytile[16 * MT][16 * RT + 8];
     static_assert(kSkinnyUnroll == 4, "one iteration covers 256 codes of a row");
 
     const int lane = __lane_id();
@@ -71,8 +73,7 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
     const int r = lane % 16;
     const int g = lane / 16;
     const int n0 = blockIdx.x * 16 * RT;
-    const int m0 = blockIdx.y * 16;
-    const int col = m0 + r; // activation row this lane feeds into the B operand
+    const int m0 = blockIdx.y * 16 * MT;
 
     const int steps_total = (k + 63) / 64;
     const int s_begin = (int)(((int64_t)wave * steps_total) / KSPLIT);
@@ -86,9 +87,18 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
         row_ok[t] = row < n;
         qrow[t] = q + (int64_t)(row_ok[t] ? row : 0) * k;
     }
-    const uint16_t *xrow = x + (int64_t)(col < m ? col : 0) * k;
-    const int8_t *qxrow = static_cast<const int8_t *>(xv) + (int64_t)(col < m ? col : 0) * k;
-    const bool col_ok = col < m;
+    // activation row m0 + 16 mt + r is what this lane feeds into the B
+    // operand of activation tile mt
+    const uint16_t *xrow[MT];
+    const int8_t *qxrow[MT];
+    bool col_ok[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int col = m0 + 16 * mt + r;
+        col_ok[mt] = col < m;
+        xrow[mt] = x + (int64_t)(col_ok[mt] ? col : 0) * k;
+        qxrow[mt] = static_cast<const int8_t *>(xv) + (int64_t)(col_ok[mt] ? col : 0) * k;
+    }
 
     // the scales of the outputs this lane ends up holding (channels
     // n0 + 16 t + 4 g + i), loaded now so that they arrive during the main
@@ -111,14 +121,16 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
     for (int t = 0; t < RT; ++t)
         zbias[t] = zero_point_bias(ZP && row_ok[t] ? (int)zeros[n0 + 16 * t + r] : 0);
 
-    acc_t acc[RT];
+    acc_t acc[RT][MT];
 #pragma unroll
     for (int t = 0; t < RT; ++t)
-        acc[t] = (acc_t){};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            acc[t][mt] = (acc_t){};
 
     for (int s = s_begin; s < s_end; s += kSkinnyUnroll) {
         u32x4_t wv[kSkinnyUnroll][RT];
-        u32x4_t xa[kSkinnyUnroll], xb[kSkinnyUnroll];
+        u32x4_t xa[kSkinnyUnroll][MT], xb[kSkinnyUnroll][MT];
         {
             // Weight codes, loaded contiguously: instruction i of tile t
             // covers rows 4 i .. 4 i + 3, 256 bytes each (lane l: row
@@ -158,14 +170,17 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
         for (int u = 0; u < kSkinnyUnroll; ++u) {
             const int kk = (s + u) * 64 + g * 16;
             const bool ok = (s + u) < s_end && kk < k;
-            xa[u] = (u32x4_t){0u, 0u, 0u, 0u};
-            xb[u] = (u32x4_t){0u, 0u, 0u, 0u};
-            if (ok && col_ok) {
-                if constexpr (A8) {
-                    xa[u] = *reinterpret_cast<const u32x4_t *>(qxrow + kk);
-                } else {
-                    xa[u] = *reinterpret_cast<const u32x4_t *>(xrow + kk);
-                    xb[u] = *reinterpret_cast<const u32x4_t *>(xrow + kk + 8);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                xa[u][mt] = (u32x4_t){0u, 0u, 0u, 0u};
+                xb[u][mt] = (u32x4_t){0u, 0u, 0u, 0u};
+                if (ok && col_ok[mt]) {
+                    if constexpr (A8) {
+                        xa[u][mt] = *reinterpret_cast<const u32x4_t *>(qxrow[mt] + kk);
+                    } else {
+                        xa[u][mt] = *reinterpret_cast<const u32x4_t *>(xrow[mt] + kk);
+                        xb[u][mt] = *reinterpret_cast<const u32x4_t *>(xrow[mt] + kk + 8);
+                    }
                 }
             }
         }
@@ -174,29 +189,37 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
             if constexpr (A8) {
 #pragma unroll
                 for (int t = 0; t < RT; ++t)
-                    acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(int4v, wv[u][t]),
-                                                                   __builtin_bit_cast(int4v, xa[u]), acc[t], 0, 0, 0);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        acc[t][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                            __builtin_bit_cast(int4v, wv[u][t]), __builtin_bit_cast(int4v, xa[u][mt]), acc[t][mt],
+                            0, 0, 0);
             } else {
-                const half8_t b0 = __builtin_bit_cast(half8_t, xa[u]);
-                const half8_t b1 = __builtin_bit_cast(half8_t, xb[u]);
 #pragma unroll
                 for (int t = 0; t < RT; ++t) {
                     const half8_t a0 = i8x8_to_half8(wv[u][t].x, wv[u][t].y, zbias[t]);
                     const half8_t a1 = i8x8_to_half8(wv[u][t].z, wv[u][t].w, zbias[t]);
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, acc[t], 0, 0, 0);
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, acc[t], 0, 0, 0);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const half8_t b0 = __builtin_bit_cast(half8_t, xa[u][mt]);
+                        const half8_t b1 = __builtin_bit_cast(half8_t, xb[u][mt]);
+                        acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, acc[t][mt], 0, 0, 0);
+                        acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, acc[t][mt], 0, 0, 0);
+                    }
                 }
             }
         }
     }
 
     if (KSPLIT > 1) {
-        acc_t *partial = reinterpret_cast<acc_t *>(smem); // [KSPLIT-1][RT][kWave]
+        acc_t *partial = reinterpret_cast<acc_t *>(smem); // [KSPLIT-1][RT][MT][kWave]
         __syncthreads(); // every wave is done with its staging slice
         if (wave > 0) {
 #pragma unroll
             for (int t = 0; t < RT; ++t)
-                partial[((wave - 1) * RT + t) * kWave + lane] = acc[t];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    partial[(((wave - 1) * RT + t) * MT + mt) * kWave + lane] = acc[t][mt];
         }
         __syncthreads();
         if (wave != 0)
@@ -205,41 +228,46 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
         for (int w = 0; w < KSPLIT - 1; ++w)
 #pragma unroll
             for (int t = 0; t < RT; ++t)
-                acc[t] += partial[(w * RT + t) * kWave + lane];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[t][mt] += partial[((w * RT + t) * MT + mt) * kWave + lane];
     }
-    const float xscale = A8 && col_ok ? f16_bits_to_f32(sx[col]) : 0.0f;
     // lane holds channels n0 + 16 t + 4 g + i (i = 0..3) of activation row
-    // m0 + r: scale, round, and transpose through LDS so that the stores
-    // are whole 16-byte pieces of Y rows
+    // m0 + 16 mt + r: scale, round, and transpose through LDS so that the
+    // stores are whole 16-byte pieces of Y rows
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
+    for (int mt = 0; mt < MT; ++mt) {
+        const float xscale = A8 && col_ok[mt] ? f16_bits_to_f32(sx[m0 + 16 * mt + r]) : 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float out;
-            if constexpr (A8) // exact int32 sum, then S[n] * Sx[m] (exact in fp32)
-                out = (float)acc[t][i] * (f16_bits_to_f32(sc[t][i]) * xscale);
-            else
-                out = acc[t][i] * f16_bits_to_f32(sc[t][i]);
-            // exact outliers of channel n0 + 16 t + 4 g + i, with X read
-            // from global memory (a few activation rows: L2-resident)
-            const int yn = n0 + 16 * t + 4 * g + i;
-            if (!A8 && ol.idx != nullptr && yn < n && col_ok) {
-                for (int e = 0; e < ol.cap; ++e) {
-                    const int kk = ol.idx[(int64_t)yn * ol.cap + e];
-                    if (kk < 0 || kk >= k)
-                        break; // used slots come first
-                    out += f16_bits_to_f32(xrow[kk]) * ol.val[(int64_t)yn * ol.cap + e];
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float out;
+                if constexpr (A8) // exact int32 sum, then S[n] * Sx[m] (exact in fp32)
+                    out = (float)acc[t][mt][i] * (f16_bits_to_f32(sc[t][i]) * xscale);
+                else
+                    out = acc[t][mt][i] * f16_bits_to_f32(sc[t][i]);
+                // exact outliers of channel n0 + 16 t + 4 g + i, with X read
+                // from global memory (a few activation rows: L2-resident)
+                const int yn = n0 + 16 * t + 4 * g + i;
+                if (!A8 && ol.idx != nullptr && yn < n && col_ok[mt]) {
+                    for (int e = 0; e < ol.cap; ++e) {
+                        const int kk = ol.idx[(int64_t)yn * ol.cap + e];
+                        if (kk < 0 || kk >= k)
+                            break; // used slots come first
+                        out += f16_bits_to_f32(xrow[mt][kk]) * ol.val[(int64_t)yn * ol.cap + e];
+                    }
                 }
+                ytile[16 * mt + r][16 * t + 4 * g + i] = f32_to_f16_bits(out);
             }
-            ytile[r][16 * t + 4 * g + i] = f32_to_f16_bits(out);
-        }
+    }
     // the tile is written and read back by the same wave: LDS keeps a
     // wave's accesses in order; the barrier only stops the compiler from
     // moving the reads above the writes
     __builtin_amdgcn_wave_barrier();
     constexpr int kPieces = 16 * RT / 8;  // 16-byte pieces per tile row
     const bool vec_ok = (n % 8) == 0 && n0 + 16 * RT <= n;
-    for (int e = lane; e < 16 * kPieces; e += kWave) {
+    for (int e = lane; e < 16 * MT * kPieces; e += kWave) {
         const int row = e / kPieces;
         const int pc = e % kPieces;
         const int ym = m0 + row;
@@ -257,57 +285,85 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
     }
 }
 
-template <int RT, int KSPLIT, bool A8>
+template <int RT, int MT, int KSPLIT, bool A8>
 hipError_t launch_cfg(const void *x, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
                       const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k,
                       hipStream_t stream)
 {
-    const dim3 grid((unsigned)((n + 16 * RT - 1) / (16 * RT)), (unsigned)((m + 15) / 16));
+    const dim3 grid((unsigned)((n + 16 * RT - 1) / (16 * RT)), (unsigned)((m + 16 * MT - 1) / (16 * MT)));
     if constexpr (!A8) {
         if (zeros != nullptr) {
-            hipLaunchKernelGGL((skinny_gemm_kernel<RT, KSPLIT, false, true>), grid, dim3(KSPLIT * kWave), 0,
+            hipLaunchKernelGGL((skinny_gemm_kernel<RT, MT, KSPLIT, false, true>), grid, dim3(KSPLIT * kWave), 0,
                                stream, x, sx, q, scales, zeros, ol, y, (int)m, (int)n, (int)k);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((skinny_gemm_kernel<RT, KSPLIT, A8>), grid, dim3(KSPLIT * kWave), 0, stream,
+    hipLaunchKernelGGL((skinny_gemm_kernel<RT, MT, KSPLIT, A8>), grid, dim3(KSPLIT * kWave), 0, stream,
                        x, sx, q, scales, zeros, ol, y, (int)m, (int)n, (int)k);
     return hipGetLastError();
 }
 
-template <int RT, bool A8>
-hipError_t launch_rt(const void *x, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
+// Largest k split per kernel variant: a workgroup of 16 waves leaves each
+// lane 128 registers, which the int8 kernel and the two-tile fp16 kernel
+// exceed (they spilled); they stop at 8 waves.
+template <int MT, bool A8>
+constexpr int max_split()
+{
+    return (A8 || MT > 1) ? 8 : 16;
+}
+
+template <int RT, int MT, bool A8>
+hipError_t launch_mt(const void *x, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
                      const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k,
                      hipStream_t stream)
 {
     // split k until the grid holds about kSkinnyTargetWaves waves, keeping
     // at least one 64-wide step per wave
-    const int64_t tiles = ((n + 16 * RT - 1) / (16 * RT)) * ((m + 15) / 16);
+    const int64_t tiles = ((n + 16 * RT - 1) / (16 * RT)) * ((m + 16 * MT - 1) / (16 * MT));
     const int64_t steps = (k + 63) / 64;
-    // (the int8 variant stops at 8 waves: with 16 the 128-register limit of
-    // a 1024-thread workgroup made it spill)
-    constexpr int kMaxSplit = A8 ? 8 : 16;
+    constexpr int kMaxSplit = max_split<MT, A8>();
     int ksplit = 1;
     while (ksplit < kMaxSplit && tiles * ksplit < kSkinnyTargetWaves && steps >= 2 * ksplit)
         ksplit *= 2;
-    switch (ksplit) {
-    case 1:
-        return launch_cfg<RT, 1, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
-    case 2:
-        return launch_cfg<RT, 2, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
-    case 4:
-        return launch_cfg<RT, 4, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
-    case 8:
-        return launch_cfg<RT, 8, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
-    default:
-        if constexpr (!A8)
-            return launch_cfg<RT, 16, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
-        else
-            return hipErrorInvalidValue; // not reached: kMaxSplit
-    }
+    if (ksplit == 1)
+        return launch_cfg<RT, MT, 1, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
+    if (ksplit == 2)
+        return launch_cfg<RT, MT, 2, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
+    if (ksplit == 4)
+        return launch_cfg<RT, MT, 4, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
+    if constexpr (kMaxSplit >= 8)
+        if (ksplit == 8)
+            return launch_cfg<RT, MT, 8, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
+    if constexpr (kMaxSplit >= 16)
+        if (ksplit == 16)
+            return launch_cfg<RT, MT, 16, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
+    return hipErrorInvalidValue; // not reached: ksplit <= kMaxSplit
+}
+
+// Activation tiles per wave from m and k.  For 17..32 rows with k >= 2048,
+// two tiles per wave take one pass over the weights instead of two
+// (measured 10% faster at k = 4096, n = 4608 and 27392).  Otherwise one
+// tile per wave and one pass per 16 rows: the passes run side by side and
+// their repeated weight reads hit in cache, so more, shorter waves win
+// (four tiles per wave measured 7-10% slower than four passes at 48 and 64
+// rows; two tiles 2-5% slower at k = 1024, where the k split then has too
+// few steps to fill the chip).
+template <int RT, bool A8>
+hipError_t launch_rt(const void *x, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
+                     const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                     hipStream_t stream)
+{
+    if (skinny_rows_per_pass(m, k) == 32)
+        return launch_mt<RT, 2, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
+    return launch_mt<RT, 1, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
 }
 
 } // namespace
+
+int skinny_rows_per_pass(int64_t m, int64_t k)
+{
+    return (m > 16 && m <= 32 && k >= 2048) ? 32 : 16;
+}
 
 hipError_t launch_skinny_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
                               const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)

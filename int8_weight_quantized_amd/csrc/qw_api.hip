@@ -38,19 +38,42 @@ int device_cu_count()
 // few rows: the skinny MFMA kernel keeps the weight stream at full rate
 // while the VALU dot products would grow with m.  Prefill: the LDS-tiled
 // MFMA GEMM, whose weight tiles are reused across activation rows.
+//
+// The skinny kernel takes 16 (or 32) activation rows per pass over the
+// weights.  Passes beyond the first read the weights again, mostly from
+// cache, at about 0.16-0.2 us per MB; the MFMA kernel at these m costs
+// about the same for any m (a few hundred tiles, each a long k loop).  In
+// the crossover sweep over m at (k, n) = (4096, 27392), (4096, 4608) and
+// (1024, 4096), the skinny kernel is the faster one while the weight bytes
+// of its extra passes stay below about 100 MB: up to 32 rows at
+// (4096, 27392), 96 at (4096, 4608) and 256 at (1024, 4096).  The int8
+// kernels (W8A8) cross over at or beyond the same points (the skinny one
+// reads int8 activations, the MFMA one runs at twice the rate), so they
+// share the rule.
+constexpr int64_t kSkinnyExtraPassBytes = int64_t(96) << 20;
+
+bool skinny_preferred(int64_t m, int64_t n, int64_t k)
+{
+    if (m <= 16)
+        return true;
+    const int64_t rows = skinny_rows_per_pass(m, k);
+    const int64_t extra = (m + rows - 1) / rows - 1;
+    return extra * n * k <= kSkinnyExtraPassBytes;
+}
+
 int auto_path(int64_t m, int64_t n, int64_t k)
 {
     if (m <= 2 && gemv_supported(m, k))
         return QW_PATH_GEMV;
-    // The skinny kernel streams the weights once per 16 activation rows; it
-    // beats the tiled MFMA kernel up to 16 rows, and up to 64 rows when the
-    // weight is narrow enough (n <= 16384) that MFMA tiles leave most CUs
-    // idle (crossover sweep over m at (k, n) = (4096, 27392), (4096, 4608),
-    // (1024, 4096)).
-    // Rows longer than the MFMA kernel takes also go to the skinny kernel.
-    if (m <= 16 || (m <= 64 && n <= 16384) || k > kMfmaMaxK)
+    // rows longer than the MFMA kernel takes also go to the skinny kernel
+    if (k > kMfmaMaxK || skinny_preferred(m, n, k))
         return QW_PATH_SKINNY;
     return QW_PATH_MFMA;
+}
+
+int auto_path_w8a8(int64_t m, int64_t n, int64_t k)
+{
+    return skinny_preferred(m, n, k) ? QW_PATH_SKINNY : QW_PATH_MFMA;
 }
 
 } // namespace qw
@@ -436,7 +459,7 @@ QW_API qw_status qw_w8a8_gemm_path(const int8_t *qx, const uint16_t *sx, const i
         return QW_ERROR_INVALID_VALUE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (path == QW_PATH_AUTO)
-        path = qw::auto_path(m, n, k) == QW_PATH_MFMA ? QW_PATH_MFMA : QW_PATH_SKINNY;
+        path = qw::auto_path_w8a8(m, n, k);
     if (path == QW_PATH_SKINNY) {
         if (m > 16 * 65535) // grid.y holds one 16-row activation tile per block row
             return QW_ERROR_UNSUPPORTED;
@@ -450,6 +473,13 @@ QW_API qw_status qw_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t
                               void *stream)
 {
     return qw_w8a8_gemm_path(qx, sx, q, scales, y, m, n, k, QW_PATH_AUTO, stream);
+}
+
+QW_API int qw_w8a8_gemm_auto_path(int64_t m, int64_t n, int64_t k)
+{
+    if (m < 0 || n < 0 || k <= 0 || k % 16 != 0 || m > kMaxDim || n > kMaxDim || k > QW_W8A8_MAX_K)
+        return -1;
+    return qw::auto_path_w8a8(m, n, k);
 }
 
 QW_API int qw_w8a8_gemm_mfma_tile(int64_t m, int64_t n, int64_t k)

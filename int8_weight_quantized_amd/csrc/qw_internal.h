@@ -31,6 +31,10 @@ constexpr int kMfmaOutlierSlots = 4;
 // tile (at most 256 rows x k bytes) and a tile's byte range stay below 2^31.
 // Longer rows go to the skinny kernel, which indexes in 64 bits.
 constexpr int64_t kMfmaMaxK = QW_MFMA_MAX_K;
+
+// Activation rows the skinny kernel covers per pass over the weights (32
+// where it runs two 16-row activation tiles per wave, else 16).
+int skinny_rows_per_pass(int64_t m, int64_t k);
 static_assert(256 * kMfmaMaxK <= (int64_t(1) << 31) && 255 * kMfmaMaxK + 64 < (int64_t(1) << 31),
               "MFMA in-tile offsets");
 

@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     decl = _declared_functions()
     for name in ("qw_quantize_weights", "qw_quantize_weights_f16", "qw_w8a16_gemm", "qw_w8a16_gemm_path",
                  "qw_w8a16_gemm_auto_path", "qw_w8a16_gemm_mfma_tile", "qw_w8a8_gemm",
-                 "qw_w8a8_gemm_mfma_tile", "qw_quantize_weights_fixed_range", "qw_quantize_weights_asym",
+                 "qw_w8a8_gemm_mfma_tile", "qw_w8a8_gemm_auto_path", "qw_quantize_weights_fixed_range",
+                 "qw_quantize_weights_asym",
                  "qw_w8a16_gemm_asym", "qw_w8a16_gemm_asym_path", "qw_outlier_capacity",
                  "qw_quantize_weights_outliers", "qw_w8a16_gemm_outliers", "qw_w8a16_gemm_outliers_path",
                  "qw_w8a16_gemm_tune", "qw_w8a16_gemm_tuned_choice", "qw_w8a16_gemm_tune_reset",
@@ -263,6 +264,21 @@ def test_w8a8_rejects(args, status):
     assert qw.w8a8_gemm_raw(*args) == status
 
 
+def test_w8a8_auto_path_choice():
+    """The int8 kernels share the W8A16 skinny/MFMA crossover (there is no
+    W8A8 GEMV)."""
+    assert qw.w8a8_auto_path(1, 27392, 4096) == "skinny"
+    assert qw.w8a8_auto_path(32, 27392, 4096) == "skinny"
+    assert qw.w8a8_auto_path(33, 27392, 4096) == "mfma"
+    assert qw.w8a8_auto_path(96, 4608, 4096) == "skinny"
+    assert qw.w8a8_auto_path(512, 27392, 4096) == "mfma"
+    for m, n, k in ((8, 4608, 4096), (48, 4608, 4096), (200, 4096, 1024), (4096, 4096, 1024)):
+        assert qw.w8a8_auto_path(m, n, k) == qw.auto_path(m, n, k)
+    assert qw.library().qw_w8a8_gemm_auto_path(8, 64, qw.W8A8_MAX_K + 16) == -1
+    with pytest.raises(ValueError):
+        qw.w8a8_auto_path(1, 4, 24)
+
+
 def test_w8a8_empty_is_noop():
     assert qw.w8a8_gemm_raw(0, 0, 0, 0, 0, 0, 4, 16) == qw.QW_SUCCESS
     assert qw.w8a8_gemm_raw(0, 0, 0, 0, 0, 3, 0, 16) == qw.QW_SUCCESS
@@ -298,11 +314,18 @@ def test_auto_path_choice():
     assert qw.auto_path(8, 4608, 4096) == "skinny"
     assert qw.auto_path(512, 27392, 4096) == "mfma"
     assert qw.auto_path(4096, 4096, 1024) == "mfma"
-    # crossover: skinny to 16 rows, to 64 rows for narrow weights
+    # crossover: the skinny kernel while the weight bytes of its passes
+    # after the first (16 rows each, 32 for 17..32 rows at k >= 2048) stay
+    # within 96 MiB
     assert qw.auto_path(16, 27392, 4096) == "skinny"
-    assert qw.auto_path(24, 27392, 4096) == "mfma"
-    assert qw.auto_path(64, 4608, 4096) == "skinny"
-    assert qw.auto_path(65, 4608, 4096) == "mfma"
+    assert qw.auto_path(24, 27392, 4096) == "skinny"   # one 32-row pass
+    assert qw.auto_path(32, 27392, 4096) == "skinny"
+    assert qw.auto_path(33, 27392, 4096) == "mfma"     # two more passes over 112 MB
+    assert qw.auto_path(24, 27392, 1024) == "skinny"   # 16-row passes at short k: one more over 28 MB
+    assert qw.auto_path(96, 4608, 4096) == "skinny"    # five more passes over 18.9 MB
+    assert qw.auto_path(97, 4608, 4096) == "mfma"
+    assert qw.auto_path(256, 4096, 1024) == "skinny"
+    assert qw.auto_path(512, 4096, 1024) == "mfma"
     # k too long for the GEMV's LDS staging: skinny even at m = 1
     assert qw.auto_path(1, 64, 65536) == "skinny"
     with pytest.raises(ValueError):

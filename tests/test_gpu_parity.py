@@ -135,6 +135,21 @@ def test_skinny_small_shapes(m, n, k):
     assert_gemm_close(y, oracle.gemm(x, q, s), "skinny %dx%dx%d" % (m, n, k))
 
 
+# The skinny kernel with two 16-row activation tiles per wave (17..32 rows,
+# k >= 2048) and with one (more rows, or shorter k), at weight shapes that
+# select several of its k splits.
+SKINNY_TILE_SHAPES = [(32, 4608, 4096), (24, 27392, 2048), (17, 1000, 2064), (31, 130, 4096), (24, 600, 1024),
+                      (64, 4608, 4096), (48, 2048, 64), (40, 4096, 8192), (64, 65536, 64), (100, 1200, 2064)]
+
+
+@pytest.mark.parametrize("m,n,k", SKINNY_TILE_SHAPES)
+def test_skinny_activation_tiles(m, n, k):
+    x, q, s = _small_case(m, n, k, seed=m * 7 + n)
+    say("gemm skinny tiles m=%d n=%d k=%d" % (m, n, k))
+    y = gpu_gemm(x, q, s, path=SKINNY)
+    assert_gemm_close(y, oracle.gemm(x, q, s), "skinny tiles %dx%dx%d" % (m, n, k))
+
+
 # Long rows: k beyond what the GEMV stages in LDS (it then falls back to the
 # skinny kernel), and long reductions on every path.
 LONG_K_SHAPES = [(1, 64, 65536), (2, 40, 32784), (9, 72, 16400), (70, 72, 16400)]
