@@ -373,26 +373,35 @@ def sweep_paths(ms=(1, 2, 3, 4, 8, 16, 24, 32, 48, 64, 96, 128, 256, 512),
                   for _ in range(sets)]
             sx = [torch.rand((m,), device="cuda:0", generator=g).half() * 1e-2 for _ in range(sets)]
             y = [torch.empty((m, n), dtype=torch.float16, device="cuda:0") for _ in range(sets)]
-            for name, path in (("gemv", 1), ("skinny", 3), ("mfma", 2), ("w8a8_skinny", 3), ("w8a8_mfma", 2)):
-                def launch(i):
-                    if name.startswith("w8a8"):
-                        return qw.w8a8_gemm_raw(qx[i].data_ptr(), sx[i].data_ptr(), q[i].data_ptr(),
-                                                s[i].data_ptr(), y[i].data_ptr(), m, n, k, stream, path)
-                    return qw.w8a16_gemm_raw(x[i].data_ptr(), q[i].data_ptr(), s[i].data_ptr(),
-                                             y[i].data_ptr(), m, n, k, stream, path)
-                if launch(0) != 0:
-                    continue
-                for it in range(5):
-                    launch(it % sets)
-                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                      for _ in range(30)]
-                torch.cuda.synchronize()
-                for it in range(30):
-                    ev[it][0].record()
-                    launch(it % sets)
-                    ev[it][1].record()
-                torch.cuda.synchronize()
-                ms_ = sorted(a.elapsed_time(b) for a, b in ev)
+            kernels = (("gemv", 1), ("skinny", 3), ("mfma", 2), ("w8a8_skinny", 3), ("w8a8_mfma", 2))
+
+            def launcher(name, path):
+                if name.startswith("w8a8"):
+                    return lambda i: qw.w8a8_gemm_raw(qx[i].data_ptr(), sx[i].data_ptr(), q[i].data_ptr(),
+                                                      s[i].data_ptr(), y[i].data_ptr(), m, n, k, stream, path)
+                return lambda i: qw.w8a16_gemm_raw(x[i].data_ptr(), q[i].data_ptr(), s[i].data_ptr(),
+                                                   y[i].data_ptr(), m, n, k, stream, path)
+            # kernels this shape supports (a forced kernel outside its limits is refused)
+            runs = [(name, launcher(name, path)) for name, path in kernels]
+            runs = [(name, f) for name, f in runs if f(0) == 0]
+            for it in range(5):
+                for j, (_, f) in enumerate(runs):
+                    f((it * len(runs) + j) % sets)
+            # round-robin: one launch of each kernel per round, so that clock
+            # and cache state after the allocations hit every kernel alike
+            ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                         for _ in range(30)] for name, _ in runs}
+            torch.cuda.synchronize()
+            # (every launch takes the next operand set, so none finds its
+            # operands in cache)
+            for it in range(30):
+                for j, (name, f) in enumerate(runs):
+                    ev[name][it][0].record()
+                    f((it * len(runs) + j) % sets)
+                    ev[name][it][1].record()
+            torch.cuda.synchronize()
+            for name, _ in runs:
+                ms_ = sorted(a.elapsed_time(b) for a, b in ev[name])
                 avg = sum(ms_) / len(ms_)
                 print(json.dumps({"sweep": "gemm_paths", "k": k, "n": n, "m": m, "kernel": name,
                                   "auto": qw.auto_path(m, n, k), "auto_w8a8": qw.w8a8_auto_path(m, n, k),
@@ -427,7 +436,8 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the W8A16 path here has no multi-GPU "
-              "execution (see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+              "execution (each GPU would hold its own slice of the weight rows); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -284,10 +284,10 @@ QW_API qw_status qw_quantize_weights_asym(const float *w, int64_t n, int64_t k, 
  *
  * The kernel is chosen from m, n and k: a bandwidth-bound VALU GEMV for
  * decode (m <= 2), a skinny MFMA kernel on register-dequantized weights for
- * a few activation rows (m <= 16, and beyond while the weight bytes it
- * reads again in its passes after the first, one per 16 or 32 rows, stay
- * within 96 MiB) and for k > QW_MFMA_MAX_K, and the LDS-tiled MFMA GEMM
- * (tile shape picked from the grid it fills) otherwise.
+ * a few activation rows (m <= 16, and beyond while it needs at most 8
+ * passes over the weights, one per 16 or 32 rows, and the passes after the
+ * first read at most 128 MiB) and for k > QW_MFMA_MAX_K, and the LDS-tiled
+ * MFMA GEMM (tile shape picked from the grid it fills) otherwise.
  *
  * Errors: QW_ERROR_INVALID_VALUE (null pointer with m, n > 0, negative
  * size, k <= 0, y overlapping x, q or scales), QW_ERROR_UNSUPPORTED

@@ -41,24 +41,25 @@ int device_cu_count()
 //
 // The skinny kernel takes 16 (or 32) activation rows per pass over the
 // weights.  Passes beyond the first read the weights again, mostly from
-// cache, at about 0.16-0.2 us per MB; the MFMA kernel at these m costs
-// about the same for any m (a few hundred tiles, each a long k loop).  In
-// the crossover sweep over m at (k, n) = (4096, 27392), (4096, 4608) and
-// (1024, 4096), the skinny kernel is the faster one while the weight bytes
-// of its extra passes stay below about 100 MB: up to 32 rows at
-// (4096, 27392), 96 at (4096, 4608) and 256 at (1024, 4096).  The int8
-// kernels (W8A8) cross over at or beyond the same points (the skinny one
-// reads int8 activations, the MFMA one runs at twice the rate), so they
-// share the rule.
-constexpr int64_t kSkinnyExtraPassBytes = int64_t(96) << 20;
+// cache: the first few are nearly free on a small weight (they fill CUs
+// the first leaves idle), later ones cost about 0.16-0.2 us per MB plus a
+// fixed share; the MFMA kernel at these m costs about the same for any m
+// (a few hundred tiles, each a long k loop).  In the crossover sweep over
+// m at (k, n) = (4096, 27392), (4096, 4608) and (1024, 4096), timed
+// round-robin, the skinny kernel is the faster one while it needs at most
+// 8 passes and its extra passes read at most 128 MiB: up to 32 rows at
+// (4096, 27392) and 128 at the two narrower weights.  The int8 kernels
+// (W8A8) cross over at the same points, so they share the rule.
+constexpr int64_t kSkinnyMaxPasses = 8;
+constexpr int64_t kSkinnyExtraPassBytes = int64_t(128) << 20;
 
 bool skinny_preferred(int64_t m, int64_t n, int64_t k)
 {
     if (m <= 16)
         return true;
     const int64_t rows = skinny_rows_per_pass(m, k);
-    const int64_t extra = (m + rows - 1) / rows - 1;
-    return extra * n * k <= kSkinnyExtraPassBytes;
+    const int64_t passes = (m + rows - 1) / rows;
+    return passes <= kSkinnyMaxPasses && (passes - 1) * n * k <= kSkinnyExtraPassBytes;
 }
 
 int auto_path(int64_t m, int64_t n, int64_t k)

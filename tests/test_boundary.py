@@ -314,18 +314,18 @@ def test_auto_path_choice():
     assert qw.auto_path(8, 4608, 4096) == "skinny"
     assert qw.auto_path(512, 27392, 4096) == "mfma"
     assert qw.auto_path(4096, 4096, 1024) == "mfma"
-    # crossover: the skinny kernel while the weight bytes of its passes
-    # after the first (16 rows each, 32 for 17..32 rows at k >= 2048) stay
-    # within 96 MiB
+    # crossover: the skinny kernel while it needs at most 8 passes (16 rows
+    # each, 32 for 17..32 rows at k >= 2048) and the passes after the first
+    # read at most 128 MiB of weights
     assert qw.auto_path(16, 27392, 4096) == "skinny"
     assert qw.auto_path(24, 27392, 4096) == "skinny"   # one 32-row pass
     assert qw.auto_path(32, 27392, 4096) == "skinny"
     assert qw.auto_path(33, 27392, 4096) == "mfma"     # two more passes over 112 MB
     assert qw.auto_path(24, 27392, 1024) == "skinny"   # 16-row passes at short k: one more over 28 MB
-    assert qw.auto_path(96, 4608, 4096) == "skinny"    # five more passes over 18.9 MB
-    assert qw.auto_path(97, 4608, 4096) == "mfma"
-    assert qw.auto_path(256, 4096, 1024) == "skinny"
-    assert qw.auto_path(512, 4096, 1024) == "mfma"
+    assert qw.auto_path(128, 4608, 4096) == "skinny"   # seven more passes over 18.9 MB (126 MiB)
+    assert qw.auto_path(129, 4608, 4096) == "mfma"     # nine passes
+    assert qw.auto_path(128, 4096, 1024) == "skinny"
+    assert qw.auto_path(256, 4096, 1024) == "mfma"     # sixteen passes
     # k too long for the GEMV's LDS staging: skinny even at m = 1
     assert qw.auto_path(1, 64, 65536) == "skinny"
     with pytest.raises(ValueError):
