@@ -303,7 +303,7 @@ typedef enum qw_gemm_path {
     QW_PATH_AUTO = 0,   /* what qw_w8a16_gemm does */
     QW_PATH_GEMV = 1,   /* VALU dot products, weights streamed once (m <= 8) */
     QW_PATH_MFMA = 2,   /* MFMA tiled GEMM, int8 tiles dequantized into LDS */
-    QW_PATH_SKINNY = 3  /* MFMA on weights dequantized in registers, 16 activation rows per pass */
+    QW_PATH_SKINNY = 3  /* MFMA on weights dequantized in registers, 16 (or 32) activation rows per pass */
 } qw_gemm_path;
 
 /*

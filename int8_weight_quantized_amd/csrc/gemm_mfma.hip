@@ -57,19 +57,22 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks)
 }
 
 // ---------------------------------------------------------------------------
-// Big-tile variant for prefill-sized m: a 256 x BM output tile per
-// workgroup of 4 waves (one per SIMD), each wave 64 output channels x all BM
-// activation rows on v_mfma_f32_32x32x16_f16 with fp32 accumulators in
-// registers.  (Splitting the channels rather than the rows halves the
+// Big-tile variant for prefill-sized m: a BN x BM output tile per
+// workgroup of 4 waves (one per SIMD), each wave BN / 4 output channels x
+// all BM activation rows on v_mfma_f32_32x32x16_f16 with fp32 accumulators
+// in registers.  (Splitting the channels rather than the rows halves the
 // per-wave int8 -> fp16 casts, each cast weight operand feeding BM / 32
-// MFMAs; the price is that every wave reads the whole activation tile.)  Operands are copied from global memory straight into LDS by
-// the gfx950 LDS-DMA loads (global_load_lds_dwordx4: each lane's 16 bytes
+// MFMAs; the price is that every wave reads the whole activation tile.)
+// Operands are copied from global memory straight into LDS by the gfx950
+// LDS-DMA loads (buffer_load_dwordx4 ... lds in full k steps,
+// global_load_lds_dwordx4 in the ragged last ones: each lane's 16 bytes
 // land at LDS base + 16 * lane) into two LDS stages:
 //
 //   step t:
 //     wait for my copies of tile t; barrier (everyone's copies landed,
 //       everyone done reading tile t-1)
-//     start copying tile t + 1 into tile t-1's stage
+//     start copying tile t + 1 into tile t-1's stage (on the 256-channel
+//       fp16 tiles, spread over the step's four MFMA groups)
 //     LDS -> registers: operands of tile t; dequantize; MFMAs of tile t
 //
 // one barrier per k step.  (Two workgroups of 67 KiB share a CU, so the
