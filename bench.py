@@ -28,6 +28,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -77,10 +78,16 @@ def act_quant_bytes(m, k):
 
 
 def kernel_source_sha(kernel):
+    """Hash of a kernel's sources with comments and whitespace runs removed,
+    so that documentation edits do not void the counters measured on the
+    code."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
