@@ -90,7 +90,8 @@ def test_quantize_outliers_wider_than_needed():
 
 
 SHAPES = [(1, 1000, 272, 99.9), (2, 300, 2064, 99.9), (8, 517, 2064, 99.99), (17, 300, 528, 99.0),
-          (65, 130, 96, 95.0), (130, 260, 4112, 99.9), (300, 513, 1040, 99.99), (257, 129, 144, 97.0)]
+          (65, 130, 96, 95.0), (130, 260, 4112, 99.9), (300, 513, 1040, 99.99), (257, 129, 144, 97.0),
+          (20, 260, 2064, 99.9)]
 
 
 @pytest.mark.parametrize("m,n,k,pct", SHAPES)
