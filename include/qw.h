@@ -388,7 +388,7 @@ QW_API int qw_w8a16_gemm_mfma_tile(int64_t m, int64_t n, int64_t k);
  * qw_w8a16_gemm_tuned_choice -- the record for the bucket of (m, n, k) on
  * the current device: path * 1000000 + tile (tile = BN * 1000 + BM for
  * QW_PATH_MFMA, 0 otherwise), or -1 if none (or bad shape).
- * qw_w8a16_gemm_tune_reset -- forget every record.
+ * qw_w8a16_gemm_tune_reset -- forget every record (W8A16 and W8A8).
  */
 QW_API qw_status qw_w8a16_gemm_tune(const uint16_t *x, const int8_t *q, const uint16_t *scales,
                                     uint16_t *y, int64_t m, int64_t n, int64_t k, void *stream);
@@ -450,9 +450,29 @@ QW_API qw_status qw_w8a8_gemm_path(const int8_t *qx, const uint16_t *sx, const i
 
 /*
  * qw_w8a8_gemm_auto_path -- the kernel qw_w8a8_gemm runs for this shape:
- * QW_PATH_SKINNY or QW_PATH_MFMA; -1 for a shape qw_w8a8_gemm rejects.
+ * QW_PATH_SKINNY or QW_PATH_MFMA (a W8A8 tuning record for the shape's
+ * bucket, else the shape rule of qw_w8a16_gemm without the GEMV); -1 for a
+ * shape qw_w8a8_gemm rejects.
  */
 QW_API int qw_w8a8_gemm_auto_path(int64_t m, int64_t n, int64_t k);
+
+/*
+ * qw_w8a8_gemm_tune -- per-shape autotuning of the W8A8 kernel choice, as
+ * qw_w8a16_gemm_tune (same source passages, timing and bucket) over the
+ * int8 kernels: the skinny kernel and the MFMA kernel with each of its
+ * three tiles (256128, 256064, 128064).  The W8A8 records are kept apart
+ * from the W8A16 ones; qw_w8a8_gemm, qw_w8a8_gemm_auto_path and
+ * qw_w8a8_gemm_mfma_tile use them.  Arguments, layout and errors as
+ * qw_w8a8_gemm; y holds the winner's result; the call synchronizes with
+ * `stream`.
+ *
+ * qw_w8a8_gemm_tuned_choice -- the W8A8 record for the bucket of (m, n, k)
+ * on the current device (encoding as qw_w8a16_gemm_tuned_choice), or -1.
+ */
+QW_API qw_status qw_w8a8_gemm_tune(const int8_t *qx, const uint16_t *sx, const int8_t *q,
+                                   const uint16_t *scales, uint16_t *y, int64_t m, int64_t n,
+                                   int64_t k, void *stream);
+QW_API int qw_w8a8_gemm_tuned_choice(int64_t m, int64_t n, int64_t k);
 
 /*
  * qw_w8a8_gemm_mfma_tile -- the output tile qw_w8a8_gemm uses for this

@@ -101,6 +101,10 @@ def _load():
     lib.qw_w8a8_gemm_mfma_tile.argtypes = [i64, i64, i64]
     lib.qw_w8a8_gemm_auto_path.argtypes = [i64, i64, i64]
     lib.qw_w8a8_gemm_auto_path.restype = ctypes.c_int
+    lib.qw_w8a8_gemm_tune.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.qw_w8a8_gemm_tune.restype = ctypes.c_int
+    lib.qw_w8a8_gemm_tuned_choice.argtypes = [i64, i64, i64]
+    lib.qw_w8a8_gemm_tuned_choice.restype = ctypes.c_int
     lib.qw_w8a8_gemm_mfma_tile.restype = ctypes.c_int
     lib.qw_w8a16_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     lib.qw_w8a16_gemm.restype = ctypes.c_int
@@ -192,10 +196,7 @@ def w8a16_gemm_tune_raw(x_ptr: int, q_ptr: int, s_ptr: int, y_ptr: int, m: int, 
     return int(library().qw_w8a16_gemm_tune(x_ptr, q_ptr, s_ptr, y_ptr, m, n, k, stream))
 
 
-def tuned_choice(m: int, n: int, k: int):
-    """The tuning record for the bucket of (m, n, k) on the current device:
-    (path name, (BN, BM) or None), or None when the shape has none."""
-    c = int(library().qw_w8a16_gemm_tuned_choice(m, n, k))
+def _decode_choice(c: int):
     if c < 0:
         return None
     path, tile = divmod(c, 1000000)
@@ -203,8 +204,25 @@ def tuned_choice(m: int, n: int, k: int):
     return name, ((tile // 1000, tile % 1000) if tile else None)
 
 
+def tuned_choice(m: int, n: int, k: int):
+    """The W8A16 tuning record for the bucket of (m, n, k) on the current
+    device: (path name, (BN, BM) or None), or None when the shape has none."""
+    return _decode_choice(int(library().qw_w8a16_gemm_tuned_choice(m, n, k)))
+
+
+def w8a8_tuned_choice(m: int, n: int, k: int):
+    """The W8A8 tuning record for the bucket of (m, n, k), as tuned_choice."""
+    return _decode_choice(int(library().qw_w8a8_gemm_tuned_choice(m, n, k)))
+
+
 def tune_reset() -> None:
+    """Forget every tuning record (W8A16 and W8A8)."""
     library().qw_w8a16_gemm_tune_reset()
+
+
+def w8a8_gemm_tune_raw(qx_ptr: int, sx_ptr: int, q_ptr: int, s_ptr: int, y_ptr: int, m: int, n: int, k: int,
+                       stream: int = 0) -> int:
+    return int(library().qw_w8a8_gemm_tune(qx_ptr, sx_ptr, q_ptr, s_ptr, y_ptr, m, n, k, stream))
 
 
 def w8a16_gemm_tune(x, q, scales, out=None):

@@ -783,6 +783,16 @@ hipError_t launch_mfma_gemm_tile(int tile, const uint16_t *x, const int8_t *q, c
     return launch_tiles<false>(x, nullptr, q, scales, zeros, ol, y, m, n, k, stream, tile);
 }
 
+hipError_t launch_w8a8_gemm_tile(int tile, const int8_t *qx, const uint16_t *sx, const int8_t *q,
+                                 const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                                 hipStream_t stream)
+{
+    if (tile != 256128 && tile != 256064 && tile != 128064)
+        return hipErrorInvalidValue;
+    return launch_tiles<true>(qx, sx, q, scales, nullptr, OutlierList{nullptr, nullptr, 0}, y, m, n, k, stream,
+                              tile);
+}
+
 hipError_t launch_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t *q,
                             const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
                             hipStream_t stream)

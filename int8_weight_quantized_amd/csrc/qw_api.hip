@@ -438,16 +438,21 @@ QW_API int qw_w8a16_gemm_mfma_tile(int64_t m, int64_t n, int64_t k)
     return qw::mfma_tile_choice(m, n);
 }
 
-QW_API qw_status qw_w8a8_gemm_path(const int8_t *qx, const uint16_t *sx, const int8_t *q,
-                                   const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
-                                   int path, void *stream)
+} // extern "C"
+
+namespace {
+
+// Argument checks shared by the W8A8 entry points; noop: nothing to do.
+qw_status check_w8a8_args(const int8_t *qx, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
+                          const uint16_t *y, int64_t m, int64_t n, int64_t k, bool &noop)
 {
-    if (path != QW_PATH_AUTO && path != QW_PATH_MFMA && path != QW_PATH_SKINNY)
-        return QW_ERROR_INVALID_VALUE;
+    noop = false;
     if (m < 0 || n < 0 || k <= 0)
         return QW_ERROR_INVALID_VALUE;
-    if (m == 0 || n == 0)
+    if (m == 0 || n == 0) {
+        noop = true;
         return QW_SUCCESS;
+    }
     if (!qx || !sx || !q || !scales || !y)
         return QW_ERROR_INVALID_VALUE;
     if (k % 16 != 0 || m > kMaxDim || n > kMaxDim || k > QW_W8A8_MAX_K)
@@ -458,9 +463,31 @@ QW_API qw_status qw_w8a8_gemm_path(const int8_t *qx, const uint16_t *sx, const i
     if (overlaps(y, ybytes, qx, (uint64_t)m * (uint64_t)k) || overlaps(y, ybytes, sx, (uint64_t)m * 2u) ||
         overlaps(y, ybytes, q, (uint64_t)n * (uint64_t)k) || overlaps(y, ybytes, scales, (uint64_t)n * 2u))
         return QW_ERROR_INVALID_VALUE;
+    return QW_SUCCESS;
+}
+
+} // namespace
+
+extern "C" {
+
+QW_API qw_status qw_w8a8_gemm_path(const int8_t *qx, const uint16_t *sx, const int8_t *q,
+                                   const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                                   int path, void *stream)
+{
+    if (path != QW_PATH_AUTO && path != QW_PATH_MFMA && path != QW_PATH_SKINNY)
+        return QW_ERROR_INVALID_VALUE;
+    bool noop = false;
+    const qw_status st = check_w8a8_args(qx, sx, q, scales, y, m, n, k, noop);
+    if (st != QW_SUCCESS || noop)
+        return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (path == QW_PATH_AUTO)
+    if (path == QW_PATH_AUTO) {
+        // a tuning record for this shape bucket wins over the shape rule
+        const int tuned = qw::tuned_choice(m, n, k, true);
+        if (tuned >= 0 && (tuned / qw::kChoicePath != QW_PATH_SKINNY || m <= 16 * 65535))
+            return launch_status(qw::launch_choice_w8a8(tuned, qx, sx, q, scales, y, m, n, k, s));
         path = qw::auto_path_w8a8(m, n, k);
+    }
     if (path == QW_PATH_SKINNY) {
         if (m > 16 * 65535) // grid.y holds one 16-row activation tile per block row
             return QW_ERROR_UNSUPPORTED;
@@ -480,6 +507,9 @@ QW_API int qw_w8a8_gemm_auto_path(int64_t m, int64_t n, int64_t k)
 {
     if (m < 0 || n < 0 || k <= 0 || k % 16 != 0 || m > kMaxDim || n > kMaxDim || k > QW_W8A8_MAX_K)
         return -1;
+    const int tuned = qw::tuned_choice(m, n, k, true);
+    if (tuned >= 0)
+        return tuned / qw::kChoicePath;
     return qw::auto_path_w8a8(m, n, k);
 }
 
@@ -490,7 +520,32 @@ QW_API int qw_w8a8_gemm_mfma_tile(int64_t m, int64_t n, int64_t k)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return -1;
+    const int tuned = qw::tuned_choice(m, n, k, true);
+    if (tuned >= 0 && tuned / qw::kChoicePath == QW_PATH_MFMA)
+        return tuned % qw::kChoicePath;
     return qw::w8a8_tile_choice(m, n);
+}
+
+QW_API qw_status qw_w8a8_gemm_tune(const int8_t *qx, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
+                                   uint16_t *y, int64_t m, int64_t n, int64_t k, void *stream)
+{
+    bool noop = false;
+    const qw_status st = check_w8a8_args(qx, sx, q, scales, y, m, n, k, noop);
+    if (st != QW_SUCCESS || noop)
+        return st;
+    int best = -1;
+    const hipError_t e = qw::tune_w8a8(qx, sx, q, scales, y, m, n, k, static_cast<hipStream_t>(stream), best);
+    if (e != hipSuccess)
+        return QW_ERROR_LAUNCH;
+    qw::record_tuned_choice(m, n, k, best, true);
+    return QW_SUCCESS;
+}
+
+QW_API int qw_w8a8_gemm_tuned_choice(int64_t m, int64_t n, int64_t k)
+{
+    if (m <= 0 || n <= 0 || k <= 0 || k % 16 != 0)
+        return -1;
+    return qw::tuned_choice(m, n, k, true);
 }
 
 QW_API const char *qw_status_string(qw_status status)

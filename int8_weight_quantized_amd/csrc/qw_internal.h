@@ -97,8 +97,9 @@ int device_cu_count();
 // Per-shape tuning records (tune.hip).  A choice encodes the kernel and the
 // MFMA tile as path * kChoicePath + tile (tile 0 for GEMV and skinny).
 constexpr int kChoicePath = 1000000;
-int tuned_choice(int64_t m, int64_t n, int64_t k);               // -1: none
-void record_tuned_choice(int64_t m, int64_t n, int64_t k, int choice);
+// The W8A16 and W8A8 (a8) GEMMs keep separate records.
+int tuned_choice(int64_t m, int64_t n, int64_t k, bool a8 = false); // -1: none
+void record_tuned_choice(int64_t m, int64_t n, int64_t k, int choice, bool a8 = false);
 void reset_tuned_choices();
 hipError_t launch_choice(int choice, const uint16_t *x, const int8_t *q, const uint16_t *scales,
                          const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k,
@@ -107,6 +108,16 @@ hipError_t launch_choice(int choice, const uint16_t *x, const int8_t *q, const u
 // with it) and returns the fastest in `best`; y holds the winner's result.
 hipError_t tune_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales, uint16_t *y, int64_t m,
                      int64_t n, int64_t k, hipStream_t stream, int &best);
+// The same for the W8A8 GEMM (skinny kernel and the int8 MFMA tiles).
+hipError_t tune_w8a8(const int8_t *qx, const uint16_t *sx, const int8_t *q, const uint16_t *scales, uint16_t *y,
+                     int64_t m, int64_t n, int64_t k, hipStream_t stream, int &best);
+hipError_t launch_choice_w8a8(int choice, const int8_t *qx, const uint16_t *sx, const int8_t *q,
+                              const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                              hipStream_t stream);
+// The W8A8 MFMA GEMM with a given tile (256128, 256064 or 128064).
+hipError_t launch_w8a8_gemm_tile(int tile, const int8_t *qx, const uint16_t *sx, const int8_t *q,
+                                 const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                                 hipStream_t stream);
 // The MFMA GEMM with a given tile (BN * 1000 + BM).
 hipError_t launch_mfma_gemm_tile(int tile, const uint16_t *x, const int8_t *q, const uint16_t *scales,
                                  const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n,

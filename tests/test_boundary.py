@@ -35,6 +35,7 @@ def test_header_declares_the_entry_points():
                  "qw_w8a16_gemm_asym", "qw_w8a16_gemm_asym_path", "qw_outlier_capacity",
                  "qw_quantize_weights_outliers", "qw_w8a16_gemm_outliers", "qw_w8a16_gemm_outliers_path",
                  "qw_w8a16_gemm_tune", "qw_w8a16_gemm_tuned_choice", "qw_w8a16_gemm_tune_reset",
+                 "qw_w8a8_gemm_tune", "qw_w8a8_gemm_tuned_choice",
                  "qw_status_string", "qw_version"):
         assert name in decl
 
@@ -298,8 +299,18 @@ def test_gemm_tune_rejects(args, status):
 def test_tuned_choice_without_records():
     qw.tune_reset()
     assert qw.tuned_choice(8, 4608, 4096) is None
+    assert qw.w8a8_tuned_choice(8, 4608, 4096) is None
     assert qw.library().qw_w8a16_gemm_tuned_choice(0, 4, 16) == -1
     assert qw.library().qw_w8a16_gemm_tuned_choice(1, 4, 24) == -1
+    assert qw.library().qw_w8a8_gemm_tuned_choice(1, 4, 24) == -1
+
+
+def test_w8a8_tune_checks_arguments_first():
+    # rejected on the host before anything is enqueued; an empty shape is a no-op
+    assert qw.w8a8_gemm_tune_raw(A, B, C, D, E, 4, 8, 24) == qw.QW_ERROR_UNSUPPORTED
+    assert qw.w8a8_gemm_tune_raw(0, B, C, D, E, 4, 8, 16) == qw.QW_ERROR_INVALID_VALUE
+    assert qw.w8a8_gemm_tune_raw(A, B, C, D, E, 4, 8, qw.W8A8_MAX_K + 16) == qw.QW_ERROR_UNSUPPORTED
+    assert qw.w8a8_gemm_tune_raw(0, 0, 0, 0, 0, 0, 8, 16) == qw.QW_SUCCESS
 
 
 def test_gemm_path_checks():
