@@ -160,11 +160,18 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
                 for (int i = 0; i < 4; ++i)
                     *reinterpret_cast<u32x4_t *>(slice + (t * 16 + 4 * i + lane / 16) * kStageRow +
                                                  16 * (lane % 16)) = raw[i][t];
+            // Each lane reads back bytes that other lanes of the wave wrote.
+            // LDS executes a wave's accesses in order, but per lane the read
+            // and write addresses never coincide, so without these barriers
+            // the compiler may move reads above the writes they depend on
+            // (or the next iteration's writes above these reads).
+            __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int u = 0; u < kSkinnyUnroll; ++u)
 #pragma unroll
                 for (int t = 0; t < RT; ++t)
                     wv[u][t] = *reinterpret_cast<const u32x4_t *>(slice + (t * 16 + r) * kStageRow + 64 * u + 16 * g);
+            __builtin_amdgcn_wave_barrier();
         }
 #pragma unroll
         for (int u = 0; u < kSkinnyUnroll; ++u) {
