@@ -131,11 +131,13 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
     for (int s = s_begin; s < s_end; s += kSkinnyUnroll) {
         u32x4_t wv[kSkinnyUnroll][RT];
         u32x4_t xa[kSkinnyUnroll][MT], xb[kSkinnyUnroll][MT];
-        // Activation operands.  With one activation tile they are requested
-        // before the weight codes, so the two loads' latencies overlap
-        // (measured 2-4% faster); with two, after (the earlier issue held
-        // twice the registers through the weight staging: 5% slower).
-        auto load_x = [&]() __attribute__((always_inline)) {
+        // Activation operands.  For the fp16 kernel with one activation
+        // tile they are requested before the weight codes, so the two
+        // loads' latencies overlap (measured 2-4% faster); otherwise after
+        // the weight staging (two tiles measured 5% slower the other way,
+        // and the int8 kernel kept its operand arrays in scratch memory).
+        constexpr bool kXFirst = MT == 1 && !A8;
+        if constexpr (kXFirst) {
 #pragma unroll
             for (int u = 0; u < kSkinnyUnroll; ++u) {
                 const int kk = (s + u) * 64 + g * 16;
@@ -154,9 +156,7 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
                     }
                 }
             }
-        };
-        if constexpr (MT == 1)
-            load_x();
+        }
         {
             // Weight codes, loaded contiguously: instruction i of tile t
             // covers rows 4 i .. 4 i + 3, 256 bytes each (lane l: row
@@ -199,8 +199,26 @@ __global__ __launch_bounds__(KSPLIT * 64) void skinny_gemm_kernel(
                     wv[u][t] = *reinterpret_cast<const u32x4_t *>(slice + (t * 16 + r) * kStageRow + 64 * u + 16 * g);
             __builtin_amdgcn_wave_barrier();
         }
-        if constexpr (MT != 1)
-            load_x();
+        if constexpr (!kXFirst) {
+#pragma unroll
+            for (int u = 0; u < kSkinnyUnroll; ++u) {
+                const int kk = (s + u) * 64 + g * 16;
+                const bool ok = (s + u) < s_end && kk < k;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    xa[u][mt] = (u32x4_t){0u, 0u, 0u, 0u};
+                    xb[u][mt] = (u32x4_t){0u, 0u, 0u, 0u};
+                    if (ok && col_ok[mt]) {
+                        if constexpr (A8) {
+                            xa[u][mt] = *reinterpret_cast<const u32x4_t *>(qxrow[mt] + kk);
+                        } else {
+                            xa[u][mt] = *reinterpret_cast<const u32x4_t *>(xrow[mt] + kk);
+                            xb[u][mt] = *reinterpret_cast<const u32x4_t *>(xrow[mt] + kk + 8);
+                        }
+                    }
+                }
+            }
+        }
 #pragma unroll
         for (int u = 0; u < kSkinnyUnroll; ++u) {
             if constexpr (A8) {
