@@ -100,6 +100,23 @@ def test_mfma_every_tile_shape():
     assert seen == {(256, 128), (256, 64), (128, 128), (128, 64)}, "tiles exercised: %s" % sorted(seen)
 
 
+# Grids on the 256 x 128 tile whose tile order walks several weight-tile
+# columns per group, the last group narrower: 107 and 13 columns with every
+# tile of an XCD resident at once, 17 columns over several rounds of
+# resident tiles.  The whole output is compared.
+GROUPED_SHAPES = [(512, 27392, 64), (4096, 3328, 64), (8192, 4352, 64)]
+
+
+@pytest.mark.parametrize("m,n,k", GROUPED_SHAPES)
+def test_mfma_grouped_tile_order(m, n, k):
+    import int8_weight_quantized_amd as qw
+    assert qw.mfma_tile(m, n, k) == (256, 128)
+    x, q, s = _small_case(m, n, k, seed=m + n + 5)
+    say("gemm mfma grouped order m=%d n=%d k=%d" % (m, n, k))
+    y = gpu_gemm(x, q, s, path=MFMA)
+    assert_gemm_close(y, oracle.gemm(x, q, s), "mfma grouped order %dx%dx%d" % (m, n, k))
+
+
 # Shapes spanning several tiles with ragged tails in m, n and k.
 SMALL_SHAPES = [
     (1, 1000, 272), (1, 129, 1040), (2, 300, 2064), (3, 257, 528), (4, 64, 16),

@@ -67,6 +67,18 @@ SHAPES = [(1, 1000, 272), (3, 257, 528), (4, 64, 16), (8, 517, 2064), (9, 200, 2
 MFMA, SKINNY = 2, 3
 
 
+# Grids on a tile with 256 weight rows whose tile order walks several
+# weight-tile columns per group, the last group narrower; whole outputs.
+@pytest.mark.parametrize("m,n,k", [(512, 27392, 64), (4096, 3328, 64), (8192, 4352, 64)])
+def test_w8a8_grouped_tile_order(m, n, k):
+    import int8_weight_quantized_amd as qw
+    assert qw.w8a8_tile(m, n, k)[0] == 256
+    qx, sx, q, s = _codes(m, n, k, seed=m + n + 9)
+    say("w8a8 gemm mfma grouped order m=%d n=%d k=%d" % (m, n, k))
+    assert_w8a8_close(gpu_w8a8(qx, sx, q, s, MFMA), oracle.w8a8_gemm(qx, sx, q, s),
+                      "w8a8 grouped order %dx%dx%d" % (m, n, k))
+
+
 @pytest.mark.parametrize("path", [0, SKINNY, MFMA])
 @pytest.mark.parametrize("m,n,k", SHAPES)
 def test_w8a8_shapes(m, n, k, path):
