@@ -665,7 +665,8 @@ int64_t slots_per_cu();
 // share an activation tile, which measured 3-7% faster there than narrower
 // groups.  Measured on MI355X against one column per group: 5-14% faster
 // for the W8A8 tiles and 1-7% for the fp16 tiles with 256 weight rows; the
-// fp16 tiles with 128 weight rows ran 1-3% slower grouped and keep one.
+// fp16 tiles with 128 weight rows ran 1-5% slower grouped, at either width,
+// and keep one.
 template <int BN, int BM, bool A8>
 int group_width(int64_t blocks, int64_t tiles_m, int64_t tiles_n)
 {
