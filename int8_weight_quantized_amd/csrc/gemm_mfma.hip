@@ -30,6 +30,7 @@
 #include "qw_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <type_traits>
 
@@ -720,22 +721,23 @@ hipError_t launch_dma(const void *x, const uint16_t *sx, const int8_t *q, const 
 }
 
 // Workgroups of this tile shape one CU holds at once (registers and LDS),
-// queried once per device.
+// queried once per device.  Host threads may race on the first query; they
+// store the same value.
 template <int BN, int BM, bool A8>
 int64_t slots_per_cu()
 {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 1;
-    if (cached[dev] == 0) {
-        int blocks = 0;
+    int blocks = cached[dev].load(std::memory_order_relaxed);
+    if (blocks == 0) {
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, mfma_gemm_dma_kernel<4, BN, BM, A8>,
                                                         4 * kWave, 0) != hipSuccess || blocks < 1)
             blocks = 1;
-        cached[dev] = blocks;
+        cached[dev].store(blocks, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return blocks;
 }
 
 template <int BN, int BM, bool A8>
