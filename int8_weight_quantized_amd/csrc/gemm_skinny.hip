@@ -340,11 +340,13 @@ hipError_t launch_cfg(const void *x, const uint16_t *sx, const int8_t *q, const 
 
 // Largest k split per kernel variant: a workgroup of 16 waves leaves each
 // lane 128 registers, which the int8 kernel and the two-tile fp16 kernel
-// exceed (they spilled); they stop at 8 waves.
-template <int MT, bool A8>
+// exceed (they spilled); they stop at 8 waves.  Four weight tiles with two
+// activation tiles stop at 4: at 8 they spilled, and their staging slices
+// would fill most of the LDS.
+template <int RT, int MT, bool A8>
 constexpr int max_split()
 {
-    return (A8 || MT > 1) ? 8 : 16;
+    return RT == 4 ? 4 : (A8 || MT > 1) ? 8 : 16;
 }
 
 template <int RT, int MT, bool A8>
@@ -356,7 +358,7 @@ hipError_t launch_mt(const void *x, const uint16_t *sx, const int8_t *q, const u
     // at least one 64-wide step per wave
     const int64_t tiles = ((n + 16 * RT - 1) / (16 * RT)) * ((m + 16 * MT - 1) / (16 * MT));
     const int64_t steps = (k + 63) / 64;
-    constexpr int kMaxSplit = max_split<MT, A8>();
+    constexpr int kMaxSplit = max_split<RT, MT, A8>();
     int ksplit = 1;
     while (ksplit < kMaxSplit && tiles * ksplit < kSkinnyTargetWaves && steps >= 2 * ksplit)
         ksplit *= 2;
@@ -419,6 +421,14 @@ hipError_t launch_auto_rt(const void *x, const uint16_t *sx, const int8_t *q, co
     const int64_t one_tile_grid = ((n + 15) / 16) * ((m + rows - 1) / rows);
     if (one_tile_grid <= device_cu_count())
         return launch_rt<1, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
+    // Two activation tiles read 32 activation rows per k step, once per
+    // workgroup: four weight tiles halve those reads where the grid stays
+    // large (n >= 24576 at one pass).  Measured at n = 27392, k = 4096:
+    // 49.4 -> 37.0 us at m = 32, 43.9 -> 35.1 us at m = 24, W8A8 m = 32
+    // 33.9 -> 28.1 us.  With one activation tile, or a grid of 256
+    // four-tile workgroups, four tiles measured slower.
+    if (rows == 32 && one_tile_grid >= 6 * (int64_t)device_cu_count())
+        return launch_mt<4, 2, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
     return launch_rt<2, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
 }
 
@@ -427,9 +437,10 @@ hipError_t launch_auto_rt(const void *x, const uint16_t *sx, const int8_t *q, co
 hipError_t launch_skinny_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
                               const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
-    // one or two 16-row weight tiles per wave (two reuse the activation
-    // operand; four measured slower: fewer waves, longer dependent MFMA
-    // chains)
+    // one, two or four 16-row weight tiles per wave (more tiles reuse the
+    // activation operand; four only with two activation tiles on a large
+    // grid, elsewhere they measured slower: fewer waves, longer dependent
+    // MFMA chains)
     return launch_auto_rt<false>(x, nullptr, q, scales, zeros, ol, y, m, n, k, stream);
 }
 

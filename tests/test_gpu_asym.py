@@ -84,7 +84,7 @@ def test_quantize_asym_outlier_workload():
 
 
 SHAPES = [(1, 1000, 272), (2, 300, 2064), (4, 64, 16), (8, 517, 2064), (17, 300, 528), (65, 130, 96),
-          (130, 260, 4112), (300, 513, 1040), (24, 517, 2064)]
+          (130, 260, 4112), (300, 513, 1040), (24, 517, 2064), (20, 25000, 2064)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES)

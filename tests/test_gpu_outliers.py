@@ -135,7 +135,7 @@ def test_gemm_outliers_mfma_tiles():
 
 
 @pytest.mark.parametrize("path", [GEMV, SKINNY, MFMA])
-@pytest.mark.parametrize("m,n,k", [(1, 96, 512), (8, 130, 2048), (200, 300, 1040)])
+@pytest.mark.parametrize("m,n,k", [(1, 96, 512), (8, 130, 2048), (200, 300, 1040), (20, 25000, 2064)])
 def test_gemm_outliers_exact_arithmetic_bitexact(path, m, n, k):
     """X in {-1,0,1}, power-of-two scales, outlier values that are multiples
     of S / 8 (so value / S is exact too): every step is exact in fp32, and
