@@ -423,11 +423,11 @@ hipError_t launch_auto_rt(const void *x, const uint16_t *sx, const int8_t *q, co
         return launch_rt<1, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
     // Two activation tiles read 32 activation rows per k step, once per
     // workgroup: four weight tiles halve those reads where the grid stays
-    // large (n >= 24576 at one pass).  Measured at n = 27392, k = 4096:
-    // 49.4 -> 37.0 us at m = 32, 43.9 -> 35.1 us at m = 24, W8A8 m = 32
-    // 33.9 -> 28.1 us.  With one activation tile, or a grid of 256
-    // four-tile workgroups, four tiles measured slower.
-    if (rows == 32 && one_tile_grid >= 6 * (int64_t)device_cu_count())
+    // large (n >= 12288 at one pass).  Measured at k = 4096: 49.4 -> 37.0 us
+    // at m = 32 and n = 27392, 31.8 -> 26.7 us at m = 32 and n = 13824,
+    // W8A8 m = 32, n = 27392 33.9 -> 28.1 us.  With one activation tile
+    // four tiles measured slower on some of these grids.
+    if (rows == 32 && one_tile_grid >= 3 * (int64_t)device_cu_count())
         return launch_mt<4, 2, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
     return launch_rt<2, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
 }

@@ -154,9 +154,9 @@ def test_skinny_small_shapes(m, n, k):
 
 # The skinny kernel with two 16-row activation tiles per wave (17..32 rows,
 # k >= 2048) and with one (more rows, or shorter k), at weight shapes that
-# select several of its k splits; n = 27392 and 25000 take four weight tiles
-# per workgroup, the last of them partly past n.
-SKINNY_TILE_SHAPES = [(32, 4608, 4096), (24, 27392, 2048), (32, 27392, 4096), (20, 25000, 2064), (17, 1000, 2064), (31, 130, 4096), (24, 600, 1024),
+# select several of its k splits; n = 27392, 25000 and 13000 take four
+# weight tiles per workgroup, the last of them partly past n.
+SKINNY_TILE_SHAPES = [(32, 4608, 4096), (24, 27392, 2048), (32, 27392, 4096), (20, 25000, 2064), (24, 13000, 2064), (17, 1000, 2064), (31, 130, 4096), (24, 600, 1024),
                       (64, 4608, 4096), (48, 2048, 64), (40, 4096, 8192), (64, 65536, 64), (100, 1200, 2064)]
 
 

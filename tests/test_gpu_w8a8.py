@@ -61,7 +61,8 @@ def test_w8a8_workload(name):
 SHAPES = [(1, 1000, 272), (3, 257, 528), (4, 64, 16), (8, 517, 2064), (9, 200, 272), (17, 300, 528),
           (31, 129, 80), (64, 256, 256), (65, 130, 96), (100, 390, 656), (128, 128, 4096),
           (130, 260, 4112), (257, 129, 144), (300, 513, 1040), (129, 600, 528), (70, 72, 16400),
-          (24, 300, 2064), (32, 1200, 4112), (20, 25000, 2064)]  # the last three: 32-row skinny passes
+          (24, 300, 2064), (32, 1200, 4112), (20, 25000, 2064),
+          (24, 13000, 2064)]  # the last four: 32-row skinny passes
 
 
 MFMA, SKINNY = 2, 3
