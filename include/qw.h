@@ -22,12 +22,17 @@
  *   - Every pointer is a HIP device pointer (or managed memory visible to
  *     the device) owned by the caller; the library allocates no device
  *     memory and keeps no per-call state.
- *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream),
+ *     passed as `void *` so that this header needs no HIP include; the two
+ *     have the same representation (hipStream_t is a pointer type).  Calls
  *     enqueue work on it and return without waiting; results are visible
  *     after the caller synchronizes the stream.
  *   - Arguments are checked on the host before anything is enqueued; on
  *     any error nothing is launched and no output byte is written.
- *   - Results are deterministic: no atomics, fixed reduction order.
+ *   - Results are deterministic: every floating-point reduction runs in a
+ *     fixed order.  The only atomics are integer additions into the
+ *     percentile quantizer's LDS histogram, whose counts do not depend on
+ *     the order of the additions; no global-memory atomics are used.
  *   - Not safe to call with overlapping input and output buffers
  *     (rejected with QW_ERROR_INVALID_VALUE when detected).
  */
@@ -482,6 +487,32 @@ QW_API int qw_w8a8_gemm_tuned_choice(int64_t m, int64_t n, int64_t k);
  * for shapes qw_w8a8_gemm rejects or when no HIP device is current.
  */
 QW_API int qw_w8a8_gemm_mfma_tile(int64_t m, int64_t n, int64_t k);
+
+/*
+ * Measurement aids.  Neither is part of the method; they put the GEMM
+ * figures in context on the machine at hand.
+ *
+ * qw_probe_stream_read -- enqueue one plain streaming read of
+ * floor(bytes / 1024) KiB starting at p (16-byte nontemporal loads, one
+ * contiguous KiB per wave instruction, as the decode GEMV loads its
+ * weights).  Its rate on a cold buffer is the practical read ceiling the
+ * GEMV is compared with.  sink: one uint32 of device memory, written only
+ * if a wave's folded bytes equal `magic` (pass any value; the write only
+ * keeps the loads alive).  Errors: QW_ERROR_INVALID_VALUE (null p or sink
+ * with bytes >= 1024, bytes < 0), QW_ERROR_MISALIGNED (p not 16-byte
+ * aligned), QW_ERROR_LAUNCH.
+ *
+ * qw_probe_shader_clock -- enqueue one wave that spins for 20 us of the
+ * 100 MHz constant clock and writes out[0] = shader-clock ticks elapsed
+ * (s_memtime) and out[1] = constant-clock ticks elapsed (s_memrealtime);
+ * the clock in MHz is 100 * out[0] / out[1].  Enqueued right after a timed
+ * loop it reads the clock the loop left the chip at.  out: two uint64 of
+ * device memory, 8-byte aligned.  Errors: QW_ERROR_INVALID_VALUE (null
+ * out), QW_ERROR_MISALIGNED, QW_ERROR_LAUNCH.
+ */
+QW_API qw_status qw_probe_stream_read(const void *p, int64_t bytes, uint32_t magic, uint32_t *sink,
+                                      void *stream);
+QW_API qw_status qw_probe_shader_clock(uint64_t *out, void *stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 QW_API const char *qw_status_string(qw_status status);

@@ -24,7 +24,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIBRARY_PATH = os.path.join(HERE, "libqw.so")
+# QW_LIBRARY names another build of the same library (the CPU tests load a
+# host-sanitizer build this way).
+LIBRARY_PATH = os.environ.get("QW_LIBRARY") or os.path.join(HERE, "libqw.so")
 
 QW_SUCCESS = 0
 QW_ERROR_INVALID_VALUE = 1
@@ -116,6 +118,10 @@ def _load():
     lib.qw_w8a16_gemm_auto_path.restype = ctypes.c_int
     lib.qw_w8a16_gemm_mfma_tile.argtypes = [i64, i64, i64]
     lib.qw_w8a16_gemm_mfma_tile.restype = ctypes.c_int
+    lib.qw_probe_stream_read.argtypes = [vp, i64, ctypes.c_uint32, vp, vp]
+    lib.qw_probe_stream_read.restype = ctypes.c_int
+    lib.qw_probe_shader_clock.argtypes = [vp, vp]
+    lib.qw_probe_shader_clock.restype = ctypes.c_int
     lib.qw_version.argtypes = []
     lib.qw_version.restype = ctypes.c_int
     _lib_handle = lib
@@ -225,24 +231,6 @@ def w8a8_gemm_tune_raw(qx_ptr: int, sx_ptr: int, q_ptr: int, s_ptr: int, y_ptr: 
     return int(library().qw_w8a8_gemm_tune(qx_ptr, sx_ptr, q_ptr, s_ptr, y_ptr, m, n, k, stream))
 
 
-def w8a16_gemm_tune(x, q, scales, out=None):
-    """Time every kernel and MFMA tile for this shape on these tensors,
-    record the fastest for the shape bucket, and return Y (the winner's)."""
-    torch = _torch()
-    _check(x, "x", torch.float16, 2)
-    _check(q, "q", torch.int8, 2)
-    _check(scales, "scales", torch.float16, 1)
-    m, k = x.shape
-    n = q.shape[0]
-    if q.shape[1] != k or scales.shape[0] != n:
-        raise ValueError("shape mismatch")
-    y = torch.empty((m, n), dtype=torch.float16, device=x.device) if out is None else out
-    st = w8a16_gemm_tune_raw(x.data_ptr(), q.data_ptr(), scales.data_ptr(), y.data_ptr(), m, n, k, _stream_of(x))
-    if st != QW_SUCCESS:
-        raise QwError(st, "qw_w8a16_gemm_tune")
-    return y
-
-
 def outlier_capacity(k: int, clip_percentile: float) -> int:
     """Side-list slots per row that always hold the outliers (host only)."""
     c = int(library().qw_outlier_capacity(k, float(clip_percentile)))
@@ -297,18 +285,91 @@ def _stream_of(t) -> int:
     return int(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _check(t, name, dtype, ndim):
+def _check(t, name, dtype, shape=None, ndim=None, device=None):
+    """Validate one tensor argument before its pointer reaches the library:
+    a torch.Tensor of `dtype`, contiguous, with exactly `shape` (or `ndim`
+    dimensions), on `device`.  The C ABI cannot see sizes or devices, so
+    every check that protects a kernel from reading or writing outside a
+    buffer happens here."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s must be on %s (the device of the first operand), got %s" % (name, device, t.device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must be %d-D, got shape %s" % (name, ndim, tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _require_gpu(t, name):
+    """The first tensor operand fixes the device; it must be a GPU tensor."""
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
     if t.device.type != "cuda":
         raise ValueError("%s must be on a GPU device, got %s" % (name, t.device))
-    if t.dtype != dtype:
-        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
-    if t.dim() != ndim:
-        raise ValueError("%s must be %d-D, got shape %s" % (name, ndim, tuple(t.shape)))
-    if not t.is_contiguous():
-        raise ValueError("%s must be contiguous" % name)
+    return t.device
+
+
+def _outputs(out, specs, device):
+    """Check caller-provided outputs (a tensor or a tuple of tensors) against
+    (name, dtype, shape) specs; None means 'allocate them'."""
+    torch = _torch()
+    if out is None:
+        return tuple(torch.empty(shape, dtype=dtype, device=device) for _, dtype, shape in specs)
+    outs = out if isinstance(out, (tuple, list)) else (out,)
+    if len(outs) != len(specs):
+        raise ValueError("out must hold %d tensor(s), got %d" % (len(specs), len(outs)))
+    for t, (name, dtype, shape) in zip(outs, specs):
+        _check(t, name, dtype, shape=shape, device=device)
+    return tuple(outs)
+
+
+def _check_path(path):
+    if path not in PATHS:
+        raise ValueError("path must be one of %s" % sorted(PATHS))
+
+
+# Validation of each call, separate from the launch so that every rejection
+# can be exercised without a GPU (with tensors on one device of any type).
+
+def _validate_quantize(w, out, device):
+    torch = _torch()
+    f16 = isinstance(w, torch.Tensor) and w.dtype == torch.float16
+    _check(w, "w", torch.float16 if f16 else torch.float32, ndim=2, device=device)
+    n, k = w.shape
+    q, s = _outputs(out, (("q", torch.int8, (n, k)), ("scales", torch.float16, (n,))), device)
+    return f16, n, k, q, s
+
+
+def _validate_gemm(x, q, scales, out, path, device, zeros=None, ol=None, a8=False, sx=None):
+    torch = _torch()
+    _check(x, "qx" if a8 else "x", torch.int8 if a8 else torch.float16, ndim=2, device=device)
+    m, k = x.shape
+    _check(q, "q", torch.int8, ndim=2, device=device)
+    n = q.shape[0]
+    _check(q, "q", torch.int8, shape=(n, k), device=device)
+    _check(scales, "scales", torch.float16, shape=(n,), device=device)
+    if sx is not None:
+        _check(sx, "sx", torch.float16, shape=(m,), device=device)
+    if zeros is not None:
+        _check(zeros, "zeros", torch.int8, shape=(n,), device=device)
+    cap = 0
+    if ol is not None:
+        ol_idx, ol_val = ol
+        _check(ol_idx, "ol_idx", torch.int32, ndim=2, device=device)
+        cap = ol_idx.shape[1]
+        _check(ol_idx, "ol_idx", torch.int32, shape=(n, cap), device=device)
+        _check(ol_val, "ol_val", torch.float32, shape=(n, cap), device=device)
+    if path is not None:
+        _check_path(path)
+    (y,) = _outputs(out, (("out", torch.float16, (m, n)),), device)
+    return m, n, k, cap, y
 
 
 def quantize_weights(w, clip_percentile: float = 100.0, out=None):
@@ -319,19 +380,8 @@ def quantize_weights(w, clip_percentile: float = 100.0, out=None):
     the row absmax.  Returns (q int8 [N, K], scales float16 [N]);
     ``out=(q, scales)`` writes into preallocated tensors.
     """
-    torch = _torch()
-    f16 = isinstance(w, torch.Tensor) and w.dtype == torch.float16
-    _check(w, "w", torch.float16 if f16 else torch.float32, 2)
-    n, k = w.shape
-    if out is None:
-        q = torch.empty((n, k), dtype=torch.int8, device=w.device)
-        s = torch.empty((n,), dtype=torch.float16, device=w.device)
-    else:
-        q, s = out
-        _check(q, "q", torch.int8, 2)
-        _check(s, "scales", torch.float16, 1)
-        if tuple(q.shape) != (n, k) or tuple(s.shape) != (n,):
-            raise ValueError("output shapes must be [N, K] and [N]")
+    device = _require_gpu(w, "w")
+    f16, n, k, q, s = _validate_quantize(w, out, device)
     raw = quantize_weights_f16_raw if f16 else quantize_weights_raw
     st = raw(w.data_ptr(), n, k, clip_percentile, q.data_ptr(), s.data_ptr(), _stream_of(w))
     if st != QW_SUCCESS:
@@ -342,24 +392,8 @@ def quantize_weights(w, clip_percentile: float = 100.0, out=None):
 def w8a16_gemm(x, q, scales, out=None, path: str = "auto"):
     """Y = X * dequant(q)^T: x cuda fp16 [M, K], q int8 [N, K], scales fp16 [N]
     -> fp16 [M, N].  ``path`` forces a kernel ("gemv", "skinny" or "mfma")."""
-    torch = _torch()
-    _check(x, "x", torch.float16, 2)
-    _check(q, "q", torch.int8, 2)
-    _check(scales, "scales", torch.float16, 1)
-    m, k = x.shape
-    n = q.shape[0]
-    if q.shape[1] != k or scales.shape[0] != n:
-        raise ValueError("shape mismatch: x %s, q %s, scales %s" % (tuple(x.shape), tuple(q.shape),
-                                                                     tuple(scales.shape)))
-    if out is None:
-        y = torch.empty((m, n), dtype=torch.float16, device=x.device)
-    else:
-        y = out
-        _check(y, "out", torch.float16, 2)
-        if tuple(y.shape) != (m, n):
-            raise ValueError("out must be [M, N]")
-    if path not in PATHS:
-        raise ValueError("path must be one of %s" % sorted(PATHS))
+    device = _require_gpu(x, "x")
+    m, n, k, _, y = _validate_gemm(x, q, scales, out, path, device)
     st = w8a16_gemm_raw(x.data_ptr(), q.data_ptr(), scales.data_ptr(), y.data_ptr(), m, n, k,
                         _stream_of(x), PATHS[path])
     if st != QW_SUCCESS:
@@ -367,21 +401,33 @@ def w8a16_gemm(x, q, scales, out=None, path: str = "auto"):
     return y
 
 
+def w8a16_gemm_tune(x, q, scales, out=None):
+    """Time every kernel and MFMA tile for this shape on these buffers,
+    record the fastest for the shape's bucket, and return Y (the winner's
+    result).  Later automatic calls of the bucket use the record."""
+    device = _require_gpu(x, "x")
+    m, n, k, _, y = _validate_gemm(x, q, scales, out, None, device)
+    st = w8a16_gemm_tune_raw(x.data_ptr(), q.data_ptr(), scales.data_ptr(), y.data_ptr(), m, n, k, _stream_of(x))
+    if st != QW_SUCCESS:
+        raise QwError(st, "qw_w8a16_gemm_tune")
+    return y
+
+
+def _validate_fixed_range(w, bounds, out, device):
+    torch = _torch()
+    _check(w, "w", torch.float32, ndim=2, device=device)
+    n, k = w.shape
+    _check(bounds, "bounds", torch.float32, shape=(n,), device=device)
+    q, s = _outputs(out, (("q", torch.int8, (n, k)), ("scales", torch.float16, (n,))), device)
+    return n, k, q, s
+
+
 def quantize_weights_fixed_range(w, bounds, out=None):
     """Per-row symmetric int8 quantization with given clip bounds: w cuda
     float32 [N, K], bounds cuda float32 [N] (finite, >= 0).  Returns
     (q int8 [N, K], scales float16 [N])."""
-    torch = _torch()
-    _check(w, "w", torch.float32, 2)
-    _check(bounds, "bounds", torch.float32, 1)
-    n, k = w.shape
-    if bounds.shape[0] != n:
-        raise ValueError("bounds must be [N]")
-    if out is None:
-        q = torch.empty((n, k), dtype=torch.int8, device=w.device)
-        s = torch.empty((n,), dtype=torch.float16, device=w.device)
-    else:
-        q, s = out
+    device = _require_gpu(w, "w")
+    n, k, q, s = _validate_fixed_range(w, bounds, out, device)
     st = quantize_weights_fixed_range_raw(w.data_ptr(), n, k, bounds.data_ptr(), q.data_ptr(), s.data_ptr(),
                                           _stream_of(w))
     if st != QW_SUCCESS:
@@ -394,13 +440,15 @@ def quantize_weights_outliers(w, clip_percentile: float):
     (q int8 [N, K], scales float16 [N], ol_idx int32 [N, C], ol_val float32
     [N, C]) with C = outlier_capacity(K, clip_percentile)."""
     torch = _torch()
-    _check(w, "w", torch.float32, 2)
+    device = _require_gpu(w, "w")
+    _check(w, "w", torch.float32, ndim=2, device=device)
     n, k = w.shape
     cap = outlier_capacity(k, clip_percentile)
-    q = torch.empty((n, k), dtype=torch.int8, device=w.device)
-    s = torch.empty((n,), dtype=torch.float16, device=w.device)
-    idx = torch.empty((n, max(cap, 1)), dtype=torch.int32, device=w.device)[:, :cap]
-    val = torch.empty((n, max(cap, 1)), dtype=torch.float32, device=w.device)[:, :cap]
+    q = torch.empty((n, k), dtype=torch.int8, device=device)
+    s = torch.empty((n,), dtype=torch.float16, device=device)
+    # (at least one slot allocated, so that the pointers are valid with cap 0)
+    idx = torch.empty((n, max(cap, 1)), dtype=torch.int32, device=device)[:, :cap]
+    val = torch.empty((n, max(cap, 1)), dtype=torch.float32, device=device)[:, :cap]
     st = quantize_weights_outliers_raw(w.data_ptr(), n, k, clip_percentile, q.data_ptr(), s.data_ptr(),
                                        idx.data_ptr(), val.data_ptr(), cap, _stream_of(w))
     if st != QW_SUCCESS:
@@ -412,21 +460,8 @@ def w8a16_gemm_outliers(x, q, scales, ol_idx, ol_val, out=None, path: str = "aut
     """Y = X * dequant(q)^T plus the exact outlier side lists: x cuda fp16
     [M, K], q int8 [N, K], scales fp16 [N], ol_idx int32 [N, C], ol_val
     float32 [N, C] -> fp16 [M, N]."""
-    torch = _torch()
-    _check(x, "x", torch.float16, 2)
-    _check(q, "q", torch.int8, 2)
-    _check(scales, "scales", torch.float16, 1)
-    m, k = x.shape
-    n = q.shape[0]
-    cap = ol_idx.shape[1]
-    if ol_idx.dtype != torch.int32 or ol_val.dtype != torch.float32 or tuple(ol_val.shape) != (n, cap) \
-            or tuple(ol_idx.shape) != (n, cap) or not ol_idx.is_contiguous() or not ol_val.is_contiguous():
-        raise ValueError("side lists must be contiguous int32 / float32 [N, C]")
-    if q.shape[1] != k or scales.shape[0] != n:
-        raise ValueError("shape mismatch")
-    y = torch.empty((m, n), dtype=torch.float16, device=x.device) if out is None else out
-    if path not in PATHS:
-        raise ValueError("path must be one of %s" % sorted(PATHS))
+    device = _require_gpu(x, "x")
+    m, n, k, cap, y = _validate_gemm(x, q, scales, out, path, device, ol=(ol_idx, ol_val))
     st = w8a16_gemm_outliers_raw(x.data_ptr(), q.data_ptr(), scales.data_ptr(), ol_idx.data_ptr(),
                                  ol_val.data_ptr(), cap, y.data_ptr(), m, n, k, _stream_of(x), PATHS[path])
     if st != QW_SUCCESS:
@@ -434,16 +469,16 @@ def w8a16_gemm_outliers(x, q, scales, ol_idx, ol_val, out=None, path: str = "aut
     return y
 
 
-def quantize_weights_asym(w):
+def quantize_weights_asym(w, out=None):
     """Asymmetric per-row int8 quantization of a cuda float32 [N, K] weight:
     returns (q int8 [N, K], scales float16 [N], zeros int8 [N]) with
     W ~ scales[:, None] * (q - zeros[:, None])."""
     torch = _torch()
-    _check(w, "w", torch.float32, 2)
+    device = _require_gpu(w, "w")
+    _check(w, "w", torch.float32, ndim=2, device=device)
     n, k = w.shape
-    q = torch.empty((n, k), dtype=torch.int8, device=w.device)
-    s = torch.empty((n,), dtype=torch.float16, device=w.device)
-    z = torch.empty((n,), dtype=torch.int8, device=w.device)
+    q, s, z = _outputs(out, (("q", torch.int8, (n, k)), ("scales", torch.float16, (n,)),
+                             ("zeros", torch.int8, (n,))), device)
     st = quantize_weights_asym_raw(w.data_ptr(), n, k, q.data_ptr(), s.data_ptr(), z.data_ptr(), _stream_of(w))
     if st != QW_SUCCESS:
         raise QwError(st, "qw_quantize_weights_asym")
@@ -453,18 +488,8 @@ def quantize_weights_asym(w):
 def w8a16_gemm_asym(x, q, scales, zeros, out=None, path: str = "auto"):
     """Y = X * (scales * (q - zeros))^T for asymmetric weights: x cuda fp16
     [M, K], q int8 [N, K], scales fp16 [N], zeros int8 [N] -> fp16 [M, N]."""
-    torch = _torch()
-    _check(x, "x", torch.float16, 2)
-    _check(q, "q", torch.int8, 2)
-    _check(scales, "scales", torch.float16, 1)
-    _check(zeros, "zeros", torch.int8, 1)
-    m, k = x.shape
-    n = q.shape[0]
-    if q.shape[1] != k or scales.shape[0] != n or zeros.shape[0] != n:
-        raise ValueError("shape mismatch")
-    y = torch.empty((m, n), dtype=torch.float16, device=x.device) if out is None else out
-    if path not in PATHS:
-        raise ValueError("path must be one of %s" % sorted(PATHS))
+    device = _require_gpu(x, "x")
+    m, n, k, _, y = _validate_gemm(x, q, scales, out, path, device, zeros=zeros)
     st = w8a16_gemm_asym_raw(x.data_ptr(), q.data_ptr(), scales.data_ptr(), zeros.data_ptr(), y.data_ptr(),
                              m, n, k, _stream_of(x), PATHS[path])
     if st != QW_SUCCESS:
@@ -482,28 +507,23 @@ def quantize_activations(x, out=None):
 def w8a8_gemm(qx, sx, q, scales, out=None):
     """Y = (qx * q^T) * sx[:, None] * scales[None, :]: qx int8 [M, K], sx fp16
     [M], q int8 [N, K], scales fp16 [N] -> fp16 [M, N]."""
-    torch = _torch()
-    _check(qx, "qx", torch.int8, 2)
-    _check(sx, "sx", torch.float16, 1)
-    _check(q, "q", torch.int8, 2)
-    _check(scales, "scales", torch.float16, 1)
-    m, k = qx.shape
-    n = q.shape[0]
-    if q.shape[1] != k or scales.shape[0] != n or sx.shape[0] != m:
-        raise ValueError("shape mismatch: qx %s, sx %s, q %s, scales %s" % (
-            tuple(qx.shape), tuple(sx.shape), tuple(q.shape), tuple(scales.shape)))
-    if out is None:
-        y = torch.empty((m, n), dtype=torch.float16, device=qx.device)
-    else:
-        y = out
-        _check(y, "out", torch.float16, 2)
-        if tuple(y.shape) != (m, n):
-            raise ValueError("out must be [M, N]")
+    device = _require_gpu(qx, "qx")
+    m, n, k, _, y = _validate_gemm(qx, q, scales, out, None, device, a8=True, sx=sx)
     st = w8a8_gemm_raw(qx.data_ptr(), sx.data_ptr(), q.data_ptr(), scales.data_ptr(), y.data_ptr(),
                        m, n, k, _stream_of(qx))
     if st != QW_SUCCESS:
         raise QwError(st, "qw_w8a8_gemm")
     return y
+
+
+def probe_stream_read_raw(p: int, nbytes: int, magic: int, sink_ptr: int, stream: int = 0) -> int:
+    """Enqueue the plain streaming-read probe over nbytes at device pointer p."""
+    return int(library().qw_probe_stream_read(p, nbytes, magic & 0xffffffff, sink_ptr, stream))
+
+
+def probe_shader_clock_raw(out_ptr: int, stream: int = 0) -> int:
+    """Enqueue the shader-clock probe; out_ptr: two uint64 of device memory."""
+    return int(library().qw_probe_shader_clock(out_ptr, stream))
 
 
 __all__ = ["quantize_weights", "quantize_weights_fixed_range", "quantize_weights_asym", "w8a16_gemm_asym",
@@ -513,4 +533,4 @@ __all__ = ["quantize_weights", "quantize_weights_fixed_range", "quantize_weights
            "status_string", "version", "library", "auto_path", "mfma_tile", "w8a8_tile",
            "quantize_weights_raw", "quantize_weights_f16_raw", "quantize_weights_fixed_range_raw", "quantize_weights_asym_raw", "w8a16_gemm_asym_raw",
            "quantize_weights_outliers_raw", "w8a16_gemm_outliers_raw", "w8a16_gemm_raw", "w8a8_gemm_raw",
-           "PATHS", "LIBRARY_PATH"]
+           "probe_stream_read_raw", "probe_shader_clock_raw", "PATHS", "LIBRARY_PATH"]

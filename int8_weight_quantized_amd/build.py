@@ -42,12 +42,13 @@ UNITS = {
     "gemm_mfma.hip": [],
     "gemm_skinny.hip": [],
     "tune.hip": [],
+    "probe.hip": [],
 }
 
 
-def _compile(unit: str, extra, verbose: bool, defines=()) -> str:
+def _compile(unit: str, extra, verbose: bool, defines=(), build_dir: str = BUILD_DIR) -> str:
     src = os.path.join(CSRC, unit)
-    obj = os.path.join(BUILD_DIR, unit.replace(".hip", ".o"))
+    obj = os.path.join(build_dir, unit.replace(".hip", ".o"))
     cmd = [HIPCC, *COMMON, *extra, *defines, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -60,20 +61,25 @@ def _compile(unit: str, extra, verbose: bool, defines=()) -> str:
     return obj
 
 
-def build(verbose: bool = False, defines=()) -> str:
-    """Compile every HIP unit and link libqw.so; returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, defines=(), extra=(), build_dir: str = BUILD_DIR, output: str = LIBRARY) -> str:
+    """Compile every HIP unit and link libqw.so; returns the library path.
+
+    `extra` adds compiler flags to every unit and `build_dir` / `output`
+    place a variant build elsewhere (the host-sanitizer build of the CPU
+    tests uses both)."""
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(UNITS))) as ex:
-        objs = list(ex.map(lambda kv: _compile(kv[0], kv[1], verbose, defines), UNITS.items()))
-    tmp = LIBRARY + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda kv: _compile(kv[0], [*kv[1], *extra], verbose, defines, build_dir),
+                           UNITS.items()))
+    tmp = output + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stderr)
-    os.replace(tmp, LIBRARY)
-    return LIBRARY
+    os.replace(tmp, output)
+    return output
 
 
 if __name__ == "__main__":

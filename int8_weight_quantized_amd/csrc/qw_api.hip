@@ -4,6 +4,7 @@
 // enqueued, so a rejected call launches nothing and writes nothing.
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <atomic>
 #include <mutex>
@@ -548,9 +549,36 @@ QW_API int qw_w8a8_gemm_tuned_choice(int64_t m, int64_t n, int64_t k)
     return qw::tuned_choice(m, n, k, true);
 }
 
+QW_API qw_status qw_probe_stream_read(const void *p, int64_t bytes, uint32_t magic, uint32_t *sink, void *stream)
+{
+    if (bytes < 0)
+        return QW_ERROR_INVALID_VALUE;
+    if (bytes < 1024)
+        return QW_SUCCESS;
+    if (p == nullptr || sink == nullptr)
+        return QW_ERROR_INVALID_VALUE;
+    if (misaligned(p))
+        return QW_ERROR_MISALIGNED;
+    return launch_status(qw::launch_stream_read(p, bytes, magic, sink, static_cast<hipStream_t>(stream)));
+}
+
+QW_API qw_status qw_probe_shader_clock(uint64_t *out, void *stream)
+{
+    if (out == nullptr)
+        return QW_ERROR_INVALID_VALUE;
+    if ((reinterpret_cast<uintptr_t>(out) & 7u) != 0)
+        return QW_ERROR_MISALIGNED;
+    return launch_status(qw::launch_shader_clock(out, static_cast<hipStream_t>(stream)));
+}
+
 QW_API const char *qw_status_string(qw_status status)
 {
-    switch (status) {
+    // C callers may pass any int; reading it through the enum type would be
+    // undefined for values outside the enumeration, so read its bytes
+    static_assert(sizeof(qw_status) == sizeof(int), "qw_status is int-sized");
+    int code = 0;
+    memcpy(&code, &status, sizeof code);
+    switch (code) {
     case QW_SUCCESS:
         return "success";
     case QW_ERROR_INVALID_VALUE:

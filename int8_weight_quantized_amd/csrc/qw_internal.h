@@ -94,6 +94,13 @@ hipError_t launch_w8a8_skinny(const int8_t *qx, const uint16_t *sx, const int8_t
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
+// Measurement aids (probe.hip): a plain streaming read of `bytes` (a
+// multiple of 1 KiB is read; the rest is ignored), and the shader clock
+// measured over a short spin (out[0] shader-clock ticks, out[1] ticks of
+// the 100 MHz constant clock).
+hipError_t launch_stream_read(const void *p, int64_t bytes, uint32_t magic, uint32_t *sink, hipStream_t stream);
+hipError_t launch_shader_clock(uint64_t *out, hipStream_t stream);
+
 // Per-shape tuning records (tune.hip).  A choice encodes the kernel and the
 // MFMA tile as path * kChoicePath + tile (tile 0 for GEMV and skinny).
 constexpr int kChoicePath = 1000000;

@@ -28,6 +28,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "qw_oracle.c")
 LIBRARY = os.path.join(_HERE, "liboracle.so")
+# QW_ORACLE_LIBRARY names another build of the oracle (the sanitizer test
+# loads an AddressSanitizer / UBSan build this way); it is used as is.
+_OVERRIDE = os.environ.get("QW_ORACLE_LIBRARY")
 
 # -ffp-contract=off: no fused multiply-add may merge two IEEE operations.
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
@@ -100,9 +103,12 @@ def lib():
     global _lib
     with _lock:
         if _lib is None:
-            if _needs_build():
-                build()
-            _lib = load_library(LIBRARY)
+            if _OVERRIDE:
+                _lib = load_library(_OVERRIDE)
+            else:
+                if _needs_build():
+                    build()
+                _lib = load_library(LIBRARY)
     return _lib
 
 

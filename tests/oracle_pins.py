@@ -413,17 +413,56 @@ def pin_gemm_zero_and_scaling(o, seed=10):
     assert np.array_equal(o.gemm(x, q[:1], s[:1].view(np.uint16))[:, 0], ref[:, 0])
 
 
-def pin_cosine_vs_unquantized(o):
-    """The W8A16 output stays above 0.99 cosine similarity to the
-    unquantized product (ChatGLM2/BM1684X page, section 2)."""
+def _cosine_vs_unquantized(o, name, rows=None):
     import synthetic
-    wl = synthetic.BY_NAME["tiny_m1_k256_n512"]
+    wl = synthetic.BY_NAME[name]
     x, w = synthetic.make_inputs(wl)
-    q, s, _ = o.quantize(w, 100.0)
+    if rows is not None:
+        x = x[:rows]
+    q, s, _ = o.quantize(w, wl.clip_percentile)
     ref = o.gemm(x, q, s).ravel()
     full = (x.astype(np.float64) @ w.astype(np.float64).T).ravel()
-    cos = float(ref @ full / (np.linalg.norm(ref) * np.linalg.norm(full)))
-    assert cos > 0.99, cos
+    return float(ref @ full / (np.linalg.norm(ref) * np.linalg.norm(full)))
+
+
+def pin_cosine_vs_unquantized(o):
+    """The W8A16 output stays above 0.99 cosine similarity to the
+    unquantized product (ChatGLM2/BM1684X page, section 2), on the tiny,
+    the small-batch and the FFN workload (the FFN with its 99.99th
+    percentile clip, on its first 256 activation rows).  A dropped scale,
+    a wrong row's scale or a transposed operand falls far below."""
+    for name, rows in (("tiny_m1_k256_n512", None), ("small_batch_m8_k4096_n4608", None),
+                       ("transformer_big_ffn_outliers_m4096_k1024_n4096", 256)):
+        cos = _cosine_vs_unquantized(o, name, rows)
+        assert cos > 0.99, (name, cos)
+
+
+def pin_page_matmul_sizes(o):
+    """ChatGLM2/BM1684X page, section 3 (TPU-MLIR实现): the right operand of
+    one ChatGLM2 MatMul, 4096 x 27392, is 214 MB in F16 and 107 MB after
+    int8 quantization (MB read as MiB, truncated; fixture
+    tests/golden/chatglm2_matmul_sizes.json).  The oracle's codes for a
+    weight of that shape take exactly N * K bytes, one per weight, and its
+    scales one binary16 per output row."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                           "chatglm2_matmul_sizes.json"), encoding="utf-8") as f:
+        g = json.load(f)
+    n, k = g["n"], g["k"]
+    w = np.zeros((n, k), dtype=np.float32)
+    w[:, 0] = 0.02  # every row gets a nonzero scale
+    q, s, _ = o.quantize(w, 100.0)
+    assert q.dtype == np.int8 and q.shape == (n, k)
+    assert (q.nbytes >> 20) == g["int8_mb"]
+    assert ((2 * n * k) >> 20) == g["f16_mb"]
+    assert s.dtype == np.uint16 and s.shape == (n,)
+    # the page's 4096-entry scale (0.008 MB) is one per K column, the
+    # recorded conflict: one per output row is N entries
+    assert abs(g["page_scale_count"] * 2 / 1e6 - g["page_scale_mb"]) < 5e-4
+    assert s.nbytes == 2 * n
+    assert np.all(q[:, 0] == 127) and np.all(q[:, 1:] == 0)
+
 
 
 # --------------------------------------------------------------------------
@@ -740,6 +779,7 @@ FAST_PINS = (
     pin_gemm_bruteforce,
     pin_gemm_zero_and_scaling,
     pin_cosine_vs_unquantized,
+    pin_page_matmul_sizes,
     pin_fixed_range_bruteforce,
     pin_fixed_range_of_measured_bound,
     pin_outliers_split,

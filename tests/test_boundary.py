@@ -375,3 +375,59 @@ def test_torch_binding_rejects_cpu_tensors():
     with pytest.raises((TypeError, ValueError)):
         qw.w8a16_gemm(torch.zeros(1, 16), torch.zeros(4, 16, dtype=torch.int8),
                       torch.zeros(4, dtype=torch.float16))
+
+
+# ---------------------------------------------------------------------------
+# Launch failures: a call that passes every host check but cannot be
+# enqueued (here: no GPU in the process) reports QW_ERROR_LAUNCH.  The fake
+# addresses are never dereferenced because nothing is launched; the test is
+# skipped wherever a GPU is visible, where they would reach a kernel.
+# ---------------------------------------------------------------------------
+
+def _gpu_visible():
+    if os.path.exists("/dev/kfd"):
+        return True
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except ImportError:
+        return False
+
+
+no_gpu_only = pytest.mark.skipif(_gpu_visible(), reason="valid calls would launch kernels on fake addresses")
+
+
+@no_gpu_only
+def test_valid_calls_without_a_device_report_launch_errors():
+    L = qw.QW_ERROR_LAUNCH
+    assert qw.quantize_weights_raw(A, 4, 16, 100.0, B, C) == L
+    assert qw.quantize_weights_raw(A, 4, 16, 99.0, B, C) == L
+    assert qw.quantize_weights_f16_raw(A, 4, 16, 100.0, B, C) == L
+    assert qw.quantize_weights_fixed_range_raw(A, 4, 16, D, B, C) == L
+    assert qw.quantize_weights_asym_raw(A, 4, 16, B, C, D) == L
+    for path in (0, 1, 2, 3):
+        assert qw.w8a16_gemm_raw(A, B, C, D, 1, 16, 16, 0, path) == L
+        assert qw.w8a16_gemm_asym_raw(A, B, C, E, D, 1, 16, 16, 0, path) == L
+    for path in (0, 2, 3):
+        assert qw.w8a8_gemm_raw(A, E, B, C, D, 4, 16, 16, 0, path) == L
+    assert qw.probe_stream_read_raw(A, 4096, 0, B) == L
+    assert qw.probe_shader_clock_raw(A) == L
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, -1, 0, B), qw.QW_ERROR_INVALID_VALUE),      # negative size
+    ((0, 4096, 0, B), qw.QW_ERROR_INVALID_VALUE),    # null buffer
+    ((A, 4096, 0, 0), qw.QW_ERROR_INVALID_VALUE),    # null sink
+    ((A + 8, 4096, 0, B), qw.QW_ERROR_MISALIGNED),
+])
+def test_probe_stream_read_rejects(args, status):
+    assert qw.probe_stream_read_raw(*args) == status
+
+
+def test_probe_stream_read_below_one_chunk_is_noop():
+    assert qw.probe_stream_read_raw(0, 1023, 0, 0) == qw.QW_SUCCESS
+
+
+def test_probe_shader_clock_rejects():
+    assert qw.probe_shader_clock_raw(0) == qw.QW_ERROR_INVALID_VALUE
+    assert qw.probe_shader_clock_raw(A + 4) == qw.QW_ERROR_MISALIGNED
