@@ -1,24 +1,31 @@
 #!/usr/bin/env python3
-"""Benchmark of the W8A16 hot path on one MI355X.
+"""Benchmark of the W8A16 GEMM on one MI355X.
 
-One step is one pass of the whole path over one batch of synthetic input:
-quantize the fp32 weight (per-row bound, fp16 scale, int8 codes; one HIP
-kernel) and run the W8A16 matmul with the activations (one HIP kernel).
-The default workload is the ChatGLM2-6B-like decode GEMV (M=1, K=4096,
-N=27392).  Inputs are seeded synthetic tensors already resident in HBM when
-the timed region starts; the step rotates over enough copies of its
-operands that the 256 MB Infinity Cache cannot serve them from one step to
-the next.
+The metric is the W8A16 GEMM's effective HBM throughput at decode (M = 1,
+the ChatGLM2-6B-like MatMul K = 4096, N = 27392) with its TFLOP/s at
+prefill (M = 512) beside it.  One step is one W8A16 GEMM call over one
+batch of synthetic input (int8 codes, fp16 scales and activations resident
+in HBM); the weight quantizer runs once per weight, offline, so it is timed
+separately ("full_step" = quantize + GEMM).  Every timed loop rotates over
+enough operand sets (more than twice the 256 MB Infinity Cache) that no
+launch finds its weights in cache, and is timed with HIP events on the
+launch stream around the whole loop of back-to-back launches: the average
+is the sustained per-launch time, which is also what a rocprofv3 kernel
+trace of the same loop reports (back-to-back launches leave no gap).
 
-Printed: ONE JSON line with the whole-step throughput (algorithmic bytes of
-both kernels / step time, in TB/s), a roofline entry for the kernel that
-takes most of the step (its algorithmic bytes / its average duration,
-measured with HIP events on the launch stream), per-kernel figures, cold
-GEMM-only figures for every workload (decode TB/s, prefill TFLOP/s), cold
-figures of the W8A8 (int8 x int8) GEMM with per-token activation
-quantization, and the CPU oracle timed on the host cores.
+Printed: ONE JSON line with
+  value / roofline       decode GEMV: effective TB/s, fraction of 8 TB/s,
+                         rocprofv3-counted HBM traffic when measured on the
+                         current source;
+  roofline_prefill       prefill MFMA GEMM: TFLOP/s, fraction of 2.5 PF;
+  stream_ceiling         a plain streaming read of the same bytes;
+  sclk_mhz               shader clock right after each timed loop;
+  full_step              quantize + GEMM on the decode workload;
+  gemm_cold              every workload, GEMM only;
+  w8a8_cold, outliers_cold, gemm_tuned   the widened paths;
+  cpu_baseline           the CPU oracle on all host cores and on one.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-secondary]
 """
 
 from __future__ import annotations
@@ -28,7 +35,9 @@ import hashlib
 import json
 import math
 import os
+import platform
 import re
+import subprocess
 import sys
 import time
 
@@ -41,6 +50,8 @@ HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, AMD published
 MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 MFMA, AMD published
 MFMA_I8_PEAK_TOPS = 5000.0       # MI355X dense int8 MFMA, AMD published
 MALL_BYTES = 256 << 20           # Infinity Cache
+DECODE = "chatglm2_decode_m1_k4096_n27392"
+PREFILL = "chatglm2_prefill_m512_k4096_n27392"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CSRC = os.path.join(ROOT, "int8_weight_quantized_amd", "csrc")
 KERNEL_SOURCES = {
@@ -105,47 +116,86 @@ def measured_traffic(kernel, workload):
     return ent.get("hbm_bytes_per_launch")
 
 
-def gemm_kernel_name(m, n, k):
-    import int8_weight_quantized_amd as qw
-    return qw.auto_path(m, n, k)
-
-
 def rotation_count(bytes_per_set, minimum=2, cap=64):
+    """Operand sets whose total exceeds twice the Infinity Cache."""
     return int(min(cap, max(minimum, math.ceil(2 * MALL_BYTES / bytes_per_set))))
 
 
-class StepRunner:
-    """Device buffers for R rotating operand sets of one workload."""
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
 
-    def __init__(self, wl, sets, with_weights=True):
-        import numpy as np
+class Clock:
+    """The shader clock right after a timed loop (library probe: shader-clock
+    ticks against the 100 MHz constant clock over a 20 us spin)."""
+
+    def __init__(self):
+        import torch
+
+        import int8_weight_quantized_amd as qw
+        self.qw, self.torch = qw, torch
+        self.buf = torch.zeros(2, dtype=torch.int64, device="cuda:0")
+
+    def enqueue(self, stream):
+        st = self.qw.probe_shader_clock_raw(self.buf.data_ptr(), stream)
+        if st:
+            raise RuntimeError(self.qw.status_string(st))
+
+    def mhz(self):
+        ticks, ref = (int(v) for v in self.buf.cpu().tolist())
+        return 100.0 * ticks / ref if ref > 0 else None
+
+
+def timed_loop(launch, sets, launches, warmup, clock=None, stream=None):
+    """Sustained per-launch time (ms) of `launches` back-to-back launches,
+    each on the next operand set, after `warmup` untimed ones.  A GPU-side
+    sleep is queued first so that every launch is enqueued before the GPU
+    reaches the start event: the event pair then brackets device time only.
+    Returns (ms per launch, wall ms of the bracket, clock MHz or None)."""
+    import torch
+    for it in range(warmup):
+        launch(it % sets)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    torch.cuda._sleep(20_000_000)
+    a.record()
+    for it in range(launches):
+        launch((warmup + it) % sets)
+    b.record()
+    if clock is not None:
+        clock.enqueue(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    return a.elapsed_time(b) / launches, wall, (clock.mhz() if clock is not None else None)
+
+
+# ---------------------------------------------------------------------------
+# operand sets
+# ---------------------------------------------------------------------------
+
+class GemmSets:
+    """R rotating W8A16 operand sets of one workload, codes and scales from
+    the library's own quantizer (or, with `with_weights`, the fp32 weights
+    too, for the quantize + GEMM step)."""
+
+    def __init__(self, wl, sets, with_weights=False):
         import torch
 
         import int8_weight_quantized_amd as qw
         import synthetic
-        self.qw, self.torch, self.wl = qw, torch, wl
+        self.qw, self.torch, self.wl, self.sets = qw, torch, wl, sets
         x, w = synthetic.make_inputs(wl)
         dev = "cuda:0"
         xd = torch.from_numpy(x).to(dev)
         self.x = [xd] + [xd.clone() for _ in range(sets - 1)]
-        if with_weights:
-            wd = torch.from_numpy(w).to(dev)
-            self.w = [wd] + [wd.clone() for _ in range(sets - 1)]
-        else:
-            self.w = None
-        self.q = [torch.empty((wl.n, wl.k), dtype=torch.int8, device=dev) for _ in range(sets)]
-        self.s = [torch.empty((wl.n,), dtype=torch.float16, device=dev) for _ in range(sets)]
+        wd = torch.from_numpy(w).to(dev)
+        del x, w
+        self.w = ([wd] + [wd.clone() for _ in range(sets - 1)]) if with_weights else None
+        q0, s0 = qw.quantize_weights(wd, wl.clip_percentile)
+        self.q = [q0] + [q0.clone() for _ in range(sets - 1)]
+        self.s = [s0] + [s0.clone() for _ in range(sets - 1)]
         self.y = [torch.empty((wl.m, wl.n), dtype=torch.float16, device=dev) for _ in range(sets)]
-        if not with_weights:
-            # codes/scales are produced once by the library's own quantizer
-            wd = torch.from_numpy(w).to(dev)
-            q0, s0 = qw.quantize_weights(wd, wl.clip_percentile)
-            for i in range(sets):
-                self.q[i].copy_(q0)
-                self.s[i].copy_(s0)
-            del wd, q0, s0
-        del np
-        self.sets = sets
         self.stream = int(torch.cuda.current_stream().cuda_stream)
 
     def quantize(self, i):
@@ -163,7 +213,7 @@ class StepRunner:
             raise RuntimeError(self.qw.status_string(st))
 
 
-class W8A8Runner:
+class W8A8Sets:
     """Rotating operand sets for the W8A8 path: fp16 activations quantized
     per token (the library's quantizer), int8 weight codes quantized once."""
 
@@ -203,44 +253,12 @@ class W8A8Runner:
         if st:
             raise RuntimeError(self.qw.status_string(st))
 
-
-def time_w8a8(wl, launches=40, warmup=10):
-    """Cold W8A8 figures for one workload: the GEMM alone (as
-    time_gemm_only) and per-token activation quantization followed by the
-    GEMM, each launch pair timed with events."""
-    import torch
-    r = W8A8Runner(wl, rotation_count(w8a8_bytes(wl.m, wl.n, wl.k) + act_quant_bytes(wl.m, wl.k)))
-    avg_ms, med_ms = time_gemm_only(r, launches, warmup)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(launches)]
-    torch.cuda.synchronize()
-    torch.cuda._sleep(40_000_000)
-    for it in range(launches):
-        i = it % r.sets
-        ev[it][0].record()
-        r.quantize(i)
-        ev[it][1].record()
-        r.gemm(i)
-        ev[it][2].record()
-    torch.cuda.synchronize()
-    aq_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / launches
-    pair_ms = sum(e[0].elapsed_time(e[2]) for e in ev) / launches
-    ops = gemm_flops(wl.m, wl.n, wl.k)
-    mfma = r.qw.w8a8_auto_path(wl.m, wl.n, wl.k) == "mfma"
-    tile = list(r.qw.w8a8_tile(wl.m, wl.n, wl.k)) if mfma else None
-    sets = r.sets
-    del r
-    torch.cuda.empty_cache()
-    return {"workload": wl.name, "kernel": "w8a8_mfma" if mfma else "w8a8_skinny", "mfma_tile": tile,
-            "cold_sets": sets,
-            "avg_us": avg_ms * 1e3, "median_us": med_ms * 1e3,
-            "TOPs": ops / (avg_ms * 1e-3) / 1e12,
-            "mfma_i8_frac": ops / (avg_ms * 1e-3) / 1e12 / MFMA_I8_PEAK_TOPS,
-            "TBps": w8a8_bytes(wl.m, wl.n, wl.k) / (avg_ms * 1e-3) / 1e12,
-            "act_quantize_us": aq_ms * 1e3,
-            "act_quantize_plus_gemm_us": pair_ms * 1e3}
+    def quantize_and_gemm(self, i):
+        self.quantize(i)
+        self.gemm(i)
 
 
-class OutlierRunner:
+class OutlierSets:
     """Rotating operand sets for the outlier-aware W8A16 GEMM: weights
     quantized once with side lists (the library's quantizer)."""
 
@@ -274,95 +292,241 @@ class OutlierRunner:
             raise RuntimeError(self.qw.status_string(st))
 
 
-def time_outliers(wl, launches=40, warmup=10):
+def gemm_entry(wl, avg_ms, wall_ms, mhz, sets, launches, kernel, tile=None):
+    gb, fl = gemm_bytes(wl.m, wl.n, wl.k), gemm_flops(wl.m, wl.n, wl.k)
+    return {"workload": wl.name, "kernel": kernel, "mfma_tile": tile, "cold_sets": sets, "launches": launches,
+            "avg_us": avg_ms * 1e3, "TBps": gb / (avg_ms * 1e-3) / 1e12,
+            "hbm_frac": gb / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "TFLOPs": fl / (avg_ms * 1e-3) / 1e12,
+            "mfma_frac": fl / (avg_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+            "sclk_mhz_after": mhz, "loop_wall_ms": wall_ms}
+
+
+def time_gemm(wl, launches, warmup, clock):
+    """Cold GEMM-only figures of one workload (automatic kernel choice)."""
+    import torch
+    r = GemmSets(wl, rotation_count(gemm_bytes(wl.m, wl.n, wl.k)))
+    avg, wall, mhz = timed_loop(r.gemm, r.sets, launches, warmup, clock, r.stream)
+    kname = r.qw.auto_path(wl.m, wl.n, wl.k)
+    tile = list(r.qw.mfma_tile(wl.m, wl.n, wl.k)) if kname == "mfma" else None
+    ent = gemm_entry(wl, avg, wall, mhz, r.sets, launches, kname, tile)
+    del r
+    torch.cuda.empty_cache()
+    return ent
+
+
+def time_w8a8(wl, launches, warmup, clock):
+    """Cold W8A8 figures for one workload: the GEMM alone and per-token
+    activation quantization followed by the GEMM."""
+    import torch
+    r = W8A8Sets(wl, rotation_count(w8a8_bytes(wl.m, wl.n, wl.k) + act_quant_bytes(wl.m, wl.k)))
+    avg, wall, mhz = timed_loop(r.gemm, r.sets, launches, warmup, clock, r.stream)
+    pair, _, _ = timed_loop(r.quantize_and_gemm, r.sets, launches, warmup)
+    ops = gemm_flops(wl.m, wl.n, wl.k)
+    mfma = r.qw.w8a8_auto_path(wl.m, wl.n, wl.k) == "mfma"
+    tile = list(r.qw.w8a8_tile(wl.m, wl.n, wl.k)) if mfma else None
+    sets = r.sets
+    del r
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "kernel": "w8a8_mfma" if mfma else "w8a8_skinny", "mfma_tile": tile,
+            "cold_sets": sets, "launches": launches, "avg_us": avg * 1e3,
+            "TOPs": ops / (avg * 1e-3) / 1e12,
+            "mfma_i8_frac": ops / (avg * 1e-3) / 1e12 / MFMA_I8_PEAK_TOPS,
+            "TBps": w8a8_bytes(wl.m, wl.n, wl.k) / (avg * 1e-3) / 1e12,
+            "act_quantize_plus_gemm_us": pair * 1e3, "sclk_mhz_after": mhz}
+
+
+def time_outliers(wl, launches, warmup, clock):
     """Cold figures of the outlier-aware GEMM (dense int8 part plus exact side
     lists) on one workload."""
     import torch
-    r = OutlierRunner(wl, rotation_count(gemm_bytes(wl.m, wl.n, wl.k)))
-    avg_ms, med_ms = time_gemm_only(r, launches, warmup)
+    r = OutlierSets(wl, rotation_count(gemm_bytes(wl.m, wl.n, wl.k)))
+    avg, wall, mhz = timed_loop(r.gemm, r.sets, launches, warmup, clock, r.stream)
     fl = gemm_flops(wl.m, wl.n, wl.k)
-    out = {"workload": wl.name, "kernel": gemm_kernel_name(wl.m, wl.n, wl.k) + "+outliers",
-           "slots_per_row": r.cap, "cold_sets": r.sets, "avg_us": avg_ms * 1e3, "median_us": med_ms * 1e3,
-           "TFLOPs": fl / (avg_ms * 1e-3) / 1e12,
-           "mfma_frac": fl / (avg_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS}
+    out = {"workload": wl.name, "kernel": r.qw.auto_path(wl.m, wl.n, wl.k) + "+outliers",
+           "slots_per_row": r.cap, "cold_sets": r.sets, "launches": launches, "avg_us": avg * 1e3,
+           "TFLOPs": fl / (avg * 1e-3) / 1e12,
+           "mfma_frac": fl / (avg * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, "sclk_mhz_after": mhz}
     del r
     torch.cuda.empty_cache()
     return out
 
 
-def time_full_steps(runner, steps, warmup):
-    """Warm up, then time exactly `steps` steps bracketed by synchronizations;
-    HIP events on the launch stream time each kernel inside the region."""
-    torch = runner.torch
-    for it in range(warmup):
-        runner.quantize(it % runner.sets)
-        runner.gemm(it % runner.sets)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for it in range(steps):
-        i = (warmup + it) % runner.sets
-        e = ev[it]
-        e[0].record()
-        runner.quantize(i)
-        e[1].record()
-        runner.gemm(i)
-        e[2].record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    quant_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    gemm_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    return (t1 - t0) * 1e3 / steps, sum(quant_ms) / steps, sum(gemm_ms) / steps
+def time_tuned(wl, launches, warmup, clock):
+    """Per-shape autotuning: time every kernel and tile once on the first
+    operand set, then the automatic call with the record (cold)."""
+    import torch
+    r = GemmSets(wl, rotation_count(gemm_bytes(wl.m, wl.n, wl.k)))
+    st = r.qw.w8a16_gemm_tune_raw(r.x[0].data_ptr(), r.q[0].data_ptr(), r.s[0].data_ptr(), r.y[0].data_ptr(),
+                                  wl.m, wl.n, wl.k, r.stream)
+    if st:
+        raise RuntimeError(r.qw.status_string(st))
+    avg, wall, mhz = timed_loop(r.gemm, r.sets, launches, warmup, clock, r.stream)
+    choice = r.qw.tuned_choice(wl.m, wl.n, wl.k)
+    del r
+    torch.cuda.empty_cache()
+    ent = gemm_entry(wl, avg, wall, mhz, rotation_count(gemm_bytes(wl.m, wl.n, wl.k)), launches, "tuned")
+    ent["choice"] = choice
+    return ent
 
 
-def time_gemm_only(runner, launches, warmup):
-    """Cold GEMM launches rotating over the operand sets; event pairs per launch.
-    A GPU-side sleep is queued first so that every launch is enqueued before
-    the GPU reaches it: the event pairs then see device time only, not gaps
-    left by host-side launch latency."""
-    torch = runner.torch
-    for it in range(warmup):
-        runner.gemm(it % runner.sets)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(launches)]
-    torch.cuda.synchronize()
-    torch.cuda._sleep(40_000_000)
-    for it in range(launches):
-        ev[it][0].record()
-        runner.gemm((warmup + it) % runner.sets)
-        ev[it][1].record()
-    torch.cuda.synchronize()
-    ms = sorted(a.elapsed_time(b) for a, b in ev)
-    return sum(ms) / len(ms), ms[len(ms) // 2]
+def time_full_step(wl, launches, warmup, clock):
+    """Quantize + GEMM on one workload, each kernel timed in its own
+    back-to-back loop and the pair as a loop of steps."""
+    import torch
+    sets = rotation_count(quant_bytes(wl.n, wl.k) + gemm_bytes(wl.m, wl.n, wl.k))
+    r = GemmSets(wl, sets, with_weights=True)
+
+    def step(i):
+        r.quantize(i)
+        r.gemm(i)
+    q_ms, _, _ = timed_loop(r.quantize, sets, launches, warmup)
+    s_ms, _, mhz = timed_loop(step, sets, launches, warmup, clock, r.stream)
+    del r
+    torch.cuda.empty_cache()
+    qb, gb = quant_bytes(wl.n, wl.k), gemm_bytes(wl.m, wl.n, wl.k)
+    return {"workload": wl.name, "step": "quantize + w8a16_gemm", "cold_sets": sets, "launches": launches,
+            "step_us": s_ms * 1e3, "step_TBps": (qb + gb) / (s_ms * 1e-3) / 1e12,
+            "quantize_us": q_ms * 1e3, "quantize_algorithmic_bytes": qb,
+            "quantize_TBps": qb / (q_ms * 1e-3) / 1e12, "quantize_hbm_frac": qb / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "sclk_mhz_after": mhz}
 
 
-def cpu_baseline(wl, target_s=10.0, max_s=30.0):
-    """The oracle as it stands, on the host cores, repeated over full steps of
-    the same workload until about `target_s` seconds of work."""
+def time_stream_ceiling(nbytes, launches, warmup, clock):
+    """The plain streaming-read probe over rotating buffers of `nbytes`."""
+    import torch
+
+    import int8_weight_quantized_amd as qw
+    sets = rotation_count(nbytes)
+    bufs = [torch.ones(nbytes, dtype=torch.int8, device="cuda:0") for _ in range(sets)]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    stream = int(torch.cuda.current_stream().cuda_stream)
+
+    def launch(i):
+        st = qw.probe_stream_read_raw(bufs[i].data_ptr(), nbytes, 0x5eed1234, sink.data_ptr(), stream)
+        if st:
+            raise RuntimeError(qw.status_string(st))
+    avg, wall, mhz = timed_loop(launch, sets, launches, warmup, clock, stream)
+    del bufs
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "cold_sets": sets, "launches": launches, "avg_us": avg * 1e3,
+            "TBps": nbytes / (avg * 1e-3) / 1e12, "hbm_frac": nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "sclk_mhz_after": mhz}
+
+
+# ---------------------------------------------------------------------------
+# the CPU oracle as a baseline
+# ---------------------------------------------------------------------------
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or None
+
+
+def _repeat(fn, min_s):
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= min_s:
+            return el / n, n
+
+
+def cpu_leg(threads, min_s):
+    """One leg of the CPU baseline, run in a child process whose OpenMP
+    thread count is fixed by its environment: the oracle's quantizer and
+    binary64 GEMM on (samples of) the decode, prefill and FFN workloads."""
     import oracle
     import synthetic
-    x, w = synthetic.make_inputs(wl)
     o = oracle.default()
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        q, s, _ = o.quantize(w, wl.clip_percentile)
-        o.gemm(x, q, s)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= target_s or el * (steps + 1) / steps > max_s:
-            break
-    per_step = el / steps
-    tbps = (quant_bytes(wl.n, wl.k) + gemm_bytes(wl.m, wl.n, wl.k)) / per_step / 1e12
-    return {"value": tbps, "unit": "TB/s", "cores": o.num_threads(), "kind": "oracle",
-            "sample": "%d full step(s) of %s (quantize + binary64 GEMM), %.1f s total, %.3f s/step"
-                      % (steps, wl.name, el, per_step)}
+    out = {"threads": o.num_threads(), "legs": []}
+    dec = synthetic.BY_NAME[DECODE]
+    x, w = synthetic.make_inputs(dec)
+    q, s, _ = o.quantize(w, dec.clip_percentile)
+    sec, reps = _repeat(lambda: o.quantize(w, dec.clip_percentile), min_s)
+    out["legs"].append({"what": "quantize", "workload": dec.name, "rows": dec.n, "s": sec, "reps": reps,
+                        "GBps": quant_bytes(dec.n, dec.k) / sec / 1e9})
+    sec, reps = _repeat(lambda: o.gemm(x, q, s), min_s)
+    out["legs"].append({"what": "gemm", "workload": dec.name, "m_rows": dec.m, "s": sec, "reps": reps,
+                        "TBps": gemm_bytes(dec.m, dec.n, dec.k) / sec / 1e12,
+                        "GFLOPs": gemm_flops(dec.m, dec.n, dec.k) / sec / 1e9})
+    pre = synthetic.BY_NAME[PREFILL]
+    xp, _ = synthetic.make_inputs(pre)  # same weight as decode (same seed and shape)
+    rows = 8 if threads > 1 else 1
+    sec, reps = _repeat(lambda: o.gemm(xp[:rows], q, s), min_s)
+    out["legs"].append({"what": "gemm", "workload": pre.name, "m_rows": rows, "s": sec, "reps": reps,
+                        "GFLOPs": gemm_flops(rows, pre.n, pre.k) / sec / 1e9})
+    del x, w, q, s, xp
+    ffn = synthetic.BY_NAME["transformer_big_ffn_outliers_m4096_k1024_n4096"]
+    x, w = synthetic.make_inputs(ffn)
+    q, s, _ = o.quantize(w, ffn.clip_percentile)
+    sec, reps = _repeat(lambda: o.quantize(w, ffn.clip_percentile), min_s)
+    out["legs"].append({"what": "quantize", "workload": ffn.name, "rows": ffn.n, "s": sec, "reps": reps,
+                        "GBps": quant_bytes(ffn.n, ffn.k) / sec / 1e9})
+    rows = 32 if threads > 1 else 4
+    sec, reps = _repeat(lambda: o.gemm(x[:rows], q, s), min_s)
+    out["legs"].append({"what": "gemm", "workload": ffn.name, "m_rows": rows, "s": sec, "reps": reps,
+                        "GFLOPs": gemm_flops(rows, ffn.n, ffn.k) / sec / 1e9})
+    return out
 
+
+def cpu_baseline(gpu):
+    """The oracle as it stands, timed in child processes on all host cores
+    and on one core, each leg repeated for about a second; `gpu` holds the
+    GPU figures each leg is compared with."""
+    legs = {}
+    host = os.cpu_count() or 1
+    for threads in (host, 1):
+        env = dict(os.environ)
+        env.update({"OMP_NUM_THREADS": str(threads), "OMP_PROC_BIND": "close"})
+        res = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-leg", str(threads)], env=env,
+                             capture_output=True, text=True, timeout=600, cwd=ROOT)
+        if res.returncode != 0:
+            raise RuntimeError("cpu baseline leg failed:\n" + res.stderr[-2000:])
+        legs[threads] = json.loads(res.stdout.strip().splitlines()[-1])
+    full = legs[host]
+    for leg in full["legs"] + legs[1]["legs"]:
+        g = gpu.get((leg["what"], leg["workload"]))
+        if g is None:
+            continue
+        if leg["what"] == "quantize":
+            leg["gpu_s"] = g
+            leg["gpu_speedup"] = leg["s"] / g
+        else:
+            # the CPU ran the first m_rows activation rows; scaled to the whole workload
+            leg["gpu_s"] = g
+            leg["gpu_speedup"] = leg["s"] / leg["m_rows"] * synthetic_rows(leg["workload"]) / g
+    dec = next(l for l in full["legs"] if l["what"] == "gemm" and l["workload"] == DECODE)
+    return {"value": dec["TBps"], "unit": "TB/s", "cores": full["threads"], "kind": "oracle",
+            "sample": "oracle binary64 W8A16 GEMM on the full decode workload (1 x 4096 x 27392), repeated "
+                      "for about a second; further legs below: the quantizer on the decode and FFN weights, "
+                      "the GEMM on the first rows of the prefill and FFN activations (GFLOP/s scaled by rows), "
+                      "each on all host threads and on one",
+            "host_cpus": host, "cpu_model": cpu_model(),
+            "all_cores": full, "one_core": legs[1]}
+
+
+def synthetic_rows(name):
+    import synthetic
+    return synthetic.BY_NAME[name].m
+
+
+# ---------------------------------------------------------------------------
+# other modes
+# ---------------------------------------------------------------------------
 
 def sweep_paths(ms=(1, 2, 3, 4, 8, 16, 24, 32, 48, 64, 96, 128, 256, 512),
                 shapes=((4096, 27392), (4096, 4608), (1024, 4096))):
     """Cold timing of each W8A16 and W8A8 GEMM kernel across m (random codes;
-    timing only)."""
+    timing only), round-robin over the kernels with a fresh operand set per
+    launch."""
     import torch
 
     import int8_weight_quantized_amd as qw
@@ -388,19 +552,14 @@ def sweep_paths(ms=(1, 2, 3, 4, 8, 16, 24, 32, 48, 64, 96, 128, 256, 512),
                                                       s[i].data_ptr(), y[i].data_ptr(), m, n, k, stream, path)
                 return lambda i: qw.w8a16_gemm_raw(x[i].data_ptr(), q[i].data_ptr(), s[i].data_ptr(),
                                                    y[i].data_ptr(), m, n, k, stream, path)
-            # kernels this shape supports (a forced kernel outside its limits is refused)
             runs = [(name, launcher(name, path)) for name, path in kernels]
             runs = [(name, f) for name, f in runs if f(0) == 0]
             for it in range(5):
                 for j, (_, f) in enumerate(runs):
                     f((it * len(runs) + j) % sets)
-            # round-robin: one launch of each kernel per round, so that clock
-            # and cache state after the allocations hit every kernel alike
             ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                          for _ in range(30)] for name, _ in runs}
             torch.cuda.synchronize()
-            # (every launch takes the next operand set, so none finds its
-            # operands in cache)
             for it in range(30):
                 for j, (name, f) in enumerate(runs):
                     ev[name][it][0].record()
@@ -424,21 +583,27 @@ def sweep_paths(ms=(1, 2, 3, 4, 8, 16, 24, 32, 48, 64, 96, 128, 256, 512),
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=50, help="timed decode GEMM launches (one step each)")
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="chatglm2_decode_m1_k4096_n27392")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-secondary", action="store_true", help="skip the cold GEMM-only figures")
-    ap.add_argument("--only-step", action="store_true", help="time the full steps only (for profiling)")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="only the headline decode and prefill figures and the stream ceiling")
+    ap.add_argument("--only-gemm", metavar="WORKLOAD",
+                    help="only the cold GEMM loop of one workload (--steps launches), one JSON line "
+                         "(for rocprofv3 kernel traces and counters)")
+    ap.add_argument("--only-step", action="store_true",
+                    help="only quantize + GEMM steps of the decode workload (for rocprofv3)")
+    ap.add_argument("--only-w8a8", metavar="WORKLOAD",
+                    help="only the W8A8 figures of one workload, one JSON line (for rocprofv3)")
+    ap.add_argument("--only-stream-ceiling", action="store_true",
+                    help="only the plain streaming read of the decode weight's bytes (for rocprofv3)")
     ap.add_argument("--sweep-paths", action="store_true",
-                    help="only time every GEMM kernel over a range of m (decode -> prefill "
-                         "crossover), one JSON line per (shape, m, kernel)")
-    ap.add_argument("--only-w8a8", action="store_true",
-                    help="only the W8A8 figures of --workload (per-token activation quantization + "
-                         "W8A8 GEMM, --steps launches after --warmup), one JSON line (for profiling)")
+                    help="only time every GEMM kernel over a range of m (decode -> prefill crossover), "
+                         "one JSON line per (shape, m, kernel)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="only run a plain elementwise copy of MIB MiB (fp16 negate, 5 launches) so "
-                         "that HBM counters can be scaled against a kernel of known traffic")
+                    help="only run a plain elementwise copy of MIB MiB (fp16 negate, 5 launches) so that HBM "
+                         "counters can be scaled against a kernel of known traffic")
+    ap.add_argument("--cpu-leg", type=int, default=0, metavar="THREADS", help=argparse.SUPPRESS)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -446,6 +611,10 @@ def main():
               "execution (each GPU would hold its own slice of the weight rows); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.cpu_leg:
+        print(json.dumps(cpu_leg(args.cpu_leg, 1.0)), flush=True)
+        return
 
     import torch
 
@@ -469,113 +638,102 @@ def main():
         sweep_paths()
         return
 
-    import int8_weight_quantized_amd as qw
-    wl = synthetic.BY_NAME[args.workload]
-    if args.only_w8a8:
-        print(json.dumps(time_w8a8(wl, launches=args.steps, warmup=args.warmup)), flush=True)
+    clock = Clock()
+    if args.only_gemm:
+        print(json.dumps(time_gemm(synthetic.BY_NAME[args.only_gemm], args.steps, args.warmup, clock)),
+              flush=True)
         return
-    per_set = quant_bytes(wl.n, wl.k) + gemm_bytes(wl.m, wl.n, wl.k)
-    sets = rotation_count(per_set)
-    runner = StepRunner(wl, sets, with_weights=True)
-    ms_step, q_ms, g_ms = time_full_steps(runner, args.steps, args.warmup)
+    if args.only_w8a8:
+        print(json.dumps(time_w8a8(synthetic.BY_NAME[args.only_w8a8], args.steps, args.warmup, clock)),
+              flush=True)
+        return
+    if args.only_step:
+        print(json.dumps(time_full_step(synthetic.BY_NAME[DECODE], args.steps, args.warmup, clock)), flush=True)
+        return
+    if args.only_stream_ceiling:
+        dec = synthetic.BY_NAME[DECODE]
+        print(json.dumps(time_stream_ceiling(dec.n * dec.k, args.steps, args.warmup, clock)), flush=True)
+        return
 
-    qb, gb = quant_bytes(wl.n, wl.k), gemm_bytes(wl.m, wl.n, wl.k)
-    gname = gemm_kernel_name(wl.m, wl.n, wl.k)
-    value = (qb + gb) / (ms_step * 1e-3) / 1e12
-    kernels = {
-        "quantize": {"avg_us": q_ms * 1e3, "algorithmic_bytes": qb,
-                     "achieved_GBps": qb / (q_ms * 1e-3) / 1e9},
-        gname: {"avg_us": g_ms * 1e3, "algorithmic_bytes": gb,
-                "achieved_GBps": gb / (g_ms * 1e-3) / 1e9,
-                "achieved_TFLOPs": gemm_flops(wl.m, wl.n, wl.k) / (g_ms * 1e-3) / 1e12},
-    }
-    for name, kd in kernels.items():
-        kd["hbm_frac"] = kd["achieved_GBps"] / HBM_PEAK_GBPS
-    dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
-    dk = kernels[dom]
-    traffic = measured_traffic(dom, wl.name)
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": dk["achieved_GBps"], "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": dk["achieved_GBps"] / HBM_PEAK_GBPS, "traffic": traffic,
-                "algorithmic_bytes_per_launch": dk["algorithmic_bytes"], "avg_launch_us": dk["avg_us"]}
-    del runner
-    torch.cuda.empty_cache()
+    # ---- headline: the decode GEMV, cold, K back-to-back steps ----
+    dec = synthetic.BY_NAME[DECODE]
+    head = time_gemm(dec, args.steps, args.warmup, clock)
+    print("[bench] decode gemm %.2f us, %.3f TB/s" % (head["avg_us"], head["TBps"]), file=sys.stderr, flush=True)
+    gb = gemm_bytes(dec.m, dec.n, dec.k)
+    roofline = {"bound": "hbm", "kernel": head["kernel"], "workload": dec.name,
+                "achieved": gb / (head["avg_us"] * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": gb / (head["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                "traffic": measured_traffic(head["kernel"], dec.name),
+                "algorithmic_bytes_per_launch": gb, "avg_launch_us": head["avg_us"],
+                "sclk_mhz_after": head["sclk_mhz_after"]}
+    pre = synthetic.BY_NAME[PREFILL]
+    pf = time_gemm(pre, 40, 10, clock)
+    print("[bench] prefill gemm %.2f us, %.1f TFLOP/s" % (pf["avg_us"], pf["TFLOPs"]), file=sys.stderr, flush=True)
+    roofline_prefill = {"bound": "mfma", "kernel": pf["kernel"], "mfma_tile": pf["mfma_tile"], "workload": pre.name,
+                        "achieved": pf["TFLOPs"], "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": pf["mfma_frac"], "traffic": measured_traffic(pf["kernel"], pre.name),
+                        "algorithmic_flops_per_launch": gemm_flops(pre.m, pre.n, pre.k),
+                        "algorithmic_bytes_per_launch": gemm_bytes(pre.m, pre.n, pre.k),
+                        "avg_launch_us": pf["avg_us"], "sclk_mhz_after": pf["sclk_mhz_after"]}
+    ceiling = time_stream_ceiling(dec.n * dec.k, 40, 10, clock)
+    print("[bench] stream ceiling %.2f us" % ceiling["avg_us"], file=sys.stderr, flush=True)
 
-    secondary = []
-    if not args.no_secondary and not args.only_step:
-        for other in synthetic.WORKLOADS:
-            gbytes = gemm_bytes(other.m, other.n, other.k)
-            r = StepRunner(other, rotation_count(gbytes), with_weights=False)
-            avg_ms, med_ms = time_gemm_only(r, launches=40, warmup=10)
-            fl = gemm_flops(other.m, other.n, other.k)
-            kname = gemm_kernel_name(other.m, other.n, other.k)
-            ent = {"workload": other.name, "kernel": kname, "cold_sets": r.sets,
-                   "mfma_tile": list(qw.mfma_tile(other.m, other.n, other.k)) if kname == "mfma" else None,
-                   "avg_us": avg_ms * 1e3, "median_us": med_ms * 1e3,
-                   "TBps": gbytes / (avg_ms * 1e-3) / 1e12,
-                   "hbm_frac": gbytes / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                   "TFLOPs": fl / (avg_ms * 1e-3) / 1e12,
-                   "mfma_frac": fl / (avg_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS}
-            secondary.append(ent)
-            del r
-            torch.cuda.empty_cache()
-
-    w8a8 = []
-    if not args.no_secondary and not args.only_step:
-        for name in ("small_batch_m8_k4096_n4608", "chatglm2_prefill_m512_k4096_n27392",
-                     "transformer_big_ffn_outliers_m4096_k1024_n4096"):
-            w8a8.append(time_w8a8(synthetic.BY_NAME[name]))
-
-    tuned = []
-    if not args.no_secondary and not args.only_step:
-        # per-shape autotuning: time every kernel and tile once, then the
-        # automatic call with the record (cold, as gemm_cold)
-        for name in ("small_batch_m8_k4096_n4608", "chatglm2_prefill_m512_k4096_n27392",
-                     "transformer_big_ffn_outliers_m4096_k1024_n4096"):
-            other = synthetic.BY_NAME[name]
-            gbytes = gemm_bytes(other.m, other.n, other.k)
-            r = StepRunner(other, rotation_count(gbytes), with_weights=False)
-            st = qw.w8a16_gemm_tune_raw(r.x[0].data_ptr(), r.q[0].data_ptr(), r.s[0].data_ptr(), r.y[0].data_ptr(),
-                                        other.m, other.n, other.k, r.stream)
-            if st:
-                raise RuntimeError(qw.status_string(st))
-            avg_ms, med_ms = time_gemm_only(r, launches=40, warmup=10)
-            fl = gemm_flops(other.m, other.n, other.k)
-            tuned.append({"workload": name, "choice": qw.tuned_choice(other.m, other.n, other.k),
-                          "avg_us": avg_ms * 1e3, "median_us": med_ms * 1e3,
-                          "TBps": gbytes / (avg_ms * 1e-3) / 1e12, "TFLOPs": fl / (avg_ms * 1e-3) / 1e12})
-            del r
-            torch.cuda.empty_cache()
+    secondary = {}
+    if not args.no_secondary:
+        secondary["full_step"] = time_full_step(dec, 40, 10, clock)
+        cold = []
+        for wl in synthetic.WORKLOADS:
+            if wl.name == dec.name:
+                cold.append(head)
+            elif wl.name == pre.name:
+                cold.append(pf)
+            else:
+                cold.append(time_gemm(wl, 40, 10, clock))
+        secondary["gemm_cold"] = cold
+        print("[bench] gemm_cold done", file=sys.stderr, flush=True)
+        secondary["w8a8_cold"] = [time_w8a8(synthetic.BY_NAME[n], 40, 10, clock)
+                                  for n in ("small_batch_m8_k4096_n4608", PREFILL,
+                                            "transformer_big_ffn_outliers_m4096_k1024_n4096")]
+        secondary["outliers_cold"] = [time_outliers(synthetic.BY_NAME["transformer_big_ffn_outliers_m4096_k1024_n4096"],
+                                                    40, 10, clock)]
+        import int8_weight_quantized_amd as qw
+        secondary["gemm_tuned"] = [time_tuned(synthetic.BY_NAME[n], 40, 10, clock)
+                                   for n in ("small_batch_m8_k4096_n4608", PREFILL,
+                                             "transformer_big_ffn_outliers_m4096_k1024_n4096")]
         qw.tune_reset()
-
-    outl = []
-    if not args.no_secondary and not args.only_step:
-        outl.append(time_outliers(synthetic.BY_NAME["transformer_big_ffn_outliers_m4096_k1024_n4096"]))
+        print("[bench] secondary done", file=sys.stderr, flush=True)
 
     result = {
         "metric": METRIC,
-        "value": value,
+        "value": head["TBps"],
         "unit": "TB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": head["avg_us"] * 1e-3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "m": wl.m, "n": wl.n, "k": wl.k,
-                   "clip_percentile": wl.clip_percentile, "step": "quantize + w8a16_gemm",
-                   "rotation_sets": sets, "parallelism": "none (1 GPU)"},
+        "config": {"workload": dec.name, "m": dec.m, "n": dec.n, "k": dec.k,
+                   "step": "one w8a16_gemm call (int8 codes + fp16 scales + fp16 X -> fp16 Y)",
+                   "rotation_sets": head["cold_sets"], "timing": "HIP events around K back-to-back launches",
+                   "parallelism": "none (1 GPU)"},
         "roofline": roofline,
-        "kernels": kernels,
-        "gemm_cold": secondary,
-        "w8a8_cold": w8a8,
-        "outliers_cold": outl,
-        "gemm_tuned": tuned,
+        "roofline_prefill": roofline_prefill,
+        "prefill_TFLOPs": pf["TFLOPs"],
+        "stream_ceiling": ceiling,
+        "sclk_mhz": {"after_decode_loop": head["sclk_mhz_after"], "after_prefill_loop": pf["sclk_mhz_after"]},
     }
-    if not args.no_cpu_baseline and not args.only_step:
-        result["cpu_baseline"] = cpu_baseline(wl)
+    result.update(secondary)
+    if not args.no_cpu_baseline:
+        gpu = {("quantize", dec.name): (secondary.get("full_step") or {}).get("quantize_us", 0) * 1e-6 or None,
+               ("gemm", dec.name): head["avg_us"] * 1e-6, ("gemm", pre.name): pf["avg_us"] * 1e-6}
+        for ent in secondary.get("gemm_cold", []):
+            gpu[("gemm", ent["workload"])] = ent["avg_us"] * 1e-6
+        gpu = {key: v for key, v in gpu.items() if v}
+        result["cpu_baseline"] = cpu_baseline(gpu)
     print(json.dumps(result), flush=True)
 
 

@@ -28,6 +28,8 @@
 #include "qw_device.h"
 #include "qw_internal.h"
 
+#include <algorithm>
+
 namespace qw {
 namespace {
 
@@ -219,6 +221,217 @@ hipError_t launch_cfg(const uint16_t *x, const int8_t *q, const uint16_t *scales
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Register-resident decode GEMV (m <= 2, k <= kStreamMaxChunks KiB).
+//
+// Each lane keeps its share of X in registers for the whole kernel: lane l
+// takes k = c * 1024 + 16 l + [0, 16) of every 1 KiB chunk c, the same 16
+// values that its 16-byte weight loads cover, so no LDS is touched in the
+// main loop.  The grid is 8 waves per CU (trimmed so that every wave walks
+// the same number of rows); wave w takes rows w, w + W, w + 2 W, ..., so
+// that at any moment the chip streams one compact window of rows, and keeps
+// two rows in flight: row t + 1's loads are issued before row t is
+// consumed.  That is 8 KiB in flight per wave, 64 KiB per CU, the depth
+// at which a plain streaming read of the same bytes peaks on MI355X.
+//
+// The cast's bias is folded per 16-code chunk: with h the fp16 value
+// 1152 + q that the byte permute produces, and z the row's zero point
+// (0 for symmetric weights),
+//     sum_j x_j (q_j - z) = sum_j x_j h_j - (sum_j x_j 1152 + z sum_j x_j),
+// where the sums run over the 16 codes of one load, each formed from zero
+// by the same chain of v_dot2_f32_f16; the two sums of x alone are formed
+// once per kernel from the registers of X.  That saves the two packed
+// subtractions per four codes; the chunk difference is then added to the
+// running sum.  The degenerate cases stay exact: a row of zero codes with
+// z = 0 gives two bitwise equal chains and adds +0, z = 0 adds exactly
+// nothing to the correction (so asymmetric weights with zero points of 0
+// give the symmetric result bit for bit), and with integer inputs whose
+// partial sums stay below 2^24 every step is exact.  The per-chunk chains
+// sum 16 terms of at most 1279 |x|, so their rounding stays far below the
+// fp16 rounding of Y.
+// ---------------------------------------------------------------------------
+
+constexpr int kStreamMaxChunks = 8; // k <= 8192: X takes 8 VGPRs per chunk and row
+constexpr int kStreamWavesPerCu = 8;
+
+template <int MT, int CH, bool ZP>
+__global__ __launch_bounds__(256) void gemv_stream_kernel(
+    const uint16_t *__restrict__ x, const int8_t *__restrict__ q, const uint16_t *__restrict__ scales,
+    const int8_t *__restrict__ zeros, OutlierList ol, uint16_t *__restrict__ y, int m, int n, int k, int waves)
+{
+    const int lane = __lane_id();
+    const int gw = blockIdx.x * kGemvWaves + threadIdx.x / kWave;
+    if (gw >= waves)
+        return;
+    // this lane's X: xr[mm][c][j] = x[mm][c * 1024 + 16 lane + 2 j + {0, 1}]
+    half2_t xr[MT][CH][8];
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int kk = c * kChunkK + lane * 16;
+            u32x4_t a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+            if (mm < m && kk < k) {
+                a = *reinterpret_cast<const u32x4_t *>(x + (int64_t)mm * k + kk);
+                b = *reinterpret_cast<const u32x4_t *>(x + (int64_t)mm * k + kk + 8);
+            }
+            xr[mm][c][0] = as_half2(a.x); xr[mm][c][1] = as_half2(a.y);
+            xr[mm][c][2] = as_half2(a.z); xr[mm][c][3] = as_half2(a.w);
+            xr[mm][c][4] = as_half2(b.x); xr[mm][c][5] = as_half2(b.y);
+            xr[mm][c][6] = as_half2(b.z); xr[mm][c][7] = as_half2(b.w);
+        }
+    }
+    // the bias chains sum_j x_j 1152 of each chunk, and (ZP) the sums of x
+    float corr[MT][CH], sx[MT][CH];
+    {
+        const half2_t b = (half2_t){(_Float16)1152.0f, (_Float16)1152.0f};
+        const half2_t one = (half2_t){(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                float a = 0.0f, e = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    a = dot2(b, xr[mm][c][j], a);
+                    if constexpr (ZP)
+                        e = dot2(one, xr[mm][c][j], e);
+                }
+                corr[mm][c] = a;
+                sx[mm][c] = e;
+            }
+    }
+    constexpr int R = MT; // partial sums per row: one per activation row
+    const int rows = (n - 1 - gw) / waves + 1;
+    const int mine = butterfly_index<R>(lane); // the activation row this lane writes (R > 1)
+    // a row in flight: its codes, and its scale and zero point (loaded with
+    // the codes, so that the epilogue does not wait for another load)
+    struct Row {
+        u32x4_t w[CH];
+        uint16_t s;
+        int8_t z;
+    };
+    // Lanes past the end of a ragged last chunk load the row's last 16
+    // codes instead (a valid address, no branch around the load); their X is
+    // zero, so those codes add exactly zero to both chains.
+    int koff[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+        koff[c] = min(c * kChunkK + lane * 16, k - 16);
+    auto issue = [&](int t, Row &b) {
+        const int8_t *qr = q + (gw + (int64_t)t * waves) * k;
+        const int64_t row = gw + (int64_t)t * waves;
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+            b.w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(qr + koff[c]));
+        b.s = scales[row];
+        b.z = ZP ? zeros[row] : (int8_t)0;
+    };
+    auto consume = [&](int t, const Row &b) {
+        const int64_t row = gw + (int64_t)t * waves;
+        float acc[R];
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm)
+            acc[mm] = 0.0f;
+        const float zf = (float)b.z;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            // the byte permute of i8x4_to_half2x2 without its subtraction:
+            // hw holds 1152 + q exactly
+            half2_t hw[8];
+            const uint32_t wv[4] = {b.w[c].x, b.w[c].y, b.w[c].z, b.w[c].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t u = wv[e] ^ 0x80808080u;
+                hw[2 * e] = as_half2(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u));
+                hw[2 * e + 1] = as_half2(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u));
+            }
+#pragma unroll
+            for (int mm = 0; mm < MT; ++mm) {
+                float a = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    a = dot2(hw[j], xr[mm][c][j], a);
+                const float cb = ZP ? corr[mm][c] + zf * sx[mm][c] : corr[mm][c];
+                acc[mm] += a - cb;
+            }
+        }
+        butterfly_reduce<R>(acc);
+        if ((lane & (kWave / R - 1)) == 0 && mine < m) {
+            float out = acc[0] * f16_bits_to_f32(b.s);
+            // exact outliers of this row, with X read from global memory
+            if (ol.idx != nullptr) {
+                for (int e = 0; e < ol.cap; ++e) {
+                    const int kk = ol.idx[row * ol.cap + e];
+                    if (kk < 0 || kk >= k)
+                        break; // used slots come first
+                    out += f16_bits_to_f32(x[(int64_t)mine * k + kk]) * ol.val[row * ol.cap + e];
+                }
+            }
+            y[(int64_t)mine * n + row] = f32_to_f16_bits(out);
+        }
+    };
+    // two rows in flight: row t + 1's loads go out before row t is consumed.
+    // The steady loop is unrolled by two (each buffer a fixed register set)
+    // and issues unconditionally, so that the compiler can count the loads in
+    // flight and waits only for the row it consumes; the last one or two
+    // rows are handled after it.
+    // (A scheduling barrier after each issue keeps the compiler from sinking
+    // the next row's loads below the start of the current row's arithmetic.)
+    Row b0, b1;
+    issue(0, b0);
+    int t = 0;
+    for (; t + 2 < rows; t += 2) {
+        issue(t + 1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(t, b0);
+        issue(t + 2, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(t + 1, b1);
+    }
+    if (t + 1 < rows) {
+        issue(t + 1, b1);
+        consume(t, b0);
+        consume(t + 1, b1);
+    } else {
+        consume(t, b0);
+    }
+}
+
+template <int MT, int CH>
+hipError_t launch_stream(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros,
+                         OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
+{
+    // about 8 waves per CU, trimmed so that every wave walks the same number of rows
+    int64_t waves = std::min<int64_t>(n, (int64_t)device_cu_count() * kStreamWavesPerCu);
+    const int64_t per = (n + waves - 1) / waves;
+    waves = (n + per - 1) / per;
+    const int blocks = (int)((waves + kGemvWaves - 1) / kGemvWaves);
+    if (zeros == nullptr)
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, CH, false>), dim3(blocks), dim3(kGemvThreads), 0, stream, x, q,
+                           scales, zeros, ol, y, (int)m, (int)n, (int)k, (int)waves);
+    else
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, CH, true>), dim3(blocks), dim3(kGemvThreads), 0, stream, x, q,
+                           scales, zeros, ol, y, (int)m, (int)n, (int)k, (int)waves);
+    return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_stream_chunks(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros,
+                                OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
+{
+    switch ((k + kChunkK - 1) / kChunkK) {
+    case 1: return launch_stream<MT, 1>(x, q, scales, zeros, ol, y, m, n, k, stream);
+    case 2: return launch_stream<MT, 2>(x, q, scales, zeros, ol, y, m, n, k, stream);
+    case 3: return launch_stream<MT, 3>(x, q, scales, zeros, ol, y, m, n, k, stream);
+    case 4: return launch_stream<MT, 4>(x, q, scales, zeros, ol, y, m, n, k, stream);
+    case 5: return launch_stream<MT, 5>(x, q, scales, zeros, ol, y, m, n, k, stream);
+    case 6: return launch_stream<MT, 6>(x, q, scales, zeros, ol, y, m, n, k, stream);
+    case 7: return launch_stream<MT, 7>(x, q, scales, zeros, ol, y, m, n, k, stream);
+    default: return launch_stream<MT, 8>(x, q, scales, zeros, ol, y, m, n, k, stream);
+    }
+}
+
 } // namespace
 
 bool gemv_supported(int64_t m, int64_t k)
@@ -236,8 +449,13 @@ hipError_t launch_gemv(const uint16_t *x, const int8_t *q, const uint16_t *scale
                        OutlierList ol, uint16_t *y,
                        int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
-    // (MT, RU, CH, waves per CU) from measured sweeps; WPC stays within what
-    // each configuration's register use lets a CU hold at once
+    // decode: one or two activation rows held in registers
+    if (m <= 2 && (k + kChunkK - 1) / kChunkK <= kStreamMaxChunks)
+        return m <= 1 ? launch_stream_chunks<1>(x, q, scales, zeros, ol, y, m, n, k, stream)
+                      : launch_stream_chunks<2>(x, q, scales, zeros, ol, y, m, n, k, stream);
+    // otherwise X is staged in LDS; (MT, RU, CH, waves per CU) from measured
+    // sweeps; WPC stays within what each configuration's register use lets a
+    // CU hold at once
     if (m <= 1)
         return launch_cfg<1, 2, 4, 28>(x, q, scales, zeros, ol, y, m, n, k, stream);
     if (m <= 2)
