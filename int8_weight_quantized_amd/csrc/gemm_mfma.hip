@@ -173,7 +173,7 @@ using stage_t = std::integral_constant<int, I>;
 // sx; the MFMA is v_mfma_i32_32x32x32_i8 with exact int32 accumulators and
 // the epilogue multiplies by S[n] * Sx[m].  Otherwise x is fp16 and sx is
 // unused.  OL: exact outlier side lists (at most kMfmaOutlierSlots per
-// weight row) are added while their activation column sits in LDS.
+// weight row) are added to the accumulators after the main loop.
 template <int NW, int BN, int BM, bool A8, bool OL = false, bool ZP = false>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm_dma_kernel(
@@ -410,7 +410,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
     // all of them live at once.  The 128-channel tiles measured slower with
     // spread copies (3% on 128 x 128, 11% on 128 x 64) and keep them at the
     // top of the step.
-    constexpr bool kSpreadTile = !A8 && !OL && BN == 256;
+    constexpr bool kSpreadTile = !A8 && BN == 256;
 
     // before_group(s) runs ahead of MFMA group s = 0..3 of the fp16 path
     auto compute = [&](const uint8_t *st, auto &&before_group) {
@@ -482,65 +482,6 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
             ol_lds[e] = (int2v){col, __builtin_bit_cast(int, o)};
         }
     }
-    // lane l < kWaveN walks the side list of its wave's channel l in column
-    // order; ocur is its next slot
-    int ocur = 0;
-
-    // Add x[row][col] * o for each outlier (channel c of this wave, column
-    // col) of the current k step to the accumulators of every activation row
-    // of the tile.  Channel c's accumulator is register
-    // R = 4 ((c % 32) / 8) + c % 4 of MFMA tile I = c / 32 in the lanes whose
-    // group l / 32 is (c % 8) / 4, one row 32 j + l % 32 per tile row j.  So
-    // that every register index is a compile-time constant, the (I, R) pairs
-    // with a hit are collected in a wave-uniform mask and visited in a fixed
-    // unrolled order; in pair (I, R) each lane fetches its half's channel's
-    // entry from the owning lane.
-    auto add_outliers = [&](int t, const uint8_t *st) __attribute__((always_inline)) {
-        const int kend = (t + 1) * kBK; // every slot still ahead has column >= t * kBK
-        const bool own = lane < C::kWaveN;
-        const int cl = wave * C::kWaveN + lane;
-        for (;;) {
-            int2v ent = {0x7fffffff, 0};
-            if (own && ocur < kMfmaOutlierSlots)
-                ent = ol_lds[cl * kMfmaOutlierSlots + ocur];
-            const bool hit = ent.x < kend;
-            const uint64_t hits = __builtin_amdgcn_ballot_w64(hit);
-            if (hits == 0)
-                break;
-            uint32_t pairs = 0;
-            for (uint64_t rest = hits; rest != 0; rest &= rest - 1) {
-                const int c = __builtin_ctzll(rest);
-                pairs |= 1u << ((c / 32) * 16 + 4 * ((c % 32) / 8) + c % 4);
-            }
-            // lane-dependent part of the source lane, made opaque here so that
-            // the per-pair arithmetic is not hoisted out of the loop (32 live
-            // values would not fit beside the accumulators)
-            int half4 = 4 * lgrp;
-            __asm__ volatile("" : "+v"(half4));
-            static_for<0, C::kSI * 16>([&](auto G) {
-                constexpr int kI = decltype(G)::value / 16, kR = decltype(G)::value % 16;
-                if (pairs & (1u << decltype(G)::value)) {
-                    const int src = half4 + (32 * kI + 8 * (kR / 4) + kR % 4);
-                    const int col = __builtin_amdgcn_ds_bpermute(src * 4, ent.x) - t * kBK;
-                    const float o = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src * 4, ent.y));
-                    // (col < 0 only for a list out of column order: skipped,
-                    // never read outside the stage)
-                    if (((hits >> src) & 1u) && col >= 0) {
-#pragma unroll
-                        for (int j = 0; j < kSJ; ++j) {
-                            const int xr = 32 * j + lrow;
-                            const uint8_t *px = st + C::kWBytes + xr * 2 * kBK +
-                                                16 * ((col / 8) ^ (half4 >= 0 ? xslot(xr) : 0)) + 2 * (col % 8);
-                            acc[kI][j][kR] += (float)*reinterpret_cast<const _Float16 *>(px) * o;
-                        }
-                    }
-                }
-            });
-            if (hit)
-                ++ocur;
-        }
-    };
-
     // Step t (stage t % 2) waits for its own copies of tile t, the barrier
     // publishes everyone's copies and certifies that tile t-1's stage is no
     // longer read, tile t + 1 is copied into that stage while tile t is
@@ -563,11 +504,6 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
                 issue(t + 1, ring(stage_t<1 - S>{}), full);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // outliers before this step's MFMAs: their adds then depend only on
-        // the previous step's MFMAs, long finished (after them, each add
-        // would wait for this step's whole MFMA chain on its accumulator)
-        if constexpr (OL)
-            add_outliers(t, ring(s));
         compute(ring(s), [&](int g) __attribute__((always_inline)) {
             if constexpr (kSpread) {
                 issue_group(t + 1, ring(stage_t<1 - S>{}), g);
@@ -602,6 +538,66 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
     // 16-byte pieces, so every wave writes whole 512-byte row segments of Y
     // instead of scattered 8-byte pieces of 32 rows.
     ring_barrier(); // every wave is done reading the ring
+
+    // OL: the side lists, one slot at a time.  The workgroup first gathers
+    // G[c][r] = x[m0 + r][column of channel c's entry] for all of its
+    // channels and activation rows into the free stage arrays (threads walk
+    // the channels of one activation row, so a wave reads one row of X),
+    // then every lane adds G * (value / S) to the accumulators it holds.
+    // Unused entries have value 0 and gather a zero.
+    if constexpr (OL) {
+        constexpr int kGRow = BM + 2; // halves per channel row of G (padded: no bank conflicts)
+        static_assert((BN / 2) * kGRow * 2 <= C::kStageAlloc, "G fits the stage arrays");
+        auto gaddr = [&](int c, int r) -> _Float16 * {
+            uint8_t *base = c < BN / 2 ? ring0 : ring1;
+            return reinterpret_cast<_Float16 *>(base) + (c % (BN / 2)) * kGRow + r;
+        };
+        // Thread tid gathers channel tid % BN for rows tid / BN + i * kRStep.
+        // The loads go out in batches of up to 32 (each a valid address:
+        // entries without an outlier, and rows past m, load x[0][0] and keep
+        // zero), so that their latencies overlap.
+        static_assert(C::kThreads % BN == 0, "one channel per thread");
+        constexpr int kRStep = C::kThreads / BN;
+        constexpr int kPer = BM / kRStep;
+        constexpr int kBatch = kPer < 32 ? kPer : 32;
+        static_assert(kPer % kBatch == 0, "whole batches");
+        const int gc = tid % BN, gr0 = tid / BN;
+        const int slots = min(ol.cap, kMfmaOutlierSlots);
+        for (int sl = 0; sl < slots; ++sl) {
+            const int col = ol_lds[gc * kMfmaOutlierSlots + sl].x;
+            const bool live = col != 0x7fffffff;
+            for (int b0 = 0; b0 < kPer; b0 += kBatch) {
+                uint16_t v[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int r = gr0 + (b0 + u) * kRStep;
+                    const bool ok = live && m0 + r < m;
+                    v[u] = x[ok ? (int64_t)(m0 + r) * k + col : 0];
+                    v[u] = ok ? v[u] : (uint16_t)0;
+                }
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u)
+                    *gaddr(gc, gr0 + (b0 + u) * kRStep) = __builtin_bit_cast(_Float16, v[u]);
+            }
+            ring_barrier();
+#pragma unroll
+            for (int i = 0; i < C::kSI; ++i) {
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int c = wave * C::kWaveN + i * 32 + 8 * (rr / 4) + 4 * lgrp + rr % 4;
+                    // (the component is copied out first: a bit cast applied to
+                    // an ext-vector component in place reads component 0)
+                    const int obits = ol_lds[c * kMfmaOutlierSlots + sl].y;
+                    const float o = __builtin_bit_cast(float, obits);
+#pragma unroll
+                    for (int j = 0; j < kSJ; ++j)
+                        acc[i][j][rr] += (float)*gaddr(c, j * 32 + lrow) * o;
+                }
+            }
+            ring_barrier();
+        }
+    }
+
 #pragma unroll
     for (int i = 0; i < C::kSI; ++i) {
 #pragma unroll
@@ -692,9 +688,7 @@ hipError_t launch_dma(const void *x, const uint16_t *sx, const int8_t *q, const 
     if (blocks > 0x7fffffff)
         return hipErrorInvalidConfiguration;
     const int group = group_width<BN, BM, A8>(blocks, tiles_m, tiles_n);
-    // side lists: not with the 256 x 128 tile (its registers are nearly all
-    // taken by accumulators and operands; the launcher maps it to 256 x 64)
-    if constexpr (!A8 && !(BN == 256 && BM == 128)) {
+    if constexpr (!A8) {
         if (ol.idx != nullptr) {
             if (ol.cap > kMfmaOutlierSlots)
                 return hipErrorInvalidValue;
@@ -779,9 +773,7 @@ hipError_t launch_tiles(const void *x, const uint16_t *sx, const int8_t *q, cons
 {
     if (k > kMfmaMaxK) // the entry points route such rows elsewhere
         return hipErrorInvalidValue;
-    int tile = forced_tile != 0 ? forced_tile : tile_choice<A8>(m, n);
-    if (ol.idx != nullptr && tile == 256128)
-        tile = 256064;
+    const int tile = forced_tile != 0 ? forced_tile : tile_choice<A8>(m, n);
     switch (tile) {
     case 256128:
         return launch_dma<4, 256, 128, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);

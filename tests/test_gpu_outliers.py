@@ -175,11 +175,12 @@ def test_outlier_workload_end_to_end():
     assert np.array_equal(val, v_ref)
     say("gemm outliers %s" % wl.name)
     y = gpu_gemm_outliers(x, q, s, idx, val)
+    # every output against the binary64 oracle
+    assert_gemm_close(y, oracle.gemm_outliers(x, q, s, idx, val), "ffn outliers")
     rng = np.random.default_rng(7)
     mi = np.concatenate([np.repeat([0, 777, 4095], wl.n), rng.integers(0, wl.m, 8192)])
     ni = np.concatenate([np.tile(np.arange(wl.n), 3), rng.integers(0, wl.n, 8192)])
-    assert_gemm_close(y[mi, ni], oracle.gemm_outliers_sampled(x, q, s, idx, val, mi, ni), "ffn outliers (sampled)")
-    # against the unquantized product on the sampled outputs
+    # against the unquantized product on sampled outputs
     exact = np.einsum("ck,ck->c", x[mi].astype(np.float64), w[ni].astype(np.float64))
     qc, sc, _ = oracle.quantize(w, wl.clip_percentile)
     clipped = oracle.gemm_sampled(x, qc, sc, mi, ni)

@@ -7,9 +7,9 @@ seeded host buffers.
     the exact-arithmetic case must be bit-exact.
 
 Full workload sizes run in the launch configuration the benchmark times
-(the automatic kernel choice); where the binary64 reference is too slow to
-compute in full, whole output rows, whole output columns and scattered
-points are sampled and computed one by one.
+(the automatic kernel choice), every output compared; forced-path sweeps
+over other shapes compare whole output rows, whole output columns and
+scattered points, computed one by one.
 """
 
 import functools
@@ -63,17 +63,15 @@ def _sample_indices(m, n, rng, rows=6, cols=6, points=4096):
 
 @pytest.mark.parametrize("name", NAMES)
 def test_gemm_workload(name):
+    """Every workload at full size through the automatic kernel choice (the
+    launch configuration the benchmark times), every output compared with
+    the binary64 oracle (the prefill one is about 10^11 multiply-adds on
+    the host's OpenMP threads)."""
     wl, x, w, q, s = workload_data(name)
     say("gemm auto %s m=%d n=%d k=%d" % (name, wl.m, wl.n, wl.k))
     y = gpu_gemm(x, q, s)
-    if wl.m * wl.n * wl.k <= 4e8:
-        ref = oracle.gemm(x, q, s)
-        assert_gemm_close(y, ref, name)
-    else:
-        mi, ni = _sample_indices(wl.m, wl.n, np.random.default_rng(123))
-        ref = oracle.gemm_sampled(x, q, s, mi, ni)
-        assert_gemm_close(y[mi, ni], ref, name + " (sampled)")
-        assert np.all(np.isfinite(y.astype(np.float32))), "non-finite output outside the sample"
+    ref = oracle.gemm(x, q, s)
+    assert_gemm_close(y, ref, name)
 
 
 # Shapes that between them land on every MFMA tile shape (the choice depends
