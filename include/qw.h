@@ -205,8 +205,8 @@ QW_API qw_status qw_quantize_weights_outliers(const float *w, int64_t n, int64_t
  * over the used slots, in fp32 (the GOBO reading above: the dense int8
  * part plus the full-precision outliers).  The GEMV and skinny kernels add
  * the side list in their epilogues; the MFMA kernel adds it (in units of
- * S[c], value / S[c] in binary32) while the activation columns pass through
- * LDS, for up to 4 slots per row (wider lists run on the skinny kernel, and
+ * S[c], value / S[c] in binary32) to its accumulators after the main loop,
+ * for up to 4 slots per row (wider lists run on the skinny kernel, and
  * QW_PATH_MFMA with more than 4 slots is QW_ERROR_UNSUPPORTED).  Accuracy
  * contract as qw_w8a16_gemm.
  *
@@ -275,7 +275,12 @@ QW_API qw_status qw_quantize_weights_asym(const float *w, int64_t n, int64_t k, 
  * binary32 (fp32 accumulation); the per-channel scale is applied to the
  * fp32 sum (algebraically the same as scaling each weight first, with less
  * rounding), and the MFMA kernels round that product to binary16 in one
- * fused step (a zero product is written as +0).  Accuracy contract:
+ * fused step (a zero product is written as +0).  The decode GEMV (one or
+ * two activation rows, k <= 8192) sums each 16-code chunk as
+ * sum x (1152 + q) - sum x 1152 (the cast's bias subtracted once per chunk
+ * instead of per code), both chains formed exactly in the same order, so a
+ * row of zero codes still sums to +0 and integer inputs whose partial sums
+ * stay below 2^24 are still exact.  Accuracy contract:
  * max |Y - exact| <= 2e-3 * max|exact| + 1e-3.
  *
  *   x       fp16 bits [m][k]
@@ -306,7 +311,7 @@ QW_API qw_status qw_w8a16_gemm(const uint16_t *x, const int8_t *q,
 /* Kernel selection for qw_w8a16_gemm_path. */
 typedef enum qw_gemm_path {
     QW_PATH_AUTO = 0,   /* what qw_w8a16_gemm does */
-    QW_PATH_GEMV = 1,   /* VALU dot products, weights streamed once (m <= 8) */
+    QW_PATH_GEMV = 1,   /* VALU dot products, weights streamed once (m <= 8; X in registers for m <= 2) */
     QW_PATH_MFMA = 2,   /* MFMA tiled GEMM, int8 tiles dequantized into LDS */
     QW_PATH_SKINNY = 3  /* MFMA on weights dequantized in registers, 16 (or 32) activation rows per pass */
 } qw_gemm_path;

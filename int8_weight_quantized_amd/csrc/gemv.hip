@@ -449,7 +449,10 @@ hipError_t launch_gemv(const uint16_t *x, const int8_t *q, const uint16_t *scale
                        OutlierList ol, uint16_t *y,
                        int64_t m, int64_t n, int64_t k, hipStream_t stream)
 {
-    // decode: one or two activation rows held in registers
+    // decode: one or two activation rows held in registers.  (Four rows
+    // measured 1.4-4x slower than the skinny kernel: the dot products per
+    // weight byte grow with the rows and the VALU, not the stream, sets the
+    // time.)
     if (m <= 2 && (k + kChunkK - 1) / kChunkK <= kStreamMaxChunks)
         return m <= 1 ? launch_stream_chunks<1>(x, q, scales, zeros, ol, y, m, n, k, stream)
                       : launch_stream_chunks<2>(x, q, scales, zeros, ol, y, m, n, k, stream);
