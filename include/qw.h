@@ -363,15 +363,47 @@ QW_API int qw_w8a16_gemm_auto_path(int64_t m, int64_t n, int64_t k);
 /*
  * qw_w8a16_gemm_mfma_tile -- the output tile QW_PATH_MFMA uses for this
  * shape on the current HIP device, encoded BN * 1000 + BM (BN output
- * channels x BM activation rows per workgroup: 256128, 256064, 128128 or
- * 128064), for benchmarks, logs and tests.  The choice depends on the
- * device's CU count and the kernels' occupancy (queried once per device):
- * the largest tile whose grid fills three quarters of the workgroups the
- * chip holds at once, else 128 x 64.  Returns -1 for shapes the GEMM
- * rejects (m, n <= 0, k <= 0, k % 16 != 0, a size beyond INT32_MAX) or
- * when no HIP device is current.
+ * channels x BM activation rows per workgroup: 256256, 256128, 256064,
+ * 128128 or 128064), for benchmarks, logs and tests.  256256 is the
+ * 8-wave ping-pong kernel (one workgroup per CU, two wave groups that take
+ * turns at the matrix cores), chosen where its grid covers at least half
+ * the device's CUs, rounding m up to 256 rows adds at most 10% over
+ * rounding it to 64, and k <= QW_PINGPONG_MAX_K (calls with outlier side
+ * lists keep the 4-wave tiles unless the tile is forced).  Otherwise the choice
+ * depends on the device's CU count and the 4-wave kernels' occupancy
+ * (queried once per device): the largest tile whose grid fills three
+ * quarters of the workgroups the chip holds at once, else 128 x 64.
+ * Returns -1 for shapes the GEMM rejects (m, n <= 0, k <= 0, k % 16 != 0,
+ * a size beyond INT32_MAX) or when no HIP device is current.
  */
 QW_API int qw_w8a16_gemm_mfma_tile(int64_t m, int64_t n, int64_t k);
+
+/* Longest reduction the 256 x 256 ping-pong tile takes (its 256-row
+ * activation tile spans 256 * k * 2 bytes of one 32-bit buffer range). */
+#define QW_PINGPONG_MAX_K 4194304
+
+/*
+ * qw_w8a16_gemm_tile -- the MFMA GEMM (QW_PATH_MFMA) with a given output
+ * tile, for tests, benchmarks and callers that pin the kernel per shape.
+ * Computes what qw_w8a16_gemm (zeros and ol_idx null), qw_w8a16_gemm_asym
+ * (zeros non-null) or qw_w8a16_gemm_outliers (cap > 0) computes, with the
+ * same contracts.
+ *
+ *   x, q, scales, y, m, n, k, stream   as qw_w8a16_gemm
+ *   zeros   int8 [n] zero points, or null for symmetric codes
+ *   ol_idx, ol_val, cap   side lists as qw_w8a16_gemm_outliers (cap 0:
+ *           none, and then both pointers may be null)
+ *   tile    256256, 256128, 256064, 128128 or 128064 (BN * 1000 + BM)
+ *
+ * Errors: as the matching entry point with QW_PATH_MFMA forced, plus
+ * QW_ERROR_INVALID_VALUE for any other tile, or for zeros with cap > 0
+ * (side lists belong to symmetric codes), and QW_ERROR_UNSUPPORTED for
+ * tile 256256 with k > QW_PINGPONG_MAX_K.
+ */
+QW_API qw_status qw_w8a16_gemm_tile(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                                    const int8_t *zeros, const int32_t *ol_idx, const float *ol_val,
+                                    int64_t cap, uint16_t *y, int64_t m, int64_t n, int64_t k, int tile,
+                                    void *stream);
 
 /*
  * qw_w8a16_gemm_tune -- per-shape autotuning of the W8A16 kernel choice.
@@ -382,7 +414,8 @@ QW_API int qw_w8a16_gemm_mfma_tile(int64_t m, int64_t n, int64_t k);
  * automatically; LightSeq deck, TVM part: per-shape parameter search with
  * the token count padded to a multiple of 8.  This call runs every
  * candidate (the GEMV when m and k allow it, the skinny kernel, and the
- * MFMA kernel with each of its four tiles) on the given buffers and
+ * MFMA kernel with each of its five tiles, the ping-pong tile only for
+ * k <= QW_PINGPONG_MAX_K) on the given buffers and
  * stream, times each with HIP events (two untimed rounds, then seven rounds
  * of one launch per candidate; the median decides), and records the
  * fastest for the bucket (current device, n, k,

@@ -37,6 +37,8 @@ QW_ERROR_LAUNCH = 4
 PATHS = {"auto": 0, "gemv": 1, "mfma": 2, "skinny": 3}
 QUANTIZE_MAX_K = 65536
 MFMA_MAX_K = 8388608     # longest reduction of the LDS-tiled MFMA kernel
+PINGPONG_MAX_K = 4194304  # longest reduction of the 256 x 256 ping-pong tile
+MFMA_TILES = ((256, 256), (256, 128), (256, 64), (128, 128), (128, 64))  # (BN, BM)
 W8A8_MAX_K = 131072
 
 
@@ -90,6 +92,8 @@ def _load():
     lib.qw_w8a16_gemm_outliers.restype = ctypes.c_int
     lib.qw_w8a16_gemm_outliers_path.argtypes = [vp, vp, vp, vp, vp, i64, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.qw_w8a16_gemm_outliers_path.restype = ctypes.c_int
+    lib.qw_w8a16_gemm_tile.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.qw_w8a16_gemm_tile.restype = ctypes.c_int
     lib.qw_quantize_weights_asym.argtypes = [vp, i64, i64, vp, vp, vp, vp]
     lib.qw_quantize_weights_asym.restype = ctypes.c_int
     lib.qw_w8a16_gemm_asym.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
@@ -249,6 +253,12 @@ def w8a16_gemm_outliers_raw(x_ptr: int, q_ptr: int, s_ptr: int, idx_ptr: int, va
                             m: int, n: int, k: int, stream: int = 0, path: int = 0) -> int:
     return int(library().qw_w8a16_gemm_outliers_path(x_ptr, q_ptr, s_ptr, idx_ptr, val_ptr, cap, y_ptr, m, n, k,
                                                      int(path), stream))
+
+
+def w8a16_gemm_tile_raw(x_ptr: int, q_ptr: int, s_ptr: int, z_ptr: int, idx_ptr: int, val_ptr: int, cap: int,
+                        y_ptr: int, m: int, n: int, k: int, tile: int, stream: int = 0) -> int:
+    return int(library().qw_w8a16_gemm_tile(x_ptr, q_ptr, s_ptr, z_ptr, idx_ptr, val_ptr, cap, y_ptr, m, n, k,
+                                            int(tile), stream))
 
 
 def quantize_weights_asym_raw(w_ptr: int, n: int, k: int, q_ptr: int, s_ptr: int, z_ptr: int,
@@ -466,6 +476,26 @@ def w8a16_gemm_outliers(x, q, scales, ol_idx, ol_val, out=None, path: str = "aut
                                  ol_val.data_ptr(), cap, y.data_ptr(), m, n, k, _stream_of(x), PATHS[path])
     if st != QW_SUCCESS:
         raise QwError(st, "qw_w8a16_gemm_outliers")
+    return y
+
+
+def w8a16_gemm_tile(x, q, scales, tile, zeros=None, outliers=None, out=None):
+    """The MFMA GEMM with a given output tile (BN, BM), one of MFMA_TILES:
+    what w8a16_gemm (no zeros, no outliers), w8a16_gemm_asym (zeros int8
+    [N]) or w8a16_gemm_outliers (outliers = (ol_idx, ol_val)) computes."""
+    if tuple(tile) not in MFMA_TILES:
+        raise ValueError("tile must be one of %s, got %r" % (MFMA_TILES, tile))
+    if zeros is not None and outliers is not None:
+        raise ValueError("outlier side lists belong to symmetric codes: pass zeros or outliers, not both")
+    device = _require_gpu(x, "x")
+    m, n, k, cap, y = _validate_gemm(x, q, scales, out, None, device, zeros=zeros, ol=outliers)
+    idx_ptr = outliers[0].data_ptr() if outliers is not None else None
+    val_ptr = outliers[1].data_ptr() if outliers is not None else None
+    st = w8a16_gemm_tile_raw(x.data_ptr(), q.data_ptr(), scales.data_ptr(),
+                             zeros.data_ptr() if zeros is not None else None, idx_ptr, val_ptr, cap,
+                             y.data_ptr(), m, n, k, tile[0] * 1000 + tile[1], _stream_of(x))
+    if st != QW_SUCCESS:
+        raise QwError(st, "qw_w8a16_gemm_tile")
     return y
 
 

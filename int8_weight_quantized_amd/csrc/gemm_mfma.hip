@@ -649,6 +649,441 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 && BM > 128 ? 1 : 2))) void mfma_gemm
     }
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong variant for grids of 256 x 256 tiles: 8 waves per workgroup,
+// two per SIMD, in two groups of four (one wave per SIMD each).  Group 0
+// computes activation rows [0, 128) of the tile, group 1 rows [128, 256);
+// wave w % 4 of either group owns output channels [64 (w % 4), +64), so a
+// wave's share of a k step is the same 64 x 128 block (8 MFMA tiles of
+// 32 x 32, 32 MFMAs) as in the 4-wave kernel above.
+//
+// The two groups run half a k step apart, separated by workgroup barriers:
+// while one group's waves issue their MFMAs back to back (registers only),
+// the other group's waves read their operands of the next k step from LDS
+// and issue their share of the copies of a later tile.  Each SIMD thus
+// holds one wave in an MFMA run and one wave in a memory phase at any time,
+// instead of two waves that contend for the same units.  Phases (p):
+//
+//   group 0: p = 2t     read tile t from LDS, copy tile t + 2 (its half)
+//            p = 2t + 1 MFMAs of tile t
+//   group 1: p = 2t + 1 read tile t from LDS, copy tile t + 2 (its half)
+//            p = 2t + 2 MFMAs of tile t
+//
+// Every wave executes the same number of barriers: 2T over the k loop of
+// T tiles, then three in the epilogue.  Three LDS stages (48 KiB each) hold
+// tiles t, t + 1 and t + 2: the stage tile t + 2 goes into held tile t - 1,
+// which group 1 read in phase 2t - 1, before the barrier that opens phase
+// 2t.  A wave's copies of tile u are waited for at the end of phase 2u - 1
+// (its own wait counter, then the barrier): they were issued in phase
+// 2u - 4 or 2u - 3, so their latency hides behind two to three phases.
+// ---------------------------------------------------------------------------
+namespace pp {
+constexpr int kBN = 256;                          // output channels per workgroup
+constexpr int kBM = 256;                          // activation rows per workgroup
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kWBytes = kBN * kBK;                // int8 weight tile per stage
+constexpr int kXBytes = kBM * kBK * 2;            // fp16 activation tile per stage
+constexpr int kStage = kWBytes + kXBytes;
+constexpr int kWInstr = kWBytes / 1024 / kWaves;  // copies per wave per tile
+constexpr int kXInstr = kXBytes / 1024 / kWaves;
+constexpr int kCopies = kWInstr + kXInstr;
+constexpr int kSI = 2;                            // 32-channel MFMA tiles per wave
+constexpr int kSJ = 4;                            // 32-row MFMA tiles per wave
+constexpr int kGroupRows = kSJ * 32;              // activation rows per group
+// epilogue image of one group's rows, [128][256] fp16 with rows padded by
+// 16 bytes; rows [0, 64) in stage 0's array, [64, 128) in stage 1's
+constexpr int kYRow = kBN * 2 + 16;
+static_assert(kWInstr * 1024 * kWaves == kWBytes && kXInstr * 1024 * kWaves == kXBytes, "copy split");
+static_assert(kXInstr % 2 == 0, "activation copies alternate between the two 8-row swizzle phases");
+static_assert((kGroupRows / 2) * kYRow <= kStage, "half a group's image fits a stage");
+static_assert(4 * kSI * 32 == kBN && 2 * kGroupRows == kBM, "wave layout");
+} // namespace pp
+
+static_assert(pp::kBM * kPingPongMaxK * 2 <= (int64_t(1) << 31), "buffer range");
+
+template <bool OL, bool ZP>
+__global__ __launch_bounds__(pp::kThreads) void mfma_pp_kernel(
+    const uint16_t *__restrict__ x, const int8_t *__restrict__ q, const uint16_t *__restrict__ scales,
+    const int8_t *__restrict__ zeros, OutlierList ol, uint16_t *__restrict__ y, int m, int n, int k,
+    int tiles_m, int tiles_n, int group)
+{
+    using namespace pp;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring0[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring1[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring2[kStage];
+    __shared__ __attribute__((aligned(16))) float scale_lds[kBN];
+    // OL: the workgroup's side lists, (column, value / S as float bits) per
+    // slot; unused slots hold column INT_MAX
+    __shared__ __attribute__((aligned(16))) int2v ol_lds[OL ? kBN * kMfmaOutlierSlots : 1];
+    auto ring = [&](auto s) -> uint8_t * {
+        if constexpr (decltype(s)::value == 0)
+            return ring0;
+        else if constexpr (decltype(s)::value == 1)
+            return ring1;
+        else
+            return ring2;
+    };
+
+    const int tid = threadIdx.x;
+    const int lane = __lane_id();
+    const int wave = __builtin_amdgcn_readlane(tid / kWave, 0);
+    const int grp = wave / 4;
+    const int nw = wave % 4;
+
+    const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+    const int gsize = group * tiles_m;
+    const int gi = tile / gsize;
+    const int gl = tile - gi * gsize;
+    const int gw = min(group, tiles_n - gi * group);
+    const int tn = gi * group + gl % gw;
+    const int tm = gl / gw;
+    const int n0 = tn * kBN;
+    const int m0 = tm * kBM;
+    const int ktiles = (k + kBK - 1) / kBK;
+    const int full_tiles = (k % kBK) != 0 ? ktiles - 1 : ktiles;
+
+    // Copy sources: as in the 4-wave kernel, with 8 waves sharing a tile.
+    // Copy i of a wave covers rows 16 i (weight) or 8 i (activations) below
+    // its copy 0, so one lane offset per swizzle phase serves all copies and
+    // the rest goes into the scalar offset.  Rows past n or m are not
+    // clamped: they lie past the end of the buffer range, and such reads
+    // return zeros (only outputs that are never stored depend on them).
+    const int wchunk = (lane % 4) ^ wslot(lane / 4);
+    const int xchunk_even = (lane % 8) ^ xslot(lane / 8);
+    const int xchunk_odd = (lane % 8) ^ xslot(8 + lane / 8);
+    const uint32_t woff = (uint32_t)((wave * kWInstr * 16 + lane / 4) * k + wchunk * 16);
+    const uint32_t xrow0 = (uint32_t)(wave * kXInstr * 8 + lane / 8);
+    const uint32_t xoff_even = (xrow0 * k + xchunk_even * 8) * 2;
+    const uint32_t xoff_odd = ((xrow0 + 8) * k + xchunk_odd * 8) * 2;
+    const int8_t *wtile = q + (int64_t)n0 * k;
+    const uint16_t *xtile = x + (int64_t)m0 * k;
+    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t *>(wtile), (short)0,
+        static_cast<int>(static_cast<uint32_t>(min((int64_t)kBN, (int64_t)(n - n0)) * k)), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(xtile), (short)0,
+        static_cast<int>(static_cast<uint32_t>(min((int64_t)kBM, (int64_t)(m - m0)) * k * 2)), kBufferFlags);
+
+    // this wave's share of the copies of tile kt into stage array st
+    auto issue_full = [&](int kt, uint8_t *st) {
+        const int k0 = kt * kBK;
+#pragma unroll
+        for (int i = 0; i < kWInstr; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, (lds_ptr_t)(st + (wave * kWInstr + i) * 1024), 16,
+                                                     (int)woff, k0 + i * 16 * k, 0, 0);
+#pragma unroll
+        for (int i = 0; i < kXInstr; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xrsrc, (lds_ptr_t)(st + kWBytes + (wave * kXInstr + i) * 1024), 16,
+                (int)((i & 1) ? xoff_odd : xoff_even), (k0 + (i & ~1) * 8 * k) * 2, 0, 0);
+    };
+    // The ragged last tile: activation chunks past k are zero-filled, so
+    // whatever the weight chunks past k hold (codes of the next row, or
+    // zeros past the buffer range) multiplies zeros.
+    auto issue_partial = [&](int kt, uint8_t *st) {
+        const int k0 = kt * kBK;
+#pragma unroll
+        for (int i = 0; i < kWInstr; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, (lds_ptr_t)(st + (wave * kWInstr + i) * 1024), 16,
+                                                     (int)woff, k0 + i * 16 * k, 0, 0);
+#pragma unroll
+        for (int i = 0; i < kXInstr; ++i) {
+            uint8_t *dst = st + kWBytes + (wave * kXInstr + i) * 1024;
+            const int gk = k0 + ((i & 1) ? xchunk_odd : xchunk_even) * 8;
+            if (gk < k)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, (lds_ptr_t)dst, 16,
+                                                         (int)((i & 1) ? xoff_odd : xoff_even),
+                                                         (k0 + (i & ~1) * 8 * k) * 2, 0, 0);
+            else
+                *reinterpret_cast<u32x4_t *>(dst + lane * 16) = (u32x4_t){0u, 0u, 0u, 0u};
+        }
+    };
+    // FULL: tile kt is known to lie inside k
+    auto issue = [&](int kt, uint8_t *st, auto full) {
+        if constexpr (decltype(full)::value) {
+            issue_full(kt, st);
+        } else {
+            if (kt < full_tiles)
+                issue_full(kt, st);
+            else if (kt < ktiles)
+                issue_partial(kt, st);
+        }
+    };
+    // End of phase 2u - 1: this wave's copies of tile u are done; the batch
+    // of tile u + 1 it issued since may stay in flight (FULL: that batch was
+    // a full tile).  Written as inline asm behind a scheduling barrier: the
+    // builtin form alone was moved past the phase's barrier, and either form
+    // ahead of the MFMAs.  The builtin beside it tells the compiler's own
+    // wait-count bookkeeping what has completed.
+    auto wait_tile = [&](int u, auto full) {
+        static_assert(kCopies == 6, "the wait below names the batch size");
+        __builtin_amdgcn_sched_barrier(0);
+        if (decltype(full)::value || u + 1 < full_tiles) {
+            __asm__ __volatile__("s_waitcnt vmcnt(6)" ::: "memory");
+            QW_WAIT_VMCNT(kCopies);
+        } else {
+            __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");
+            QW_WAIT_VMCNT(0);
+        }
+    };
+    // A phase boundary.  The scheduling barriers keep the compiler from
+    // moving any instruction (the MFMAs above all, which touch no memory)
+    // across the workgroup barrier into the neighbouring phase.
+    auto phase_end = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        ring_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // operand layout of v_mfma_f32_32x32x16_f16 as in the 4-wave kernel
+    const int lrow = lane % 32;
+    const int lgrp = lane / 32;
+    // The row bases have bits 4..7 clear, so the swizzled 16-byte chunk
+    // c ^ slot of chunk c = c0 + s is the base's chunk c0 XOR s: one lane
+    // offset per operand, the others one XOR away (kept out of registers
+    // across the loop).
+    const int wrow = nw * (kSI * 32) + lrow; // + 32 i
+    const int w_off0 = wrow * kBK + 16 * ((2 * lgrp) ^ wslot(wrow));
+    const int xrow = grp * kGroupRows + lrow; // + 32 j
+    const int x_off0 = kWBytes + xrow * 2 * kBK + 16 * ((4 * lgrp) ^ xslot(xrow));
+
+    float16v acc[kSI][kSJ];
+#pragma unroll
+    for (int i = 0; i < kSI; ++i)
+#pragma unroll
+        for (int j = 0; j < kSJ; ++j)
+            acc[i][j] = (float16v){};
+    half2_t zbias[kSI];
+#pragma unroll
+    for (int i = 0; i < kSI; ++i) {
+        const int zr = n0 + wrow + 32 * i;
+        zbias[i] = zero_point_bias(ZP && zr < n ? (int)zeros[zr] : 0);
+    }
+
+    // Operands of one k step: the weight codes are cast to fp16 in the
+    // memory phase, right after their LDS reads, so that the MFMA phase is
+    // MFMAs only (cast between the MFMAs, the casts' VALU work did not
+    // overlap them and stretched the MFMA phase by about 40%).
+    half8_t a[kSI][4];
+    half8_t b[kSJ][4];
+    auto load = [&](const uint8_t *st) {
+        int w_off1, x_off[4];
+        x_off[0] = x_off0;
+        // (volatile: computed here, in the memory phase, rather than hoisted
+        // out of the loop into registers held across it)
+        __asm__ __volatile__("v_xor_b32 %0, 16, %1" : "=v"(w_off1) : "v"(w_off0));
+        __asm__ __volatile__("v_xor_b32 %0, 16, %1" : "=v"(x_off[1]) : "v"(x_off0));
+        __asm__ __volatile__("v_xor_b32 %0, 32, %1" : "=v"(x_off[2]) : "v"(x_off0));
+        __asm__ __volatile__("v_xor_b32 %0, 48, %1" : "=v"(x_off[3]) : "v"(x_off0));
+        u32x4_t clo[kSI], chi[kSI];
+#pragma unroll
+        for (int i = 0; i < kSI; ++i) {
+            clo[i] = *reinterpret_cast<const u32x4_t *>(st + w_off0 + i * 32 * kBK);
+            chi[i] = *reinterpret_cast<const u32x4_t *>(st + w_off1 + i * 32 * kBK);
+        }
+#pragma unroll
+        for (int sidx = 0; sidx < 4; ++sidx)
+#pragma unroll
+            for (int j = 0; j < kSJ; ++j)
+                b[j][sidx] = *reinterpret_cast<const half8_t *>(st + x_off[sidx] + j * 32 * 2 * kBK);
+#pragma unroll
+        for (int i = 0; i < kSI; ++i) {
+            a[i][0] = i8x8_to_half8(clo[i].x, clo[i].y, zbias[i]);
+            a[i][1] = i8x8_to_half8(clo[i].z, clo[i].w, zbias[i]);
+            a[i][2] = i8x8_to_half8(chi[i].x, chi[i].y, zbias[i]);
+            a[i][3] = i8x8_to_half8(chi[i].z, chi[i].w, zbias[i]);
+        }
+    };
+    auto compute = [&]() {
+#pragma unroll
+        for (int sidx = 0; sidx < 4; ++sidx)
+#pragma unroll
+            for (int i = 0; i < kSI; ++i)
+#pragma unroll
+                for (int j = 0; j < kSJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][sidx], b[j][sidx], acc[i][j], 0, 0, 0);
+    };
+    // memory phase of tile t (stage S): copies of tile t + 2, then operands
+    auto mem = [&](int t, auto s, auto full) {
+        constexpr int S = decltype(s)::value;
+        issue(t + 2, ring(stage_t<(S + 2) % 3>{}), full);
+        __builtin_amdgcn_sched_barrier(0);
+        load(ring(s));
+    };
+    using full_t = std::integral_constant<bool, true>;
+    using partial_t = std::integral_constant<bool, false>;
+
+    // prologue: tiles 0 and 1 in flight, scales staged, tile 0 landed
+    issue(0, ring0, partial_t{});
+    issue(1, ring1, partial_t{});
+    for (int c = tid; c < kBN; c += kThreads)
+        scale_lds[c] = n0 + c < n ? f16_bits_to_f32(scales[n0 + c]) : 0.0f;
+    if constexpr (OL) {
+        for (int e = tid; e < kBN * kMfmaOutlierSlots; e += kThreads) {
+            const int c = e / kMfmaOutlierSlots, slot = e % kMfmaOutlierSlots;
+            int col = 0x7fffffff;
+            float o = 0.0f;
+            if (n0 + c < n && slot < ol.cap) {
+                const int64_t at = (int64_t)(n0 + c) * ol.cap + slot;
+                const int kk = ol.idx[at];
+                if (kk >= 0 && kk < k) {
+                    col = kk;
+                    o = __fdiv_rn(ol.val[at], f16_bits_to_f32(scales[n0 + c]));
+                }
+            }
+            ol_lds[e] = (int2v){col, __builtin_bit_cast(int, o)};
+        }
+    }
+    wait_tile(0, partial_t{});
+    phase_end();
+
+    // The steady loop runs while tiles t + 2 ... t + 4, copied by its three
+    // steps, lie inside k; at most five steps remain after it.
+    auto run = [&](auto &&body) {
+        int t = 0;
+        for (; t + 5 <= full_tiles; t += 3) {
+            body(t, stage_t<0>{}, full_t{});
+            body(t + 1, stage_t<1>{}, full_t{});
+            body(t + 2, stage_t<2>{}, full_t{});
+        }
+        static_for<0, 5>([&](auto d) {
+            if (t + d < ktiles)
+                body(t + d, stage_t<decltype(d)::value % 3>{}, partial_t{});
+        });
+    };
+    if (grp == 0) {
+        run([&](int t, auto s, auto full) {
+            mem(t, s, full);
+            phase_end(); // end of phase 2t
+            compute();
+            wait_tile(t + 1, full);
+            phase_end(); // end of phase 2t + 1
+        });
+    } else {
+        phase_end(); // end of phase 0
+        run([&](int t, auto s, auto full) {
+            mem(t, s, full);
+            wait_tile(t + 1, full);
+            phase_end(); // end of phase 2t + 1
+            compute();
+            if (t + 1 < ktiles)
+                phase_end(); // end of phase 2t + 2
+        });
+    }
+
+    // ---- epilogue: one group at a time through an LDS image of its rows ----
+    // group 0 writes its image in phase 2T (all stages are free: group 1
+    // read the last tile in phase 2T - 1) while group 1 finishes its MFMAs
+    auto write_image = [&]() {
+#pragma unroll
+        for (int i = 0; i < kSI; ++i) {
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const int nl = nw * (kSI * 32) + i * 32 + 8 * qd + 4 * lgrp;
+                const float4v sc = *reinterpret_cast<const float4v *>(scale_lds + nl);
+#pragma unroll
+                for (int j = 0; j < kSJ; ++j) {
+                    uint8_t *img = j < kSJ / 2 ? ring0 + (j * 32 + lrow) * kYRow
+                                               : ring1 + (j * 32 - kGroupRows / 2 + lrow) * kYRow;
+                    const uint32_t o0 = f32_to_f16_bits(acc[i][j][4 * qd + 0] * sc[0]);
+                    const uint32_t o1 = f32_to_f16_bits(acc[i][j][4 * qd + 1] * sc[1]);
+                    const uint32_t o2 = f32_to_f16_bits(acc[i][j][4 * qd + 2] * sc[2]);
+                    const uint32_t o3 = f32_to_f16_bits(acc[i][j][4 * qd + 3] * sc[3]);
+                    *reinterpret_cast<u32x2_t *>(img + nl * 2) = (u32x2_t){o0 | (o1 << 16), o2 | (o3 << 16)};
+                }
+            }
+        }
+    };
+    constexpr int kRowChunks = kBN / 8;
+    const bool vec_ok = (n % 8) == 0 && n0 + kBN <= n;
+    auto store_rows = [&](int g) {
+        const int r0 = m0 + g * kGroupRows;
+        const int rows = min(kGroupRows, m - r0);
+        for (int c = tid; c < rows * kRowChunks; c += kThreads) {
+            const int row = c / kRowChunks;
+            const int cc = c % kRowChunks;
+            const uint8_t *img = row < kGroupRows / 2 ? ring0 + row * kYRow : ring1 + (row - kGroupRows / 2) * kYRow;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(img + cc * 16);
+            uint16_t *dst = y + (int64_t)(r0 + row) * n + n0 + cc * 8;
+            if (vec_ok) {
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst));
+            } else {
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (n0 + cc * 8 + e < n)
+                        dst[e] = (uint16_t)(w[e / 2] >> (16 * (e % 2)));
+            }
+        }
+    };
+    if constexpr (OL) {
+        // Outlier side lists, one slot at a time, after both groups' MFMAs
+        // (end of phase 2T): the workgroup gathers G[c][r] = x[m0 + r][column
+        // of channel c's entry] for all 256 channels and rows into the three
+        // stage arrays (86 channels each, rows padded by 2 halves), then every
+        // lane adds G * (value / S) to the accumulators it holds.  Unused
+        // entries have value 0 and gather a zero.
+        ring_barrier();
+        constexpr int kGRow = kBM + 2;
+        constexpr int kGPer = 86;
+        static_assert(kGPer * kGRow * 2 <= kStage && 3 * kGPer >= kBN, "G fits the stage arrays");
+        auto gaddr = [&](int c, int r) -> _Float16 * {
+            const int a = c / kGPer;
+            uint8_t *base = a == 0 ? ring0 : (a == 1 ? ring1 : ring2);
+            return reinterpret_cast<_Float16 *>(base) + (c - a * kGPer) * kGRow + r;
+        };
+        constexpr int kRStep = kThreads / kBN;
+        constexpr int kPer = kBM / kRStep;
+        constexpr int kBatch = 32;
+        static_assert(kThreads % kBN == 0 && kPer % kBatch == 0, "gather split");
+        const int gc = tid % kBN, gr0 = tid / kBN;
+        const int slots = min(ol.cap, kMfmaOutlierSlots);
+        for (int sl = 0; sl < slots; ++sl) {
+            const int col = ol_lds[gc * kMfmaOutlierSlots + sl].x;
+            const bool live = col != 0x7fffffff;
+            for (int b0 = 0; b0 < kPer; b0 += kBatch) {
+                uint16_t v[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int r = gr0 + (b0 + u) * kRStep;
+                    const bool ok = live && m0 + r < m;
+                    v[u] = x[ok ? (int64_t)(m0 + r) * k + col : 0];
+                    v[u] = ok ? v[u] : (uint16_t)0;
+                }
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u)
+                    *gaddr(gc, gr0 + (b0 + u) * kRStep) = __builtin_bit_cast(_Float16, v[u]);
+            }
+            ring_barrier();
+#pragma unroll
+            for (int i = 0; i < kSI; ++i) {
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int c = nw * (kSI * 32) + i * 32 + 8 * (rr / 4) + 4 * lgrp + rr % 4;
+                    // (copied out first: a bit cast of an ext-vector
+                    // component in place reads component 0)
+                    const int obits = ol_lds[c * kMfmaOutlierSlots + sl].y;
+                    const float o = __builtin_bit_cast(float, obits);
+#pragma unroll
+                    for (int j = 0; j < kSJ; ++j)
+                        acc[i][j][rr] += (float)*gaddr(c, grp * kGroupRows + j * 32 + lrow) * o;
+                }
+            }
+            ring_barrier();
+        }
+    }
+    if (grp == 0)
+        write_image();
+    ring_barrier();
+    store_rows(0);
+    ring_barrier();
+    if (grp == 1)
+        write_image();
+    ring_barrier();
+    store_rows(1);
+}
+
 template <int BN, int BM, bool A8>
 int64_t slots_per_cu();
 
@@ -749,9 +1184,31 @@ bool fills(int64_t m, int64_t n)
     return 4 * tiles >= 3 * slots;
 }
 
-template <bool A8>
-int tile_choice(int64_t m, int64_t n)
+// The ping-pong tile (fp16 activations) where its grid covers at least half
+// the CUs (one workgroup per CU) and rounding m up to 256 rows costs at most
+// 10% more rows than rounding it to 64 (the smallest 4-wave tile).
+// Measured on MI355X against the 4-wave tiles: 10-13% faster at 512 x 4096
+// x 27392, 8% at 2048 x 4096 x 4608 (144 tiles), even at 4096 x 1024 x
+// 4096; 20% slower at 256 x 4096 x 27392 (107 tiles).
+bool pp_fills(int64_t m, int64_t n, int64_t k)
 {
+    if (k > kPingPongMaxK)
+        return false;
+    const int64_t tiles = ((m + pp::kBM - 1) / pp::kBM) * ((n + pp::kBN - 1) / pp::kBN);
+    const int64_t rows256 = (m + 255) / 256 * 256, rows64 = (m + 63) / 64 * 64;
+    return 2 * tiles >= (int64_t)device_cu_count() && 10 * rows256 <= 11 * rows64;
+}
+
+// PP: the ping-pong tile may be chosen.  Calls with outlier side lists keep
+// the 4-wave tiles: the ping-pong kernel's epilogue gather of the side
+// lists' activation columns, one workgroup per CU with nothing to overlap
+// it, measured 54% above the plain GEMM on 4096 x 1024 x 4096 (one slot)
+// against 43% for the 256 x 128 tile.
+template <bool A8>
+int tile_choice(int64_t m, int64_t n, int64_t k, bool pp = true)
+{
+    if (!A8 && pp && pp_fills(m, n, k))
+        return 256256;
     // largest tile first (more reuse per byte staged); 256 x 64 before
     // 128 x 128 (same area, half the activation bytes per tile)
     if (fills<256, 128, A8>(m, n))
@@ -766,6 +1223,34 @@ int tile_choice(int64_t m, int64_t n)
     return 128064;
 }
 
+// Ping-pong launch: one 512-thread workgroup per 256 x 256 tile, one per CU
+// (144 KiB of LDS).  Grouped tile order as for the 4-wave tiles, with one
+// resident workgroup per CU.
+hipError_t launch_pp(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros,
+                     OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
+{
+    const int64_t tiles_m = (m + pp::kBM - 1) / pp::kBM;
+    const int64_t tiles_n = (n + pp::kBN - 1) / pp::kBN;
+    const int64_t blocks = tiles_m * tiles_n;
+    if (blocks > 0x7fffffff || k < 1 || k > kPingPongMaxK || (ol.idx != nullptr && ol.cap > kMfmaOutlierSlots))
+        return hipErrorInvalidValue;
+    const int64_t share = (blocks + 7) / 8;
+    const int64_t resident = std::max<int64_t>(1, (int64_t)device_cu_count() / 8);
+    const double r = (double)std::max<int64_t>(1, std::min(share, resident));
+    int64_t a = std::llround(std::sqrt(r * pp::kBM * 2 / pp::kBN));
+    a = std::max<int64_t>(a, ((int64_t)r + tiles_m - 1) / tiles_m);
+    const int group = (int)std::max<int64_t>(1, std::min(a, tiles_n));
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(pp::kThreads), 0, stream, x, q, scales, zeros, ol, y,
+                           (int)m, (int)n, (int)k, (int)tiles_m, (int)tiles_n, group);
+        return hipGetLastError();
+    };
+    // side lists come with symmetric codes only (as in the 4-wave kernels)
+    if (ol.idx != nullptr)
+        return go(mfma_pp_kernel<true, false>);
+    return zeros != nullptr ? go(mfma_pp_kernel<false, true>) : go(mfma_pp_kernel<false, false>);
+}
+
 template <bool A8>
 hipError_t launch_tiles(const void *x, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
                         const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k,
@@ -773,8 +1258,12 @@ hipError_t launch_tiles(const void *x, const uint16_t *sx, const int8_t *q, cons
 {
     if (k > kMfmaMaxK) // the entry points route such rows elsewhere
         return hipErrorInvalidValue;
-    const int tile = forced_tile != 0 ? forced_tile : tile_choice<A8>(m, n);
+    const int tile = forced_tile != 0 ? forced_tile : tile_choice<A8>(m, n, k, ol.idx == nullptr);
     switch (tile) {
+    case 256256:
+        if constexpr (!A8)
+            return launch_pp(static_cast<const uint16_t *>(x), q, scales, zeros, ol, y, m, n, k, stream);
+        return hipErrorInvalidValue;
     case 256128:
         return launch_dma<4, 256, 128, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
     case 256064:
@@ -790,14 +1279,14 @@ hipError_t launch_tiles(const void *x, const uint16_t *sx, const int8_t *q, cons
 
 } // namespace
 
-int mfma_tile_choice(int64_t m, int64_t n)
+int mfma_tile_choice(int64_t m, int64_t n, int64_t k)
 {
-    return tile_choice<false>(m, n);
+    return tile_choice<false>(m, n, k);
 }
 
 int w8a8_tile_choice(int64_t m, int64_t n)
 {
-    return tile_choice<true>(m, n);
+    return tile_choice<true>(m, n, 0);
 }
 
 hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
@@ -811,7 +1300,9 @@ hipError_t launch_mfma_gemm_tile(int tile, const uint16_t *x, const int8_t *q, c
                                  const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n,
                                  int64_t k, hipStream_t stream)
 {
-    if (tile != 256128 && tile != 256064 && tile != 128128 && tile != 128064)
+    if (tile != 256256 && tile != 256128 && tile != 256064 && tile != 128128 && tile != 128064)
+        return hipErrorInvalidValue;
+    if (tile == 256256 && k > kPingPongMaxK)
         return hipErrorInvalidValue;
     return launch_tiles<false>(x, nullptr, q, scales, zeros, ol, y, m, n, k, stream, tile);
 }

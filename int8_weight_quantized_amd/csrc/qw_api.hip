@@ -203,7 +203,7 @@ qw_status quantize_common(const void *w, int wbytes, int64_t n, int64_t k, doubl
 // ol.idx == nullptr: no outlier side lists).
 qw_status gemm_common(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros,
                       uint16_t *y, int64_t m, int64_t n, int64_t k, int path, void *stream,
-                      qw::OutlierList ol = qw::OutlierList{nullptr, nullptr, 0})
+                      qw::OutlierList ol = qw::OutlierList{nullptr, nullptr, 0}, int tile = 0)
 {
     if (path != QW_PATH_AUTO && path != QW_PATH_GEMV && path != QW_PATH_MFMA &&
         path != QW_PATH_SKINNY)
@@ -235,7 +235,8 @@ qw_status gemm_common(const uint16_t *x, const int8_t *q, const uint16_t *scales
         const int tpath = tuned / qw::kChoicePath;
         if (tuned >= 0 && (tpath != QW_PATH_GEMV || qw::gemv_supported(m, k)) &&
             (tpath != QW_PATH_MFMA || ((ol.idx == nullptr || ol.cap <= qw::kMfmaOutlierSlots) &&
-                                       k <= qw::kMfmaMaxK)) &&
+                                       k <= qw::kMfmaMaxK &&
+                                       (tuned % qw::kChoicePath != 256256 || k <= qw::kPingPongMaxK))) &&
             (tpath != QW_PATH_SKINNY || m <= 16 * 65535))
             return launch_status(qw::launch_choice(tuned, x, q, scales, zeros, ol, y, m, n, k, s));
         path = qw::auto_path(m, n, k);
@@ -255,6 +256,8 @@ qw_status gemm_common(const uint16_t *x, const int8_t *q, const uint16_t *scales
             return QW_ERROR_UNSUPPORTED;
         return launch_status(qw::launch_skinny_gemm(x, q, scales, zeros, ol, y, m, n, k, s));
     }
+    if (tile != 0)
+        return launch_status(qw::launch_mfma_gemm_tile(tile, x, q, scales, zeros, ol, y, m, n, k, s));
     return launch_status(qw::launch_mfma_gemm(x, q, scales, zeros, ol, y, m, n, k, s));
 }
 
@@ -369,6 +372,23 @@ QW_API qw_status qw_w8a16_gemm_outliers_path(const uint16_t *x, const int8_t *q,
                        qw::OutlierList{cap > 0 ? ol_idx : nullptr, ol_val, (int)cap});
 }
 
+QW_API qw_status qw_w8a16_gemm_tile(const uint16_t *x, const int8_t *q, const uint16_t *scales,
+                                    const int8_t *zeros, const int32_t *ol_idx, const float *ol_val,
+                                    int64_t cap, uint16_t *y, int64_t m, int64_t n, int64_t k, int tile,
+                                    void *stream)
+{
+    if (tile != 256256 && tile != 256128 && tile != 256064 && tile != 128128 && tile != 128064)
+        return QW_ERROR_INVALID_VALUE;
+    if (cap < 0 || cap > k || cap > kMaxDim || (zeros != nullptr && cap > 0))
+        return QW_ERROR_INVALID_VALUE;
+    if (m > 0 && n > 0 && cap > 0 && (!ol_idx || !ol_val))
+        return QW_ERROR_INVALID_VALUE;
+    if (tile == 256256 && k > qw::kPingPongMaxK && k % 16 == 0)
+        return QW_ERROR_UNSUPPORTED;
+    return gemm_common(x, q, scales, zeros, y, m, n, k, QW_PATH_MFMA, stream,
+                       qw::OutlierList{cap > 0 ? ol_idx : nullptr, ol_val, (int)cap}, tile);
+}
+
 QW_API qw_status qw_w8a16_gemm_outliers(const uint16_t *x, const int8_t *q, const uint16_t *scales,
                                         const int32_t *ol_idx, const float *ol_val, int64_t cap,
                                         uint16_t *y, int64_t m, int64_t n, int64_t k, void *stream)
@@ -436,7 +456,7 @@ QW_API int qw_w8a16_gemm_mfma_tile(int64_t m, int64_t n, int64_t k)
     const int tuned = qw::tuned_choice(m, n, k);
     if (tuned >= 0 && tuned / qw::kChoicePath == QW_PATH_MFMA)
         return tuned % qw::kChoicePath;
-    return qw::mfma_tile_choice(m, n);
+    return qw::mfma_tile_choice(m, n, k);
 }
 
 } // extern "C"

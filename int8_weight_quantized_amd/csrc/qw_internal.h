@@ -77,8 +77,13 @@ hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *
                             int64_t k, hipStream_t stream);
 
 // Output tile of the MFMA GEMM for this shape on the current device,
-// encoded BN * 1000 + BM.
-int mfma_tile_choice(int64_t m, int64_t n);
+// encoded BN * 1000 + BM (256256: the 8-wave ping-pong kernel).
+int mfma_tile_choice(int64_t m, int64_t n, int64_t k);
+
+// Longest reduction of the 256 x 256 ping-pong tile: its 256-row activation
+// tile spans 256 * k * 2 bytes of one buffer range, kept below 2^31.
+constexpr int64_t kPingPongMaxK = QW_PINGPONG_MAX_K;
+static_assert(256 * kPingPongMaxK * 2 <= (int64_t(1) << 31), "ping-pong buffer range");
 
 // W8A8 GEMM on the matrix cores (int8 activation codes qx [m, k] with one
 // fp16 scale per row in sx), any m, n, k with k % 16 == 0, and its tile.
@@ -125,7 +130,8 @@ hipError_t launch_choice_w8a8(int choice, const int8_t *qx, const uint16_t *sx, 
 hipError_t launch_w8a8_gemm_tile(int tile, const int8_t *qx, const uint16_t *sx, const int8_t *q,
                                  const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
                                  hipStream_t stream);
-// The MFMA GEMM with a given tile (BN * 1000 + BM).
+// The MFMA GEMM with a given tile (BN * 1000 + BM); hipErrorInvalidValue for
+// a tile that is not built or a k the tile does not take.
 hipError_t launch_mfma_gemm_tile(int tile, const uint16_t *x, const int8_t *q, const uint16_t *scales,
                                  const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n,
                                  int64_t k, hipStream_t stream);

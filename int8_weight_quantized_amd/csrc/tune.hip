@@ -155,6 +155,8 @@ hipError_t tune_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
         cands[nc++] = QW_PATH_GEMV * kChoicePath;
     if (m <= 16 * 65535)
         cands[nc++] = QW_PATH_SKINNY * kChoicePath;
+    if (k <= kPingPongMaxK)
+        cands[nc++] = QW_PATH_MFMA * kChoicePath + 256256;
     if (k <= kMfmaMaxK)
         for (int tile : {256128, 256064, 128128, 128064})
             cands[nc++] = QW_PATH_MFMA * kChoicePath + tile;

@@ -119,3 +119,28 @@ def assert_gemm_close(y: np.ndarray, ref: np.ndarray, what: str = ""):
     tol = TOL_REL * (np.abs(ref).max() if ref.size else 0.0) + TOL_ABS
     assert err <= tol, "%s: max err %.3g > tol %.3g" % (what, err, tol)
     return err, tol
+
+
+def gpu_gemm_tile(x: np.ndarray, q: np.ndarray, s_bits: np.ndarray, tile, zeros=None, idx=None, val=None):
+    """The MFMA GEMM with a forced output tile (BN, BM) through the C ABI
+    (zeros: asymmetric codes; idx/val: outlier side lists); returns Y as
+    float16."""
+    import int8_weight_quantized_amd as qw
+    torch = torch_mod()
+    m, k = x.shape
+    n = q.shape[0]
+    xd = dev(np.ascontiguousarray(x, dtype=np.float16).view(np.int16))
+    qd = dev(np.ascontiguousarray(q, dtype=np.int8))
+    sd = dev(np.ascontiguousarray(s_bits, dtype=np.uint16).view(np.int16))
+    zd = dev(np.ascontiguousarray(zeros, dtype=np.int8)) if zeros is not None else None
+    cap = idx.shape[1] if idx is not None else 0
+    idd = dev(np.ascontiguousarray(idx, dtype=np.int32)) if cap else None
+    vd = dev(np.ascontiguousarray(val, dtype=np.float32)) if cap else None
+    yd = torch.full((m, n), 0x7e00, dtype=torch.int16, device="cuda:0")  # NaN canary
+    st = qw.w8a16_gemm_tile_raw(xd.data_ptr(), qd.data_ptr(), sd.data_ptr(),
+                                zd.data_ptr() if zd is not None else None,
+                                idd.data_ptr() if idd is not None else None,
+                                vd.data_ptr() if vd is not None else None, cap, yd.data_ptr(), m, n, k,
+                                tile[0] * 1000 + tile[1], int(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, qw.status_string(st)
+    return host(yd).view(np.float16)

@@ -181,7 +181,21 @@ def test_public_calls_refuse_cpu_tensors_before_the_library():
         lambda: qw.w8a16_gemm_outliers(x, q, s, t((N, 1), torch.int32, cpu), t((N, 1), torch.float32, cpu)),
         lambda: qw.w8a8_gemm(t((M, K), torch.int8, cpu), t((M,), torch.float16, cpu), q, s),
         lambda: qw.quantize_activations(x),
+        lambda: qw.w8a16_gemm_tile(x, q, s, (256, 256)),
     ]
     for call in calls:
         with pytest.raises(ValueError, match="GPU"):
             call()
+
+
+def test_gemm_tile_argument_rejections():
+    """A tile outside the built set, or zero points together with side
+    lists, is refused before any tensor is looked at."""
+    x, q, s = gemm_operands()
+    for tile in ((256, 512), (64, 64), (256,), "256256"):
+        with pytest.raises(ValueError, match="tile"):
+            qw.w8a16_gemm_tile(x, q, s, tile)
+    with pytest.raises(ValueError, match="zeros or outliers"):
+        qw.w8a16_gemm_tile(x, q, s, (256, 256), zeros=t((N,), torch.int8),
+                           outliers=(t((N, 1), torch.int32), t((N, 1), torch.float32)))
+    assert set(qw.MFMA_TILES) == {(256, 256), (256, 128), (256, 64), (128, 128), (128, 64)}

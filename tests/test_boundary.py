@@ -209,6 +209,27 @@ def test_gemm_outliers_mfma_slot_limit():
     assert qw.w8a16_gemm_outliers_raw(A, B, C, D, E, 5, F, 64, 64, 64, 0, 2) == qw.QW_ERROR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("args,status", [
+    ((A, B, C, 0, 0, 0, 0, D, 4, 4, 16, 256000), qw.QW_ERROR_INVALID_VALUE),        # no such tile
+    ((A, B, C, 0, 0, 0, 0, D, 4, 4, 16, 0), qw.QW_ERROR_INVALID_VALUE),             # tile 0
+    ((A, B, C, E, A, B, 2, D, 4, 4, 16, 256256), qw.QW_ERROR_INVALID_VALUE),        # zeros and side lists
+    ((A, B, C, 0, 0, B, 2, D, 4, 4, 16, 256256), qw.QW_ERROR_INVALID_VALUE),        # cap > 0, null idx
+    ((A, B, C, 0, 0, 0, -1, D, 4, 4, 16, 256256), qw.QW_ERROR_INVALID_VALUE),       # cap < 0
+    ((A, B, C, 0, 0, 0, 0, D, -1, 4, 16, 256256), qw.QW_ERROR_INVALID_VALUE),       # m < 0
+    ((0, B, C, 0, 0, 0, 0, D, 4, 4, 16, 256256), qw.QW_ERROR_INVALID_VALUE),        # null x
+    ((A, B, C, 0, 0, 0, 0, D, 4, 4, 24, 256256), qw.QW_ERROR_UNSUPPORTED),          # k % 16
+    ((A, B, C, 0, 0, 0, 0, D, 4, 4, qw.PINGPONG_MAX_K + 16, 256256), qw.QW_ERROR_UNSUPPORTED),  # k limit
+    ((A, B, C, 0, E, F, 5, D, 4, 4, 64, 256128), qw.QW_ERROR_UNSUPPORTED),          # > 4 slots on MFMA
+    ((A + 8, B, C, 0, 0, 0, 0, D, 4, 4, 16, 128064), qw.QW_ERROR_MISALIGNED),       # misaligned x
+])
+def test_gemm_tile_rejects(args, status):
+    assert qw.w8a16_gemm_tile_raw(*args) == status
+
+
+def test_gemm_tile_empty_is_noop():
+    assert qw.w8a16_gemm_tile_raw(0, 0, 0, 0, 0, 0, 0, 0, 0, 4, 16, 256256) == qw.QW_SUCCESS
+
+
 def test_quantize_empty_is_noop():
     # n == 0: nothing to do, null pointers allowed
     assert qw.quantize_weights_raw(0, 0, 16, 100.0, 0, 0) == qw.QW_SUCCESS

@@ -19,7 +19,7 @@ import pytest
 
 import oracle
 import synthetic
-from gpu_util import assert_gemm_close, gpu_gemm, gpu_quantize, say
+from gpu_util import assert_gemm_close, gpu_gemm, gpu_gemm_tile, gpu_quantize, say
 
 pytestmark = pytest.mark.gpu
 
@@ -79,7 +79,7 @@ def test_gemm_workload(name):
 # which shape gets which tile).
 TILE_SHAPES = [(512, 27392, 256), (2048, 4608, 128), (256, 27392, 128), (384, 13824, 128),
                (96, 27392, 256), (1024, 9216, 128), (4096, 4096, 64), (320, 6144, 144),
-               (384, 32768, 128), (129, 40960, 64)]
+               (384, 32768, 128), (129, 40960, 64), (1088, 9216, 128)]
 
 
 def test_mfma_every_tile_shape():
@@ -95,23 +95,22 @@ def test_mfma_every_tile_shape():
         ref = oracle.gemm_sampled(x, q, s, mi, ni)
         assert_gemm_close(y[mi, ni], ref, "mfma tile %s %dx%dx%d (sampled)" % (tile, m, n, k))
         assert np.all(np.isfinite(y.astype(np.float32))), "non-finite output outside the sample"
-    assert seen == {(256, 128), (256, 64), (128, 128), (128, 64)}, "tiles exercised: %s" % sorted(seen)
+    assert seen == {(256, 256), (256, 128), (256, 64), (128, 128), (128, 64)}, "tiles exercised: %s" % sorted(seen)
 
 
-# Grids on the 256 x 128 tile whose tile order walks several weight-tile
-# columns per group, the last group narrower: 107 and 13 columns with every
-# tile of an XCD resident at once, 17 columns over several rounds of
-# resident tiles.  The whole output is compared.
+# Grids on the 256 x 128 tile (forced: the automatic choice gives these
+# shapes the 256 x 256 ping-pong tile) whose tile order walks several
+# weight-tile columns per group, the last group narrower: 107 and 13
+# columns with every tile of an XCD resident at once, 17 columns over
+# several rounds of resident tiles.  The whole output is compared.
 GROUPED_SHAPES = [(512, 27392, 64), (4096, 3328, 64), (8192, 4352, 64)]
 
 
 @pytest.mark.parametrize("m,n,k", GROUPED_SHAPES)
 def test_mfma_grouped_tile_order(m, n, k):
-    import int8_weight_quantized_amd as qw
-    assert qw.mfma_tile(m, n, k) == (256, 128)
     x, q, s = _small_case(m, n, k, seed=m + n + 5)
-    say("gemm mfma grouped order m=%d n=%d k=%d" % (m, n, k))
-    y = gpu_gemm(x, q, s, path=MFMA)
+    say("gemm mfma 256x128 grouped order m=%d n=%d k=%d" % (m, n, k))
+    y = gpu_gemm_tile(x, q, s, (256, 128))
     assert_gemm_close(y, oracle.gemm(x, q, s), "mfma grouped order %dx%dx%d" % (m, n, k))
 
 
