@@ -503,7 +503,7 @@ QW_API int qw_w8a8_gemm_auto_path(int64_t m, int64_t n, int64_t k);
  * qw_w8a8_gemm_tune -- per-shape autotuning of the W8A8 kernel choice, as
  * qw_w8a16_gemm_tune (same source passages, timing and bucket) over the
  * int8 kernels: the skinny kernel and the MFMA kernel with each of its
- * three tiles (256128, 256064, 128064).  The W8A8 records are kept apart
+ * four tiles (256256, 256128, 256064, 128064).  The W8A8 records are kept apart
  * from the W8A16 ones; qw_w8a8_gemm, qw_w8a8_gemm_auto_path and
  * qw_w8a8_gemm_mfma_tile use them.  Arguments, layout and errors as
  * qw_w8a8_gemm; y holds the winner's result; the call synchronizes with
@@ -520,11 +520,23 @@ QW_API int qw_w8a8_gemm_tuned_choice(int64_t m, int64_t n, int64_t k);
 /*
  * qw_w8a8_gemm_mfma_tile -- the output tile qw_w8a8_gemm uses for this
  * shape on the current HIP device (same encoding and rules as
- * qw_w8a16_gemm_mfma_tile, with the W8A8 kernels' occupancy: 256128,
- * 256064 or 128064; 128 x 128 is not used).  Returns -1
- * for shapes qw_w8a8_gemm rejects or when no HIP device is current.
+ * qw_w8a16_gemm_mfma_tile, the ping-pong tile 256256 included, with the
+ * W8A8 kernels' occupancy: 256256, 256128, 256064 or 128064; 128 x 128 is
+ * not used).  Returns -1 for shapes qw_w8a8_gemm rejects or when no HIP
+ * device is current.
  */
 QW_API int qw_w8a8_gemm_mfma_tile(int64_t m, int64_t n, int64_t k);
+
+/*
+ * qw_w8a8_gemm_tile -- the W8A8 MFMA GEMM with a given output tile
+ * (256256: the 8-wave ping-pong kernel, 256128, 256064 or 128064; BN * 1000
+ * + BM), for tests, benchmarks and callers that pin the kernel per shape.
+ * Arguments, result and errors as qw_w8a8_gemm, plus QW_ERROR_INVALID_VALUE
+ * for any other tile.
+ */
+QW_API qw_status qw_w8a8_gemm_tile(const int8_t *qx, const uint16_t *sx, const int8_t *q,
+                                   const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                                   int tile, void *stream);
 
 /*
  * Measurement aids.  Neither is part of the method; they put the GEMM

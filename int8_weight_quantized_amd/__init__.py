@@ -39,6 +39,7 @@ QUANTIZE_MAX_K = 65536
 MFMA_MAX_K = 8388608     # longest reduction of the LDS-tiled MFMA kernel
 PINGPONG_MAX_K = 4194304  # longest reduction of the 256 x 256 ping-pong tile
 MFMA_TILES = ((256, 256), (256, 128), (256, 64), (128, 128), (128, 64))  # (BN, BM)
+W8A8_TILES = ((256, 256), (256, 128), (256, 64), (128, 64))
 W8A8_MAX_K = 131072
 
 
@@ -94,6 +95,8 @@ def _load():
     lib.qw_w8a16_gemm_outliers_path.restype = ctypes.c_int
     lib.qw_w8a16_gemm_tile.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.qw_w8a16_gemm_tile.restype = ctypes.c_int
+    lib.qw_w8a8_gemm_tile.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.qw_w8a8_gemm_tile.restype = ctypes.c_int
     lib.qw_quantize_weights_asym.argtypes = [vp, i64, i64, vp, vp, vp, vp]
     lib.qw_quantize_weights_asym.restype = ctypes.c_int
     lib.qw_w8a16_gemm_asym.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
@@ -259,6 +262,11 @@ def w8a16_gemm_tile_raw(x_ptr: int, q_ptr: int, s_ptr: int, z_ptr: int, idx_ptr:
                         y_ptr: int, m: int, n: int, k: int, tile: int, stream: int = 0) -> int:
     return int(library().qw_w8a16_gemm_tile(x_ptr, q_ptr, s_ptr, z_ptr, idx_ptr, val_ptr, cap, y_ptr, m, n, k,
                                             int(tile), stream))
+
+
+def w8a8_gemm_tile_raw(qx_ptr: int, sx_ptr: int, q_ptr: int, s_ptr: int, y_ptr: int, m: int, n: int, k: int,
+                       tile: int, stream: int = 0) -> int:
+    return int(library().qw_w8a8_gemm_tile(qx_ptr, sx_ptr, q_ptr, s_ptr, y_ptr, m, n, k, int(tile), stream))
 
 
 def quantize_weights_asym_raw(w_ptr: int, n: int, k: int, q_ptr: int, s_ptr: int, z_ptr: int,
@@ -543,6 +551,20 @@ def w8a8_gemm(qx, sx, q, scales, out=None):
                        m, n, k, _stream_of(qx))
     if st != QW_SUCCESS:
         raise QwError(st, "qw_w8a8_gemm")
+    return y
+
+
+def w8a8_gemm_tile(qx, sx, q, scales, tile, out=None):
+    """The W8A8 MFMA GEMM with a given output tile (BN, BM), one of
+    W8A8_TILES; otherwise as w8a8_gemm."""
+    if tuple(tile) not in W8A8_TILES:
+        raise ValueError("tile must be one of %s, got %r" % (W8A8_TILES, tile))
+    device = _require_gpu(qx, "qx")
+    m, n, k, _, y = _validate_gemm(qx, q, scales, out, None, device, a8=True, sx=sx)
+    st = w8a8_gemm_tile_raw(qx.data_ptr(), sx.data_ptr(), q.data_ptr(), scales.data_ptr(), y.data_ptr(),
+                            m, n, k, tile[0] * 1000 + tile[1], _stream_of(qx))
+    if st != QW_SUCCESS:
+        raise QwError(st, "qw_w8a8_gemm_tile")
     return y
 
 

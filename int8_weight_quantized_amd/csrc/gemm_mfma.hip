@@ -682,37 +682,57 @@ constexpr int kBN = 256;                          // output channels per workgro
 constexpr int kBM = 256;                          // activation rows per workgroup
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kWBytes = kBN * kBK;                // int8 weight tile per stage
-constexpr int kXBytes = kBM * kBK * 2;            // fp16 activation tile per stage
-constexpr int kStage = kWBytes + kXBytes;
-constexpr int kWInstr = kWBytes / 1024 / kWaves;  // copies per wave per tile
-constexpr int kXInstr = kXBytes / 1024 / kWaves;
-constexpr int kCopies = kWInstr + kXInstr;
 constexpr int kSI = 2;                            // 32-channel MFMA tiles per wave
 constexpr int kSJ = 4;                            // 32-row MFMA tiles per wave
 constexpr int kGroupRows = kSJ * 32;              // activation rows per group
+constexpr int kWBytes = kBN * kBK;                // int8 weight tile per stage
 // epilogue image of one group's rows, [128][256] fp16 with rows padded by
 // 16 bytes; rows [0, 64) in stage 0's array, [64, 128) in stage 1's
 constexpr int kYRow = kBN * 2 + 16;
-static_assert(kWInstr * 1024 * kWaves == kWBytes && kXInstr * 1024 * kWaves == kXBytes, "copy split");
-static_assert(kXInstr % 2 == 0, "activation copies alternate between the two 8-row swizzle phases");
-static_assert((kGroupRows / 2) * kYRow <= kStage, "half a group's image fits a stage");
 static_assert(4 * kSI * 32 == kBN && 2 * kGroupRows == kBM, "wave layout");
+
+// A8: int8 activation codes (W8A8), laid out in LDS like the weight rows
+// (16 rows per 1 KiB copy); otherwise fp16 (8 rows per copy).
+template <bool A8>
+struct Cfg {
+    static constexpr int kXBytes = kBM * kBK * (A8 ? 1 : 2); // activation tile per stage
+    static constexpr int kStage = kWBytes + kXBytes;
+    static constexpr int kWInstr = kWBytes / 1024 / kWaves;  // copies per wave per tile
+    static constexpr int kXInstr = kXBytes / 1024 / kWaves;
+    static constexpr int kCopies = kWInstr + kXInstr;
+    // a stage array also holds half a group's epilogue image
+    static constexpr int kImageHalf = (kGroupRows / 2) * kYRow;
+    static constexpr int kStageAlloc = kStage > kImageHalf ? kStage : kImageHalf;
+    static_assert(kWInstr * 1024 * kWaves == kWBytes && kXInstr * 1024 * kWaves == kXBytes, "copy split");
+    static_assert(A8 || kXInstr % 2 == 0, "fp16 activation copies alternate between the two 8-row swizzle phases");
+};
 } // namespace pp
 
 static_assert(pp::kBM * kPingPongMaxK * 2 <= (int64_t(1) << 31), "buffer range");
 
-template <bool OL, bool ZP>
+// A8 (W8A8): xv holds int8 activation codes with one fp16 scale per row in
+// sx; the MFMA is v_mfma_i32_32x32x32_i8 (two per 64-wide k step and tile,
+// no casts), int32 accumulators, and the epilogue multiplies by S[n] * Sx[m].
+// Otherwise xv is fp16 and sx unused.
+template <bool A8, bool OL, bool ZP>
 __global__ __launch_bounds__(pp::kThreads) void mfma_pp_kernel(
-    const uint16_t *__restrict__ x, const int8_t *__restrict__ q, const uint16_t *__restrict__ scales,
-    const int8_t *__restrict__ zeros, OutlierList ol, uint16_t *__restrict__ y, int m, int n, int k,
-    int tiles_m, int tiles_n, int group)
+    const void *__restrict__ xv, const uint16_t *__restrict__ sx, const int8_t *__restrict__ q,
+    const uint16_t *__restrict__ scales, const int8_t *__restrict__ zeros, OutlierList ol,
+    uint16_t *__restrict__ y, int m, int n, int k, int tiles_m, int tiles_n, int group)
 {
     using namespace pp;
-    __shared__ __attribute__((aligned(1024))) uint8_t ring0[kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t ring1[kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t ring2[kStage];
+    using C = Cfg<A8>;
+    constexpr int kStage = C::kStage;
+    constexpr int kWInstr = C::kWInstr;
+    constexpr int kXInstr = C::kXInstr;
+    constexpr int kCopies = C::kCopies;
+    static_assert(!A8 || (!OL && !ZP), "W8A8 takes symmetric codes without side lists");
+    const uint16_t *__restrict__ x = static_cast<const uint16_t *>(xv);
+    __shared__ __attribute__((aligned(1024))) uint8_t ring0[C::kStageAlloc];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring1[C::kStageAlloc];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring2[C::kStageAlloc];
     __shared__ __attribute__((aligned(16))) float scale_lds[kBN];
+    __shared__ __attribute__((aligned(16))) float xscale_lds[A8 ? kBM : 1];
     // OL: the workgroup's side lists, (column, value / S as float bits) per
     // slot; unused slots hold column INT_MAX
     __shared__ __attribute__((aligned(16))) int2v ol_lds[OL ? kBN * kMfmaOutlierSlots : 1];
@@ -752,18 +772,23 @@ __global__ __launch_bounds__(pp::kThreads) void mfma_pp_kernel(
     const int wchunk = (lane % 4) ^ wslot(lane / 4);
     const int xchunk_even = (lane % 8) ^ xslot(lane / 8);
     const int xchunk_odd = (lane % 8) ^ xslot(8 + lane / 8);
+    constexpr int kXE = A8 ? 1 : 2; // bytes per activation element
     const uint32_t woff = (uint32_t)((wave * kWInstr * 16 + lane / 4) * k + wchunk * 16);
-    const uint32_t xrow0 = (uint32_t)(wave * kXInstr * 8 + lane / 8);
-    const uint32_t xoff_even = (xrow0 * k + xchunk_even * 8) * 2;
-    const uint32_t xoff_odd = ((xrow0 + 8) * k + xchunk_odd * 8) * 2;
+    // A8: activation copy i covers rows 16 i below copy 0, like the weight
+    const uint32_t xrow0 = (uint32_t)(A8 ? wave * kXInstr * 16 + lane / 4 : wave * kXInstr * 8 + lane / 8);
+    const uint32_t xoff_even = A8 ? xrow0 * k + wchunk * 16 : (xrow0 * k + xchunk_even * 8) * 2;
+    const uint32_t xoff_odd = A8 ? xoff_even : ((xrow0 + 8) * k + xchunk_odd * 8) * 2;
+    // (the scalar offset of activation copy i, written out at each use: as a
+    // lambda or a template helper it kept the host pass from emitting the
+    // kernels' launch stubs)
     const int8_t *wtile = q + (int64_t)n0 * k;
-    const uint16_t *xtile = x + (int64_t)m0 * k;
+    const uint8_t *xtile = static_cast<const uint8_t *>(xv) + (int64_t)m0 * k * kXE;
     const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int8_t *>(wtile), (short)0,
         static_cast<int>(static_cast<uint32_t>(min((int64_t)kBN, (int64_t)(n - n0)) * k)), kBufferFlags);
     const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(xtile), (short)0,
-        static_cast<int>(static_cast<uint32_t>(min((int64_t)kBM, (int64_t)(m - m0)) * k * 2)), kBufferFlags);
+        const_cast<uint8_t *>(xtile), (short)0,
+        static_cast<int>(static_cast<uint32_t>(min((int64_t)kBM, (int64_t)(m - m0)) * k * kXE)), kBufferFlags);
 
     // this wave's share of the copies of tile kt into stage array st
     auto issue_full = [&](int kt, uint8_t *st) {
@@ -776,7 +801,7 @@ __global__ __launch_bounds__(pp::kThreads) void mfma_pp_kernel(
         for (int i = 0; i < kXInstr; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 xrsrc, (lds_ptr_t)(st + kWBytes + (wave * kXInstr + i) * 1024), 16,
-                (int)((i & 1) ? xoff_odd : xoff_even), (k0 + (i & ~1) * 8 * k) * 2, 0, 0);
+                (int)((i & 1) ? xoff_odd : xoff_even), (A8 ? k0 + i * 16 * k : (k0 + (i & ~1) * 8 * k) * 2), 0, 0);
     };
     // The ragged last tile: activation chunks past k are zero-filled, so
     // whatever the weight chunks past k hold (codes of the next row, or
@@ -790,11 +815,10 @@ __global__ __launch_bounds__(pp::kThreads) void mfma_pp_kernel(
 #pragma unroll
         for (int i = 0; i < kXInstr; ++i) {
             uint8_t *dst = st + kWBytes + (wave * kXInstr + i) * 1024;
-            const int gk = k0 + ((i & 1) ? xchunk_odd : xchunk_even) * 8;
+            const int gk = k0 + (A8 ? wchunk * 16 : ((i & 1) ? xchunk_odd : xchunk_even) * 8);
             if (gk < k)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, (lds_ptr_t)dst, 16,
-                                                         (int)((i & 1) ? xoff_odd : xoff_even),
-                                                         (k0 + (i & ~1) * 8 * k) * 2, 0, 0);
+                                                         (int)((i & 1) ? xoff_odd : xoff_even), (A8 ? k0 + i * 16 * k : (k0 + (i & ~1) * 8 * k) * 2), 0, 0);
             else
                 *reinterpret_cast<u32x4_t *>(dst + lane * 16) = (u32x4_t){0u, 0u, 0u, 0u};
         }
@@ -817,10 +841,13 @@ __global__ __launch_bounds__(pp::kThreads) void mfma_pp_kernel(
     // ahead of the MFMAs.  The builtin beside it tells the compiler's own
     // wait-count bookkeeping what has completed.
     auto wait_tile = [&](int u, auto full) {
-        static_assert(kCopies == 6, "the wait below names the batch size");
+        static_assert(kCopies == 6 || kCopies == 4, "the wait below names the batch size");
         __builtin_amdgcn_sched_barrier(0);
         if (decltype(full)::value || u + 1 < full_tiles) {
-            __asm__ __volatile__("s_waitcnt vmcnt(6)" ::: "memory");
+            if constexpr (kCopies == 6)
+                __asm__ __volatile__("s_waitcnt vmcnt(6)" ::: "memory");
+            else
+                __asm__ __volatile__("s_waitcnt vmcnt(4)" ::: "memory");
             QW_WAIT_VMCNT(kCopies);
         } else {
             __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");
@@ -846,14 +873,17 @@ __global__ __launch_bounds__(pp::kThreads) void mfma_pp_kernel(
     const int wrow = nw * (kSI * 32) + lrow; // + 32 i
     const int w_off0 = wrow * kBK + 16 * ((2 * lgrp) ^ wslot(wrow));
     const int xrow = grp * kGroupRows + lrow; // + 32 j
-    const int x_off0 = kWBytes + xrow * 2 * kBK + 16 * ((4 * lgrp) ^ xslot(xrow));
+    // A8: the activation rows are read like the weight rows (chunks 2g, 2g+1)
+    const int x_off0 = A8 ? kWBytes + xrow * kBK + 16 * ((2 * lgrp) ^ wslot(xrow))
+                          : kWBytes + xrow * 2 * kBK + 16 * ((4 * lgrp) ^ xslot(xrow));
 
-    float16v acc[kSI][kSJ];
+    using acc_t = std::conditional_t<A8, int16v, float16v>;
+    acc_t acc[kSI][kSJ];
 #pragma unroll
     for (int i = 0; i < kSI; ++i)
 #pragma unroll
         for (int j = 0; j < kSJ; ++j)
-            acc[i][j] = (float16v){};
+            acc[i][j] = (acc_t){};
     half2_t zbias[kSI];
 #pragma unroll
     for (int i = 0; i < kSI; ++i) {
@@ -867,7 +897,26 @@ __global__ __launch_bounds__(pp::kThreads) void mfma_pp_kernel(
     // overlap them and stretched the MFMA phase by about 40%).
     half8_t a[kSI][4];
     half8_t b[kSJ][4];
+    // A8: the 16 codes of chunk 2g + s per lane, weight (A) and activation
+    // (B) operands of v_mfma_i32_32x32x32_i8 alike, as in the 4-wave kernel
+    u32x4_t a8[kSI][2], b8[kSJ][2];
     auto load = [&](const uint8_t *st) {
+        if constexpr (A8) {
+            int w_off1, x_off1;
+            __asm__ __volatile__("v_xor_b32 %0, 16, %1" : "=v"(w_off1) : "v"(w_off0));
+            __asm__ __volatile__("v_xor_b32 %0, 16, %1" : "=v"(x_off1) : "v"(x_off0));
+#pragma unroll
+            for (int i = 0; i < kSI; ++i) {
+                a8[i][0] = *reinterpret_cast<const u32x4_t *>(st + w_off0 + i * 32 * kBK);
+                a8[i][1] = *reinterpret_cast<const u32x4_t *>(st + w_off1 + i * 32 * kBK);
+            }
+#pragma unroll
+            for (int j = 0; j < kSJ; ++j) {
+                b8[j][0] = *reinterpret_cast<const u32x4_t *>(st + x_off0 + j * 32 * kBK);
+                b8[j][1] = *reinterpret_cast<const u32x4_t *>(st + x_off1 + j * 32 * kBK);
+            }
+            return;
+        }
         int w_off1, x_off[4];
         x_off[0] = x_off0;
         // (volatile: computed here, in the memory phase, rather than hoisted
@@ -896,13 +945,25 @@ __global__ __launch_bounds__(pp::kThreads) void mfma_pp_kernel(
         }
     };
     auto compute = [&]() {
+        if constexpr (A8) {
 #pragma unroll
-        for (int sidx = 0; sidx < 4; ++sidx)
+            for (int sidx = 0; sidx < 2; ++sidx)
 #pragma unroll
-            for (int i = 0; i < kSI; ++i)
+                for (int i = 0; i < kSI; ++i)
 #pragma unroll
-                for (int j = 0; j < kSJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][sidx], b[j][sidx], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < kSJ; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(int4v, a8[i][sidx]),
+                                                                         __builtin_bit_cast(int4v, b8[j][sidx]),
+                                                                         acc[i][j], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int sidx = 0; sidx < 4; ++sidx)
+#pragma unroll
+                for (int i = 0; i < kSI; ++i)
+#pragma unroll
+                    for (int j = 0; j < kSJ; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i][sidx], b[j][sidx], acc[i][j], 0, 0, 0);
+        }
     };
     // memory phase of tile t (stage S): copies of tile t + 2, then operands
     auto mem = [&](int t, auto s, auto full) {
@@ -919,6 +980,10 @@ __global__ __launch_bounds__(pp::kThreads) void mfma_pp_kernel(
     issue(1, ring1, partial_t{});
     for (int c = tid; c < kBN; c += kThreads)
         scale_lds[c] = n0 + c < n ? f16_bits_to_f32(scales[n0 + c]) : 0.0f;
+    if constexpr (A8) {
+        for (int r = tid; r < kBM; r += kThreads)
+            xscale_lds[r] = m0 + r < m ? f16_bits_to_f32(sx[m0 + r]) : 0.0f;
+    }
     if constexpr (OL) {
         for (int e = tid; e < kBN * kMfmaOutlierSlots; e += kThreads) {
             const int c = e / kMfmaOutlierSlots, slot = e % kMfmaOutlierSlots;
@@ -986,10 +1051,19 @@ __global__ __launch_bounds__(pp::kThreads) void mfma_pp_kernel(
                 for (int j = 0; j < kSJ; ++j) {
                     uint8_t *img = j < kSJ / 2 ? ring0 + (j * 32 + lrow) * kYRow
                                                : ring1 + (j * 32 - kGroupRows / 2 + lrow) * kYRow;
-                    const uint32_t o0 = f32_to_f16_bits(acc[i][j][4 * qd + 0] * sc[0]);
-                    const uint32_t o1 = f32_to_f16_bits(acc[i][j][4 * qd + 1] * sc[1]);
-                    const uint32_t o2 = f32_to_f16_bits(acc[i][j][4 * qd + 2] * sc[2]);
-                    const uint32_t o3 = f32_to_f16_bits(acc[i][j][4 * qd + 3] * sc[3]);
+                    // W8A16: acc * S[n].  W8A8: float(acc) * (S[n] * Sx[m]);
+                    // the product of two fp16 scales is exact in fp32.
+                    auto val = [&](int e) -> float {
+                        if constexpr (A8)
+                            return (float)acc[i][j][4 * qd + e] *
+                                   (sc[e] * xscale_lds[grp * kGroupRows + j * 32 + lrow]);
+                        else
+                            return acc[i][j][4 * qd + e] * sc[e];
+                    };
+                    const uint32_t o0 = f32_to_f16_bits(val(0));
+                    const uint32_t o1 = f32_to_f16_bits(val(1));
+                    const uint32_t o2 = f32_to_f16_bits(val(2));
+                    const uint32_t o3 = f32_to_f16_bits(val(3));
                     *reinterpret_cast<u32x2_t *>(img + nl * 2) = (u32x2_t){o0 | (o1 << 16), o2 | (o3 << 16)};
                 }
             }
@@ -1207,7 +1281,7 @@ bool pp_fills(int64_t m, int64_t n, int64_t k)
 template <bool A8>
 int tile_choice(int64_t m, int64_t n, int64_t k, bool pp = true)
 {
-    if (!A8 && pp && pp_fills(m, n, k))
+    if (pp && pp_fills(m, n, k))
         return 256256;
     // largest tile first (more reuse per byte staged); 256 x 64 before
     // 128 x 128 (same area, half the activation bytes per tile)
@@ -1226,8 +1300,10 @@ int tile_choice(int64_t m, int64_t n, int64_t k, bool pp = true)
 // Ping-pong launch: one 512-thread workgroup per 256 x 256 tile, one per CU
 // (144 KiB of LDS).  Grouped tile order as for the 4-wave tiles, with one
 // resident workgroup per CU.
-hipError_t launch_pp(const uint16_t *x, const int8_t *q, const uint16_t *scales, const int8_t *zeros,
-                     OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k, hipStream_t stream)
+template <bool A8>
+hipError_t launch_pp(const void *x, const uint16_t *sx, const int8_t *q, const uint16_t *scales,
+                     const int8_t *zeros, OutlierList ol, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                     hipStream_t stream)
 {
     const int64_t tiles_m = (m + pp::kBM - 1) / pp::kBM;
     const int64_t tiles_n = (n + pp::kBN - 1) / pp::kBN;
@@ -1237,18 +1313,27 @@ hipError_t launch_pp(const uint16_t *x, const int8_t *q, const uint16_t *scales,
     const int64_t share = (blocks + 7) / 8;
     const int64_t resident = std::max<int64_t>(1, (int64_t)device_cu_count() / 8);
     const double r = (double)std::max<int64_t>(1, std::min(share, resident));
-    int64_t a = std::llround(std::sqrt(r * pp::kBM * 2 / pp::kBN));
+    int64_t a = std::llround(std::sqrt(r * pp::kBM * (A8 ? 1 : 2) / pp::kBN));
     a = std::max<int64_t>(a, ((int64_t)r + tiles_m - 1) / tiles_m);
     const int group = (int)std::max<int64_t>(1, std::min(a, tiles_n));
-    auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(pp::kThreads), 0, stream, x, q, scales, zeros, ol, y,
-                           (int)m, (int)n, (int)k, (int)tiles_m, (int)tiles_n, group);
-        return hipGetLastError();
-    };
-    // side lists come with symmetric codes only (as in the 4-wave kernels)
-    if (ol.idx != nullptr)
-        return go(mfma_pp_kernel<true, false>);
-    return zeros != nullptr ? go(mfma_pp_kernel<false, true>) : go(mfma_pp_kernel<false, false>);
+#define QW_PP_LAUNCH(A, O, Z)                                                                                   \
+    hipLaunchKernelGGL((mfma_pp_kernel<A, O, Z>), dim3((unsigned)blocks), dim3(pp::kThreads), 0, stream, x, sx, q,  \
+                       scales, zeros, ol, y, (int)m, (int)n, (int)k, (int)tiles_m, (int)tiles_n, group)
+    if constexpr (A8) {
+        if (ol.idx != nullptr || zeros != nullptr)
+            return hipErrorInvalidValue;
+        QW_PP_LAUNCH(true, false, false);
+    } else {
+        // side lists come with symmetric codes only (as in the 4-wave kernels)
+        if (ol.idx != nullptr)
+            QW_PP_LAUNCH(false, true, false);
+        else if (zeros != nullptr)
+            QW_PP_LAUNCH(false, false, true);
+        else
+            QW_PP_LAUNCH(false, false, false);
+    }
+#undef QW_PP_LAUNCH
+    return hipGetLastError();
 }
 
 template <bool A8>
@@ -1261,9 +1346,7 @@ hipError_t launch_tiles(const void *x, const uint16_t *sx, const int8_t *q, cons
     const int tile = forced_tile != 0 ? forced_tile : tile_choice<A8>(m, n, k, ol.idx == nullptr);
     switch (tile) {
     case 256256:
-        if constexpr (!A8)
-            return launch_pp(static_cast<const uint16_t *>(x), q, scales, zeros, ol, y, m, n, k, stream);
-        return hipErrorInvalidValue;
+        return launch_pp<A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
     case 256128:
         return launch_dma<4, 256, 128, A8>(x, sx, q, scales, zeros, ol, y, m, n, k, stream);
     case 256064:
@@ -1284,9 +1367,9 @@ int mfma_tile_choice(int64_t m, int64_t n, int64_t k)
     return tile_choice<false>(m, n, k);
 }
 
-int w8a8_tile_choice(int64_t m, int64_t n)
+int w8a8_tile_choice(int64_t m, int64_t n, int64_t k)
 {
-    return tile_choice<true>(m, n, 0);
+    return tile_choice<true>(m, n, k);
 }
 
 hipError_t launch_mfma_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
@@ -1311,7 +1394,7 @@ hipError_t launch_w8a8_gemm_tile(int tile, const int8_t *qx, const uint16_t *sx,
                                  const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
                                  hipStream_t stream)
 {
-    if (tile != 256128 && tile != 256064 && tile != 128064)
+    if (tile != 256256 && tile != 256128 && tile != 256064 && tile != 128064)
         return hipErrorInvalidValue;
     return launch_tiles<true>(qx, sx, q, scales, nullptr, OutlierList{nullptr, nullptr, 0}, y, m, n, k, stream,
                               tile);

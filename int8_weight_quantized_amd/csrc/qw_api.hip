@@ -517,6 +517,20 @@ QW_API qw_status qw_w8a8_gemm_path(const int8_t *qx, const uint16_t *sx, const i
     return launch_status(qw::launch_w8a8_gemm(qx, sx, q, scales, y, m, n, k, s));
 }
 
+QW_API qw_status qw_w8a8_gemm_tile(const int8_t *qx, const uint16_t *sx, const int8_t *q,
+                                   const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
+                                   int tile, void *stream)
+{
+    if (tile != 256256 && tile != 256128 && tile != 256064 && tile != 128064)
+        return QW_ERROR_INVALID_VALUE;
+    bool noop = false;
+    const qw_status st = check_w8a8_args(qx, sx, q, scales, y, m, n, k, noop);
+    if (st != QW_SUCCESS || noop)
+        return st;
+    return launch_status(
+        qw::launch_w8a8_gemm_tile(tile, qx, sx, q, scales, y, m, n, k, static_cast<hipStream_t>(stream)));
+}
+
 QW_API qw_status qw_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t *q,
                               const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
                               void *stream)
@@ -544,7 +558,7 @@ QW_API int qw_w8a8_gemm_mfma_tile(int64_t m, int64_t n, int64_t k)
     const int tuned = qw::tuned_choice(m, n, k, true);
     if (tuned >= 0 && tuned / qw::kChoicePath == QW_PATH_MFMA)
         return tuned % qw::kChoicePath;
-    return qw::w8a8_tile_choice(m, n);
+    return qw::w8a8_tile_choice(m, n, k);
 }
 
 QW_API qw_status qw_w8a8_gemm_tune(const int8_t *qx, const uint16_t *sx, const int8_t *q, const uint16_t *scales,

@@ -90,7 +90,7 @@ static_assert(256 * kPingPongMaxK * 2 <= (int64_t(1) << 31), "ping-pong buffer r
 hipError_t launch_w8a8_gemm(const int8_t *qx, const uint16_t *sx, const int8_t *q,
                             const uint16_t *scales, uint16_t *y, int64_t m, int64_t n, int64_t k,
                             hipStream_t stream);
-int w8a8_tile_choice(int64_t m, int64_t n);
+int w8a8_tile_choice(int64_t m, int64_t n, int64_t k);
 // W8A8 skinny kernel (int8 MFMA on the skinny kernel's layout) for a few
 // activation rows, any m, n, k with k % 16 == 0.
 hipError_t launch_w8a8_skinny(const int8_t *qx, const uint16_t *sx, const int8_t *q, const uint16_t *scales,

@@ -169,13 +169,13 @@ hipError_t tune_gemm(const uint16_t *x, const int8_t *q, const uint16_t *scales,
 hipError_t tune_w8a8(const int8_t *qx, const uint16_t *sx, const int8_t *q, const uint16_t *scales, uint16_t *y,
                      int64_t m, int64_t n, int64_t k, hipStream_t stream, int &best)
 {
-    // the int8 kernels: the skinny kernel and the three W8A8 MFMA tiles (the
+    // the int8 kernels: the skinny kernel and the four W8A8 MFMA tiles (the
     // int8 128 x 128 tile is not built)
-    int cands[4];
+    int cands[5];
     int nc = 0;
     if (m <= 16 * 65535)
         cands[nc++] = QW_PATH_SKINNY * kChoicePath;
-    for (int tile : {256128, 256064, 128064})
+    for (int tile : {256256, 256128, 256064, 128064})
         cands[nc++] = QW_PATH_MFMA * kChoicePath + tile;
     return time_candidates(cands, nc, stream, [&](int choice) {
         return launch_choice_w8a8(choice, qx, sx, q, scales, y, m, n, k, stream);

@@ -144,3 +144,21 @@ def gpu_gemm_tile(x: np.ndarray, q: np.ndarray, s_bits: np.ndarray, tile, zeros=
                                 tile[0] * 1000 + tile[1], int(torch.cuda.current_stream().cuda_stream))
     assert st == 0, qw.status_string(st)
     return host(yd).view(np.float16)
+
+
+def gpu_w8a8_tile(qx: np.ndarray, sx_bits: np.ndarray, q: np.ndarray, s_bits: np.ndarray, tile):
+    """W8A8 MFMA GEMM with a forced output tile (BN, BM) through the C ABI;
+    returns Y as float16."""
+    import int8_weight_quantized_amd as qw
+    torch = torch_mod()
+    m, k = qx.shape
+    n = q.shape[0]
+    qxd = dev(np.ascontiguousarray(qx, dtype=np.int8))
+    sxd = dev(np.ascontiguousarray(sx_bits, dtype=np.uint16).view(np.int16))
+    qd = dev(np.ascontiguousarray(q, dtype=np.int8))
+    sd = dev(np.ascontiguousarray(s_bits, dtype=np.uint16).view(np.int16))
+    yd = torch.full((m, n), 0x7e00, dtype=torch.int16, device="cuda:0")  # NaN canary
+    st = qw.w8a8_gemm_tile_raw(qxd.data_ptr(), sxd.data_ptr(), qd.data_ptr(), sd.data_ptr(), yd.data_ptr(),
+                               m, n, k, tile[0] * 1000 + tile[1], int(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, qw.status_string(st)
+    return host(yd).view(np.float16)

@@ -182,6 +182,7 @@ def test_public_calls_refuse_cpu_tensors_before_the_library():
         lambda: qw.w8a8_gemm(t((M, K), torch.int8, cpu), t((M,), torch.float16, cpu), q, s),
         lambda: qw.quantize_activations(x),
         lambda: qw.w8a16_gemm_tile(x, q, s, (256, 256)),
+        lambda: qw.w8a8_gemm_tile(t((M, K), torch.int8, cpu), t((M,), torch.float16, cpu), q, s, (256, 256)),
     ]
     for call in calls:
         with pytest.raises(ValueError, match="GPU"):
@@ -199,3 +200,7 @@ def test_gemm_tile_argument_rejections():
         qw.w8a16_gemm_tile(x, q, s, (256, 256), zeros=t((N,), torch.int8),
                            outliers=(t((N, 1), torch.int32), t((N, 1), torch.float32)))
     assert set(qw.MFMA_TILES) == {(256, 256), (256, 128), (256, 64), (128, 128), (128, 64)}
+    qx = t((M, K), torch.int8)
+    for tile in ((128, 128), (512, 256)):
+        with pytest.raises(ValueError, match="tile"):
+            qw.w8a8_gemm_tile(qx, t((M,), torch.float16), q, s, tile)

@@ -226,6 +226,18 @@ def test_gemm_tile_rejects(args, status):
     assert qw.w8a16_gemm_tile_raw(*args) == status
 
 
+@pytest.mark.parametrize("args,status", [
+    ((A, B, C, D, E, 4, 4, 16, 128128), qw.QW_ERROR_INVALID_VALUE),     # not a W8A8 tile
+    ((A, B, C, D, E, 4, 4, 16, 0), qw.QW_ERROR_INVALID_VALUE),          # tile 0
+    ((A, B, C, D, E, -1, 4, 16, 256256), qw.QW_ERROR_INVALID_VALUE),    # m < 0
+    ((0, B, C, D, E, 4, 4, 16, 256256), qw.QW_ERROR_INVALID_VALUE),     # null qx
+    ((A, B, C, D, E, 4, 4, 24, 256256), qw.QW_ERROR_UNSUPPORTED),       # k % 16
+    ((A + 8, B, C, D, E, 4, 4, 16, 256256), qw.QW_ERROR_MISALIGNED),    # misaligned qx
+])
+def test_w8a8_gemm_tile_rejects(args, status):
+    assert qw.w8a8_gemm_tile_raw(*args) == status
+
+
 def test_gemm_tile_empty_is_noop():
     assert qw.w8a16_gemm_tile_raw(0, 0, 0, 0, 0, 0, 0, 0, 0, 4, 16, 256256) == qw.QW_SUCCESS
 

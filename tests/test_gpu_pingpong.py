@@ -1,6 +1,7 @@
 """GPU parity of the 256 x 256 ping-pong MFMA tile (8 waves, two wave groups
 taking turns at the matrix cores, three LDS stages), forced through
-qw_w8a16_gemm_tile and reached through the automatic kernel choice.
+qw_w8a16_gemm_tile / qw_w8a8_gemm_tile and reached through the automatic
+kernel choice.
 
 Cases span one to several tiles with ragged tails in m (the second wave
 group's rows partly or wholly past m), n (partial weight tiles, rows not a
@@ -17,7 +18,7 @@ import pytest
 
 import oracle
 import synthetic
-from gpu_util import assert_gemm_close, gpu_gemm, gpu_gemm_tile, say
+from gpu_util import assert_gemm_close, assert_w8a8_close, gpu_gemm, gpu_gemm_tile, gpu_w8a8_tile, say
 
 pytestmark = pytest.mark.gpu
 
@@ -158,3 +159,46 @@ def test_pingpong_choice():
     assert qw.mfma_tile(129, 40960, 4096) != PP
     assert qw.mfma_tile(512, 27392, qw.PINGPONG_MAX_K + 16) != PP
 
+
+
+# ---- W8A8 (int8 activation codes, v_mfma_i32_32x32x32_i8) ----
+
+def _codes(m, n, k, seed):
+    x = synthetic.random_x(m, k, seed)
+    w = synthetic.random_w(n, k, seed + 1)
+    qx, sx, _ = oracle.quantize(x.astype(np.float32), 100.0)
+    q, s, _ = oracle.quantize(w, 100.0)
+    return qx, sx, q, s
+
+
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_pingpong_w8a8_shapes(m, n, k):
+    qx, sx, q, s = _codes(m, n, k, seed=5 * m + n + k)
+    say("w8a8 pingpong m=%d n=%d k=%d" % (m, n, k))
+    y = gpu_w8a8_tile(qx, sx, q, s, PP)
+    assert_w8a8_close(y, oracle.w8a8_gemm(qx, sx, q, s), "w8a8 pingpong %dx%dx%d" % (m, n, k))
+
+
+@pytest.mark.parametrize("m,n,k", [(256, 256, 64), (300, 522, 1040), (640, 4100, 272)])
+def test_pingpong_w8a8_exact_arithmetic_bitexact(m, n, k):
+    """|acc| <= k * 127^2 < 2^24 and power-of-two scales: Y is the binary16
+    rounding of the exact value, bit for bit (one row and one column
+    saturated)."""
+    rng = np.random.default_rng(m + 2 * n + k)
+    qx = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+    q = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+    sx = (2.0 ** (-rng.integers(0, 8, size=m))).astype(np.float16).view(np.uint16)
+    s = (2.0 ** (-rng.integers(10, 15, size=n))).astype(np.float16).view(np.uint16)
+    qx[0, :] = 127
+    q[0, :] = 127
+    say("w8a8 pingpong exact m=%d n=%d k=%d" % (m, n, k))
+    y = gpu_w8a8_tile(qx, sx, q, s, PP)
+    assert np.array_equal(y.view(np.uint16), oracle.f64_to_f16_bits(oracle.w8a8_gemm(qx, sx, q, s)))
+
+
+@pytest.mark.parametrize("m,n,k", [(512, 27392, 64), (4096, 3328, 64)])
+def test_pingpong_w8a8_grouped_tile_order(m, n, k):
+    qx, sx, q, s = _codes(m, n, k, seed=m + n + 1)
+    say("w8a8 pingpong grouped m=%d n=%d k=%d" % (m, n, k))
+    y = gpu_w8a8_tile(qx, sx, q, s, PP)
+    assert_w8a8_close(y, oracle.w8a8_gemm(qx, sx, q, s), "w8a8 pingpong grouped %dx%dx%d" % (m, n, k))

@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import synthetic
-from gpu_util import assert_w8a8_close, gpu_quantize, gpu_w8a8, say
+from gpu_util import assert_w8a8_close, gpu_quantize, gpu_w8a8, gpu_w8a8_tile, say
 
 pytestmark = pytest.mark.gpu
 
@@ -76,8 +76,12 @@ def test_w8a8_grouped_tile_order(m, n, k):
     assert qw.w8a8_tile(m, n, k)[0] == 256
     qx, sx, q, s = _codes(m, n, k, seed=m + n + 9)
     say("w8a8 gemm mfma grouped order m=%d n=%d k=%d" % (m, n, k))
-    assert_w8a8_close(gpu_w8a8(qx, sx, q, s, MFMA), oracle.w8a8_gemm(qx, sx, q, s),
-                      "w8a8 grouped order %dx%dx%d" % (m, n, k))
+    ref = oracle.w8a8_gemm(qx, sx, q, s)
+    assert_w8a8_close(gpu_w8a8(qx, sx, q, s, MFMA), ref, "w8a8 grouped order %dx%dx%d" % (m, n, k))
+    # the 256 x 128 tile on the same grids (the automatic choice gives them
+    # the ping-pong tile)
+    say("w8a8 gemm mfma 256x128 grouped order m=%d n=%d k=%d" % (m, n, k))
+    assert_w8a8_close(gpu_w8a8_tile(qx, sx, q, s, (256, 128)), ref, "w8a8 256x128 grouped %dx%dx%d" % (m, n, k))
 
 
 @pytest.mark.parametrize("path", [0, SKINNY, MFMA])
@@ -91,7 +95,7 @@ def test_w8a8_shapes(m, n, k, path):
 
 TILE_SHAPES = [(512, 27392, 256), (2048, 4608, 128), (256, 27392, 128), (384, 13824, 128),
                (96, 27392, 256), (1024, 9216, 128), (4096, 4096, 64), (320, 6144, 144),
-               (384, 32768, 128), (129, 40960, 64), (200, 16384, 80)]
+               (384, 32768, 128), (129, 40960, 64), (200, 16384, 80), (1088, 9216, 128)]
 
 
 def test_w8a8_every_tile_shape():
@@ -107,8 +111,8 @@ def test_w8a8_every_tile_shape():
         assert_w8a8_close(y[mi, ni], oracle.w8a8_gemm_sampled(qx, sx, q, s, mi, ni),
                           "w8a8 tile %s %dx%dx%d (sampled)" % (tile, m, n, k))
         assert np.all(np.isfinite(y.astype(np.float32))), "non-finite output outside the sample"
-    # the W8A8 kernel has three tile shapes (no 128 x 128)
-    assert seen == {(256, 128), (256, 64), (128, 64)}, "tiles exercised: %s" % sorted(seen)
+    # the W8A8 kernel has four tile shapes (no 128 x 128)
+    assert seen == {(256, 256), (256, 128), (256, 64), (128, 64)}, "tiles exercised: %s" % sorted(seen)
 
 
 @pytest.mark.parametrize("path", [SKINNY, MFMA])
