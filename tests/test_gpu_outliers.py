@@ -134,6 +134,56 @@ def test_gemm_outliers_mfma_tiles():
         assert np.all(np.isfinite(y.astype(np.float32)))
 
 
+# Every 4-wave MFMA tile forced, with side lists of one to four slots per
+# row, rows of 512 and 1024 codes (the FFN's), ragged m and n: against the
+# oracle, and bit-exact on exact inputs.
+FORCED_TILES = [(256, 128), (256, 64), (128, 128), (128, 64)]
+
+
+@pytest.mark.parametrize("tile", FORCED_TILES)
+@pytest.mark.parametrize("m,n,k,cap", [(300, 520, 1024, 1), (97, 333, 512, 3), (256, 256, 1024, 3)])
+def test_gemm_outliers_forced_tiles(tile, m, n, k, cap):
+    from gpu_util import gpu_gemm_tile
+    x = synthetic.random_x(m, k, m + k + cap)
+    w = _weights(n, k, n + k + cap, frac=0.003)
+    pct = 99.99 if cap == 1 else 99.7
+    q, s, idx, val = oracle.quantize_outliers(w, pct, cap=max(cap, oracle.outlier_capacity(k, pct)))
+    idx, val = np.ascontiguousarray(idx), np.ascontiguousarray(val)
+    say("gemm outliers forced tile=%s m=%d n=%d k=%d cap=%d" % (tile, m, n, k, idx.shape[1]))
+    y = gpu_gemm_tile(x, q, s, tile, idx=idx, val=val)
+    assert_gemm_close(y, oracle.gemm_outliers(x, q, s, idx, val), "outliers forced tile %s %dx%dx%d" % (tile, m, n, k))
+    # the automatic MFMA tile on the same data
+    y_auto = gpu_gemm_outliers(x, q, s, idx, val, MFMA)
+    assert np.all(np.isfinite(y.astype(np.float32)))
+    assert_gemm_close(y, y_auto.astype(np.float64), "forced tile vs auto %s" % (tile,))
+
+
+@pytest.mark.parametrize("tile", FORCED_TILES)
+def test_gemm_outliers_forced_tiles_exact(tile):
+    """Exact arithmetic (as below) through the forced tiles at k = 1024 and
+    512: bit-exact against the oracle."""
+    from gpu_util import gpu_gemm_tile
+    for (m, n, k) in ((130, 300, 1024), (64, 64, 512)):
+        rng = np.random.default_rng(m + n + k + tile[0] + tile[1])
+        x = rng.integers(-1, 2, size=(m, k)).astype(np.float16)
+        q = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+        e = rng.integers(0, 11, size=n)
+        s = (2.0 ** (-e)).astype(np.float16)
+        cap = 4
+        idx = np.full((n, cap), -1, dtype=np.int32)
+        val = np.zeros((n, cap), dtype=np.float32)
+        for r in range(n):
+            c = int(rng.integers(0, cap + 1))
+            cols = np.sort(rng.choice(k, size=c, replace=False))
+            idx[r, :c] = cols
+            val[r, :c] = rng.integers(-4000, 4000, size=c) * (float(s[r]) / 8)
+            q[r, cols] = 0
+        say("gemm outliers forced tile exact tile=%s m=%d n=%d k=%d" % (tile, m, n, k))
+        y = gpu_gemm_tile(x, q, s.view(np.uint16), tile, idx=idx, val=val)
+        want = oracle.f64_to_f16_bits(oracle.gemm_outliers(x, q, s.view(np.uint16), idx, val))
+        assert np.array_equal(y.view(np.uint16), want), (tile, m, n, k)
+
+
 @pytest.mark.parametrize("path", [GEMV, SKINNY, MFMA])
 @pytest.mark.parametrize("m,n,k", [(1, 96, 512), (8, 130, 2048), (200, 300, 1040), (20, 25000, 2064)])
 def test_gemm_outliers_exact_arithmetic_bitexact(path, m, n, k):
